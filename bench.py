@@ -1,0 +1,215 @@
+"""Benchmark: MoE layer forward + backward tokens/s on one MI355X.
+
+One step = the whole layer on one batch: moe_route, moe_dispatch,
+moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward (all through the C ABI,
+inputs already resident in HBM). Default workload: the Switch-Base-shaped layer
+(T=8192 tokens as 16x512, d_model=768, 128 ReLU experts 768->3072->768, top-1,
+capacity factor 1.25, bf16 activations and weights, fp32 router, aux alpha 0.01).
+
+Prints one JSON line (see the keys below). Also measured and reported:
+  roofline: the stage with the largest per-launch time, timed with HIP events on
+    its own stream over the timed region, against its algorithmic bytes or flops;
+  cpu_baseline: the oracle (plain C++ in double) on a bounded token sample of the
+    same layer, on this host's cores (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # flop/s, dense bf16 matrix cores
+PEAK_F32_VALU = 78.6e12    # flop/s, fp32 vector FMA without packed-fp32 instructions
+
+
+class HipEvents:
+    """Raw HIP events (for the library's stage timing hook)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            p = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(p)) == 0
+            self.ev[i] = p
+        self.n = n
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(self.ev[b])
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) == 0
+        return ms.value
+
+
+def stage_work(c, rows, ne_experts):
+    """Algorithmic (flops, bytes) of one launch of each stage, from the realised routing.
+    rows: kept routed rows; ne_experts: experts with at least one row."""
+    T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
+    f1 = 2 * f if c.act == "swiglu" else f
+    eb = 2 if c.dtype == "bf16" else 4
+    S = T if c.shared else 0
+    R = rows + S
+    W1 = (ne_experts + (1 if c.shared else 0)) * f1 * d * eb
+    W2 = (ne_experts + (1 if c.shared else 0)) * d * f * eb
+    W1all = (E + (1 if c.shared else 0)) * f1 * d * eb
+    W2all = (E + (1 if c.shared else 0)) * d * f * eb
+    return {
+        "route": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 + T * k * 8),
+        "dispatch": (0, T * k * 4 * 3 + T * d * eb + rows * d * eb + rows * 4),
+        "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * (f1 + f) * eb),
+        "ffn_gemm2": (2 * R * f * d, W2 + R * f * eb + R * d * eb),
+        "combine": (0, T * d * eb * (2 + (1 if c.shared else 0)) + rows * d * eb + T * k * 8),
+        "aux": (0, T * E * 4),
+        "bwd_combine": (0, T * d * eb + rows * d * eb * 2 + T * k * 12),
+        "bwd_dgrad2": (2 * R * d * f, W2 + R * d * eb + 2 * R * f1 * eb),
+        "bwd_wgrad2": (2 * R * d * f, W2all + R * d * eb + R * f * eb),
+        "bwd_dgrad1": (2 * R * f1 * d, W1 + R * f1 * eb + R * d * eb),
+        "bwd_wgrad1": (2 * R * f1 * d, W1all + R * f1 * eb + R * d * eb),
+        "bwd_dlogits": (0, T * E * 8 + T * k * 12),
+        "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 + T * d * 4),
+        "bwd_unpermute": (0, T * d * eb * 2 + rows * d * eb + T * d * 4),
+    }
+
+
+def cpu_baseline(c, inp, budget_tokens):
+    """Oracle forward+backward of the same layer on the first `budget_tokens` tokens
+    (an independent batch of that size; capacity follows the formula for it)."""
+    import oracle as O
+    sub = c.replace(T=budget_tokens)
+    oin = {k: O.f64(v[:budget_tokens] if k in ("x", "dy") else v) for k, v in inp.items()}
+    spec = O.Spec.of(sub)
+    t0 = time.perf_counter()
+    fw = O.forward(spec, oin)
+    O.backward(spec, oin, fw, oin["dy"])
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{budget_tokens}-token batch of the same layer (same weights), forward+backward, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="switch_base")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the layer on one GPU only; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is a design note, not an implementation).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mixture_experts_25_amd as M
+    from synth import CONFIGS, make_inputs
+
+    c = CONFIGS[args.config]
+    if c.fwd_only:
+        c = c.replace(fwd_only=False)
+    torch.cuda.set_device(0)
+    inp = make_inputs(c, seed=args.seed, device="cuda")
+    cfg = M.make_config(c.T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate, act=c.act,
+                        dtype=c.dtype, alpha=c.alpha, shared=c.shared)
+    buf = M.LayerBuffers.allocate(cfg)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        M.forward(buf, inp, stream=stream)
+        M.backward(buf, inp, inp["dy"], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-stage times over a few steps (every stage armed) to find the dominant one
+    nst = 32
+    ev = HipEvents(2 * nst * 4)
+    M.lib().moe_profile_arm.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int]
+    M.lib().moe_profile_stage.restype = ctypes.c_char_p
+    M.lib().moe_profile_arm(None, ctypes.cast(ev.ev, ctypes.c_void_p), nst * 4)
+    for _ in range(3):
+        step()
+    npairs = M.lib().moe_profile_disarm()
+    torch.cuda.synchronize()
+    per_stage = {}
+    for i in range(npairs):
+        name = M.lib().moe_profile_stage(i).decode()
+        per_stage.setdefault(name, []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
+    per_stage = {k: sum(v) / len(v) for k, v in per_stage.items()}
+    dom = max(per_stage, key=per_stage.get)
+
+    # timed region: K steps; the dominant stage's launches are bracketed by events
+    evd = HipEvents(2 * args.steps)
+    M.lib().moe_profile_arm(dom.encode(), ctypes.cast(evd.ev, ctypes.c_void_p), args.steps)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    nd = M.lib().moe_profile_disarm()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    dom_ms = sum(evd.elapsed_ms(2 * i, 2 * i + 1) for i in range(nd)) / max(nd, 1)
+
+    offs = buf.t["expert_offsets"].cpu()
+    rows = int(offs[-1])
+    ne = int(((offs[1:] - offs[:-1]) > 0).sum())
+    work = stage_work(c, rows, ne)
+    fl, by = work[dom]
+    if fl and fl / max(by, 1) > PEAK_BF16 / PEAK_HBM and dom.startswith(("ffn", "bwd_dgrad", "bwd_wgrad")):
+        roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["launch_ms"] = dom_ms
+
+    total_flops = sum(v[0] for v in work.values())
+    line = {
+        "metric": "MoE layer fwd+bwd tokens/sec on 1 MI355X",
+        "value": c.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, random-init weights of the layer's shapes)",
+        "config": {"workload": c.name, "T": c.T, "d_model": c.d, "d_ff": c.f, "experts": c.E, "top_k": c.k,
+                   "capacity_factor": c.cf, "act": c.act, "gate": c.gate, "kept_rows": rows,
+                   "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12},
+        "roofline": roof,
+    }
+    if args.stages:
+        print(json.dumps({"stage_ms": per_stage}), file=sys.stderr)
+    line["stage_ms"] = {k: round(v, 4) for k, v in per_stage.items()}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, {k: v for k, v in inp.items()}, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

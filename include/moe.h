@@ -1,0 +1,217 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) token-routed Mixture-of-Experts layer.
+ *
+ * One layer, forward and backward, on one GPU. Every call enqueues HIP kernels
+ * on the caller's stream and returns at once: no host synchronisation, no
+ * device allocation, no global state. The caller owns every buffer, including
+ * the tensors the forward produces and the backward consumes.
+ *
+ * Pages cited by title:
+ *   [SW]   "Mixture of Experts (MoE) を1から解説 — Switch Transformerのルーティングと負荷分散"
+ *          (ta-paperlens.web.app, explainer of the Switch Transformer paper)
+ *   [WIKI] "Mixture-of-Experts" (notes.yuuk.io concept page)
+ *   [LRMOE] LRMoE news item (ai-cafe.club), section "この記事のポイント"
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers unless stated otherwise; tensors are dense
+ *     and row-major with the shapes given. `act` below means the activation
+ *     storage type: bf16 (MOE_DT_BF16) or fp32 (MOE_DT_F32). Router tensors
+ *     (w_router, probs, topk_w, logit_offset, sel_bias, dw_router) are fp32.
+ *   - Device pointers must be 16-byte aligned. d_model and d_ff must be
+ *     multiples of 8.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Arguments are validated on the host before any HIP call; a bad argument
+ *     returns an error and enqueues nothing. MOE_ERR_HIP reports a launch error
+ *     taken from hipGetLastError after the launches. Kernels that run
+ *     asynchronously report nothing back.
+ *   - Where a call takes a workspace, `ws` must hold at least the
+ *     `workspace_bytes` that moe_plan returns for the same config. Its contents
+ *     need not be initialised and are clobbered.
+ *   - Capacity mode (capacity_factor > 0) keeps at most C rows per expert;
+ *     dropless mode (capacity_factor <= 0) keeps every assignment. max_rows
+ *     (from moe_plan) bounds the number of kept rows; rows of the permuted
+ *     buffers at or beyond the kept count are never read or written.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, bad size, misalignment */
+#define MOE_ERR_UNSUPPORTED (-2)  /* unknown gate / activation / dtype combination */
+#define MOE_ERR_WORKSPACE (-3)    /* workspace missing or smaller than moe_plan says */
+#define MOE_ERR_HIP (-4)          /* a kernel launch failed */
+
+/* gates */
+#define MOE_GATE_SOFTMAX 0        /* [SW] eq. (1); selection on the logits */
+#define MOE_GATE_SIGMOID_BIAS 1   /* [WIKI] sigmoid gate + per-expert bias used only to select */
+/* expert activations */
+#define MOE_ACT_RELU 0
+#define MOE_ACT_SWIGLU 1          /* silu(x Wg^T) * (x Wu^T); W1 stacks [Wg; Wu] */
+/* activation / expert-weight storage types */
+#define MOE_DT_F32 0
+#define MOE_DT_BF16 1
+
+/* Layer description. Field names follow the vocabulary of [SW] (section on
+ * using the method in practice: num_experts, capacity_factor, expert capacity,
+ * aux-loss coefficient). Host memory. */
+typedef struct moe_config {
+  int32_t num_tokens;       /* T: tokens in the batch */
+  int32_t d_model;          /* d */
+  int32_t d_ff;             /* f: expert hidden width (each half, for SwiGLU) */
+  int32_t num_experts;      /* E: routed experts */
+  int32_t top_k;            /* k: experts per token, 1 <= k <= E */
+  float capacity_factor;    /* > 0: capacity mode ([SW] eq. (3)); <= 0: dropless */
+  int32_t renormalize;      /* 1: the k selected weights are divided by their sum */
+  int32_t gate;             /* MOE_GATE_* */
+  int32_t act;              /* MOE_ACT_* */
+  int32_t dtype;            /* MOE_DT_*: activations and expert weights */
+  float aux_alpha;          /* alpha of [SW] eq. (4); 0 disables the aux loss */
+  int32_t num_shared_experts; /* 0 or 1: an always-on expert added with weight 1 ([WIKI]) */
+} moe_config;
+
+/* Sizes derived from a config (host memory), filled by moe_plan. */
+typedef struct moe_plan_info {
+  int32_t expert_capacity;  /* C = ceil(T / E * capacity_factor) in double; -1 when dropless */
+  int32_t f1;               /* width of the first expert matmul: f (ReLU) or 2f (SwiGLU) */
+  int64_t max_rows;         /* rows the permuted buffers must hold: T*k, or min(T*k, E*C) */
+  size_t workspace_bytes;   /* workspace any call of this config needs */
+} moe_plan_info;
+
+/* Tensors the forward produced, handed to the backward (device memory).
+ * Shapes use R = max_rows and f1 from moe_plan. */
+typedef struct moe_saved {
+  const void* x;                 /* [T, d] act: layer input */
+  const float* probs;            /* [T, E] router probabilities (softmax) or sigmoid scores */
+  const int32_t* topk_idx;       /* [T, k] */
+  const float* topk_w;           /* [T, k] */
+  const int32_t* slot;           /* [T, k] row in the permuted buffers, -1 = dropped */
+  const int32_t* expert_counts;  /* [E] assignments per expert before drops */
+  const int32_t* expert_offsets; /* [E+1] first permuted row of each expert */
+  const void* x_perm;            /* [R, d]  act */
+  const void* act_saved;         /* [R, f1] act: pre-activation(s) */
+  const void* h_saved;           /* [R, f]  act: activation fed to the second matmul */
+  const void* y_perm;            /* [R, d]  act: expert outputs */
+  const void* act_shared;        /* [T, f1] shared expert (NULL without one) */
+  const void* h_shared;          /* [T, f]  shared expert (NULL without one) */
+} moe_saved;
+
+/* Layer parameters (device memory). */
+typedef struct moe_weights {
+  const float* w_router;  /* [E, d] fp32 */
+  const void* w1;         /* [E, f1, d] act (SwiGLU: rows [0,f) gate, [f,2f) up) */
+  const void* w2;         /* [E, d, f]  act */
+  const void* ws1;        /* [f1, d] shared expert, NULL without one */
+  const void* ws2;        /* [d, f]  shared expert, NULL without one */
+} moe_weights;
+
+/* Gradients written by moe_backward (device memory; every one is overwritten,
+ * experts with no kept rows get zeros). */
+typedef struct moe_grads {
+  void* dx;          /* [T, d] act */
+  float* dw_router;  /* [E, d] fp32 */
+  void* dw1;         /* [E, f1, d] act */
+  void* dw2;         /* [E, d, f] act */
+  void* dws1;        /* [f1, d] act, shared expert only */
+  void* dws2;        /* [d, f] act, shared expert only */
+} moe_grads;
+
+/* Validate a config and derive its sizes. Host only; enqueues nothing.
+ * cfg, out: host pointers. */
+int moe_plan(const moe_config* cfg, moe_plan_info* out);
+
+/* Router: [SW] eq. (1) and the top-k choice of the section on routing.
+ *   h[t,e] = sum_j x[t,j] * w_router[e,j] in fp32, ascending j, one fused
+ *            multiply-add per term from +0 (this fixed order makes the routing
+ *            reproducible bit for bit); plus logit_offset[e] (one fp32 add) when given.
+ *   softmax gate: probs = softmax(h) over the E experts; selection key = h.
+ *   sigmoid gate: probs = s = 1/(1 + exp_c(-h)) with exp_c the library's fixed
+ *            fp32 exponential (Cody-Waite reduction + degree-7 Taylor); key = s + sel_bias[e].
+ *   topk_idx[t,:] = the k experts of largest key, equal keys broken by the lower
+ *            index, listed in that order. topk_w[t,r] = probs[t,e_r], divided by the
+ *            sum over the k selected when cfg->renormalize.
+ * x: [T,d] act. w_router: [E,d]. logit_offset, sel_bias: [E] or NULL (sel_bias
+ * is used only by the sigmoid gate). Outputs probs [T,E], topk_idx [T,k], topk_w [T,k]. */
+int moe_route(const moe_config* cfg, const void* x, const float* w_router,
+              const float* logit_offset, const float* sel_bias, float* probs,
+              int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Capacity, positions and permutation: [SW] eq. (3) and the section on expert
+ * capacity (seats fixed before the data is seen, overflow rides the residual),
+ * with the compacted expert-contiguous layout of [LRMOE].
+ *   pos(t,r) = number of earlier tokens t' < t routed to the same expert;
+ *   kept iff pos < C (always in dropless mode).
+ *   expert_counts[e] = assignments before drops; expert_offsets = exclusive
+ *   prefix sum of kept rows (offsets[E] = kept total); slot[t,r] =
+ *   offsets[e] + pos if kept else -1; row_token[slot] = t;
+ *   x_perm[slot] = x[t] (bitwise copy).
+ * topk_idx may come from moe_route or from the caller (values must lie in [0,E)).
+ * Outputs: expert_counts [E], expert_offsets [E+1], slot [T,k], row_token [R],
+ * x_perm [R,d] act. Needs the workspace. */
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot,
+                 int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs over the compacted rows (grouped matmul over ragged groups),
+ * [SW] section on replacing the FFN by N expert copies; [LRMOE] variable-size
+ * grouped GEMM. For each expert e and its rows r in [offsets[e], offsets[e+1]):
+ *   ReLU:   act = x_perm W1_e^T, h = max(act, 0)
+ *   SwiGLU: act = x_perm W1_e^T ([gate | up], 2f wide), h = silu(gate) * up
+ *   y_perm = h W2_e^T
+ * act and h are stored in the activation type (bf16: round to nearest even
+ * from the fp32 accumulator; h is formed from the unrounded accumulators).
+ * With a shared expert, the same is computed for every token row of x with
+ * ws1/ws2 into act_shared [T,f1], h_shared [T,f], y_shared [T,d]; those pointers
+ * must be NULL without one. Inputs: x_perm [R,d], expert_offsets [E+1] (device,
+ * as written by moe_dispatch), w1 [E,f1,d], w2 [E,d,f]. Outputs: act_saved
+ * [R,f1], h_saved [R,f], y_perm [R,d]. Needs the workspace. */
+int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w1, const void* w2, const void* x, const void* ws1,
+                   const void* ws2, void* act_saved, void* h_saved, void* y_perm,
+                   void* act_shared, void* h_shared, void* y_shared, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Combine: [SW] eq. (2) plus the residual.
+ *   y[t] = x[t] + sum over kept r of topk_w[t,r] * y_perm[slot[t,r]] (+ y_shared[t])
+ * accumulated in fp32 and stored once in the activation type. A token whose
+ * every choice was dropped gets y = x bit for bit. Weights are not
+ * renormalised after drops. x [T,d], y_perm [R,d], slot [T,k], topk_w [T,k],
+ * y_shared [T,d] or NULL; output y [T,d]. */
+int moe_combine(const moe_config* cfg, const void* x, const void* y_perm, const int32_t* slot,
+                const float* topk_w, const void* y_shared, void* y, void* stream);
+
+/* Switch load-balancing loss, [SW] eq. (4) and the numpy sketch after it:
+ *   aux = alpha * E * sum_i f_i * P_i,  f_i = expert_counts[i] / (T*k) (counted
+ *   before drops), P_i = mean over t of probs[t,i].
+ * probs [T,E], expert_counts [E]; aux_out: one fp32 on the device. Writes 0
+ * when aux_alpha == 0. Needs the workspace. */
+int moe_aux_loss(const moe_config* cfg, const float* probs, const int32_t* expert_counts,
+                 float* aux_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the layer for the loss L = sum_t <dy[t], y[t]> + aux (aux term
+ * only when aux_alpha != 0): [SW] eq. (2) (the gate multiplies the expert
+ * output, so the router is trained through it) and eq. (4) (only P carries
+ * gradient). Writes every field of *g:
+ *   dx = dy + sum over kept r of dX_perm[slot] + dx_router (+ dx_shared)
+ *   dw1, dw2 per expert from its rows (zeros for experts with no rows),
+ *   dws1, dws2 for the shared expert, dw_router = dlogits^T x in fp32.
+ * dy: [T,d] act. s, w, g: host structs holding device pointers. Needs the workspace. */
+int moe_backward(const moe_config* cfg, const void* dy, const moe_saved* s,
+                 const moe_weights* w, const moe_grads* g, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Static string naming a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,224 @@
+"""Python binding of the MI355X MoE layer library (libmoe.so, C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch supplies device memory and the current stream. There is no
+fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
+calls raises.
+
+Entry points mirror the C ABI: moe_plan, moe_route, moe_dispatch,
+moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward, moe_status_string.
+``LayerBuffers`` allocates the tensors one forward+backward needs, and
+``forward`` / ``backward`` issue the ABI calls in order on those buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = 0, 1
+MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+
+EXPORTS = ["moe_plan", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
+           "moe_backward", "moe_status_string"]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("aux_alpha", ctypes.c_float), ("num_shared_experts", ctypes.c_int32)]
+
+
+class moe_plan_info(ctypes.Structure):
+    _fields_ = [("expert_capacity", ctypes.c_int32), ("f1", ctypes.c_int32), ("max_rows", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_vp = ctypes.c_void_p
+
+
+class moe_saved(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "probs", "topk_idx", "topk_w", "slot", "expert_counts",
+                                   "expert_offsets", "x_perm", "act_saved", "h_saved", "y_perm",
+                                   "act_shared", "h_shared")]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_router", "w1", "w2", "ws1", "ws2")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("dx", "dw_router", "dw1", "dw2", "dws1", "dws2")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_25_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        cfg = P(moe_config)
+        L.moe_plan.argtypes = [cfg, P(moe_plan_info)]
+        L.moe_route.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_dispatch.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
+        L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_aux_loss.argtypes = [cfg, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_backward.argtypes = [cfg, _vp, P(moe_saved), P(moe_weights), P(moe_grads), _vp,
+                                   ctypes.c_size_t, _vp]
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        for n in EXPORTS[:-1]:
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(f"{what}: {moe_status_string(status)} ({status})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_config(T, d, f, E, k, *, cf=0.0, renorm=False, gate="softmax", act="relu", dtype="bf16",
+                alpha=0.0, shared=0) -> moe_config:
+    return moe_config(int(T), int(d), int(f), int(E), int(k), float(cf), int(bool(renorm)),
+                      MOE_GATE_SIGMOID_BIAS if gate == "sigmoid_bias" else MOE_GATE_SOFTMAX,
+                      MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_RELU,
+                      MOE_DT_BF16 if dtype == "bf16" else MOE_DT_F32, float(alpha), int(shared))
+
+
+def moe_plan(cfg: moe_config) -> moe_plan_info:
+    info = moe_plan_info()
+    _check(lib().moe_plan(ctypes.byref(cfg), ctypes.byref(info)), "moe_plan")
+    return info
+
+
+def moe_route(cfg, x, w_router, logit_offset, sel_bias, probs, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(sel_bias), _p(probs),
+                           _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_dispatch(cfg, x, topk_idx, expert_counts, expert_offsets, slot, row_token, x_perm, ws, stream=None):
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _p(x), _p(topk_idx), _p(expert_counts), _p(expert_offsets),
+                              _p(slot), _p(row_token), _p(x_perm), _p(ws), ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(cfg, x_perm, expert_offsets, w1, w2, x, ws1, ws2, act_saved, h_saved, y_perm, act_shared,
+                   h_shared, y_shared, ws, stream=None):
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(expert_offsets), _p(w1), _p(w2), _p(x),
+                                _p(ws1), _p(ws2), _p(act_saved), _p(h_saved), _p(y_perm), _p(act_shared),
+                                _p(h_shared), _p(y_shared), _p(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(cfg, x, y_perm, slot, topk_w, y_shared, y, stream=None):
+    _check(lib().moe_combine(ctypes.byref(cfg), _p(x), _p(y_perm), _p(slot), _p(topk_w), _p(y_shared), _p(y),
+                             _stream(stream)), "moe_combine")
+
+
+def moe_aux_loss(cfg, probs, expert_counts, aux_out, ws, stream=None):
+    _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(probs), _p(expert_counts), _p(aux_out), _p(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_aux_loss")
+
+
+def moe_backward(cfg, dy, saved: dict, weights: dict, grads: dict, ws, stream=None):
+    s = moe_saved(*[_p(saved.get(n)) for n, _ in moe_saved._fields_])
+    w = moe_weights(*[_p(weights.get(n)) for n, _ in moe_weights._fields_])
+    g = moe_grads(*[_p(grads.get(n)) for n, _ in moe_grads._fields_])
+    _check(lib().moe_backward(ctypes.byref(cfg), _p(dy), ctypes.byref(s), ctypes.byref(w), ctypes.byref(g),
+                              _p(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_backward")
+
+
+# --------------------------------------------------------------- buffers + call order
+
+@dataclass
+class LayerBuffers:
+    """Device tensors for one forward + backward of a config (allocated with torch)."""
+    cfg: moe_config
+    info: moe_plan_info
+    t: dict
+
+    @staticmethod
+    def allocate(cfg: moe_config, device="cuda", backward=True) -> "LayerBuffers":
+        info = moe_plan(cfg)
+        T, d, f, E, k = cfg.num_tokens, cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k
+        R, f1 = int(info.max_rows), int(info.f1)
+        dt = torch.bfloat16 if cfg.dtype == MOE_DT_BF16 else torch.float32
+        i32, f32 = torch.int32, torch.float32
+        e = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=device)
+        t = dict(probs=e((T, E), f32), topk_idx=e((T, k), i32), topk_w=e((T, k), f32),
+                 expert_counts=e((E,), i32), expert_offsets=e((E + 1,), i32), slot=e((T, k), i32),
+                 row_token=e((max(R, 1),), i32), x_perm=e((max(R, 1), d), dt), act_saved=e((max(R, 1), f1), dt),
+                 h_saved=e((max(R, 1), f), dt), y_perm=e((max(R, 1), d), dt), y=e((T, d), dt),
+                 aux=e((1,), f32), ws=e((max(int(info.workspace_bytes), 256),), torch.uint8))
+        if cfg.num_shared_experts:
+            t.update(act_shared=e((T, f1), dt), h_shared=e((T, f), dt), y_shared=e((T, d), dt))
+        if backward:
+            t.update(dx=e((T, d), dt), dw_router=e((E, d), f32), dw1=e((E, f1, d), dt), dw2=e((E, d, f), dt))
+            if cfg.num_shared_experts:
+                t.update(dws1=e((f1, d), dt), dws2=e((d, f), dt))
+        return LayerBuffers(cfg, info, t)
+
+
+def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
+    """moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (-> moe_aux_loss)."""
+    c, t = buf.cfg, buf.t
+    moe_route(c, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"), t["probs"],
+              t["topk_idx"], t["topk_w"], stream)
+    moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"], t["row_token"],
+                 t["x_perm"], t["ws"], stream)
+    moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
+                   inp.get("ws2"), t["act_saved"], t["h_saved"], t["y_perm"], t.get("act_shared"),
+                   t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
+    moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
+    if aux:
+        moe_aux_loss(c, t["probs"], t["expert_counts"], t["aux"], t["ws"], stream)
+
+
+SAVED_KEYS = ["probs", "topk_idx", "topk_w", "slot", "expert_counts", "expert_offsets", "x_perm", "act_saved",
+              "h_saved", "y_perm", "act_shared", "h_shared"]
+
+
+def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream=None):
+    """moe_backward from the forward's saved tensors (``saved`` overrides any of them)."""
+    t = buf.t
+    sv = {k: t.get(k) for k in SAVED_KEYS}
+    sv["x"] = inp["x"]
+    if saved:
+        sv.update(saved)
+    weights = {k: inp.get(k) for k in ("w_router", "w1", "w2", "ws1", "ws2")}
+    grads = {k: t.get(k) for k in ("dx", "dw_router", "dw1", "dw2", "dws1", "dws2")}
+    moe_backward(buf.cfg, dy, sv, weights, grads, t["ws"], stream)

@@ -1,0 +1,404 @@
+// C ABI of the MoE layer: argument validation, sizes, workspace carving and
+// the launch sequence of each call. No allocation, no host synchronisation,
+// no global state.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+#include "../../include/moe.h"
+#include "../../include/moe_profile.h"
+
+namespace moe {
+int gemm_f32_row_tile();
+}
+
+namespace {
+
+constexpr int kBf16RowTile = 128;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(const moe_config* c) { return c->dtype == MOE_DT_BF16 ? 2 : 4; }
+
+int check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->d_model < 8 || c->d_ff < 8) return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 8 || c->d_ff % 8) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts > 512 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)c->num_tokens * c->top_k > (int64_t)0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype != MOE_DT_F32 && c->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->num_shared_experts != 0 && c->num_shared_experts != 1) return MOE_ERR_UNSUPPORTED;
+  if (!(c->capacity_factor == c->capacity_factor) || !(c->aux_alpha == c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int capacity_of(const moe_config* c) {
+  if (c->capacity_factor <= 0.0f) return -1;
+  // evaluated in double in the order of the capacity formula
+  const double v = ceil((double)c->num_tokens / (double)c->num_experts * (double)c->capacity_factor);
+  return v > 2147483647.0 ? 2147483647 : (int)v;
+}
+
+int64_t max_rows_of(const moe_config* c, int C) {
+  const int64_t tk = (int64_t)c->num_tokens * c->top_k;
+  if (C < 0) return tk;
+  const int64_t ec = (int64_t)c->num_experts * C;
+  return tk < ec ? tk : ec;
+}
+
+// Backward workspace layout.
+struct BwdWs {
+  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, total;
+};
+BwdWs bwd_layout(const moe_config* c, int64_t R) {
+  const int64_t T = c->num_tokens, d = c->d_model, E = c->num_experts, k = c->top_k;
+  const int64_t f1 = c->act == MOE_ACT_SWIGLU ? 2 * (int64_t)c->d_ff : c->d_ff;
+  const int64_t eb = elem_bytes(c);
+  const int64_t ns = moe::router_grad_splits((int)T);
+  BwdWs w;
+  size_t o = 0;
+  w.dO = o; o += align_up(R * d * eb);
+  w.dA = o; o += align_up(R * f1 * eb);
+  w.dXp = o; o += align_up(R * d * eb);
+  w.dg = o; o += align_up(T * k * 4);
+  w.dl = o; o += align_up(T * E * 4);
+  w.dxr = o; o += align_up(T * d * 4);
+  w.part = o; o += align_up(ns * E * d * 4);
+  w.dA_sh = o; o += c->num_shared_experts ? align_up(T * f1 * eb) : 0;
+  w.dX_sh = o; o += c->num_shared_experts ? align_up(T * d * eb) : 0;
+  w.total = o;
+  return w;
+}
+
+size_t workspace_of(const moe_config* c, int64_t R) {
+  size_t ws = align_up((size_t)moe::dispatch_num_chunks(c->num_tokens, c->top_k) * c->num_experts * 4);
+  const size_t aux = align_up((size_t)moe::aux_num_blocks(c->num_tokens) * c->num_experts * 4);
+  if (aux > ws) ws = aux;
+  const size_t bw = bwd_layout(c, R).total;
+  if (bw > ws) ws = bw;
+  return ws;
+}
+
+int64_t row_tile_bound(const moe_config* c, int64_t R, int shared_rows) {
+  const int64_t bm = c->dtype == MOE_DT_BF16 ? kBf16RowTile : moe::gemm_f32_row_tile();
+  return (R + bm - 1) / bm + c->num_experts + (shared_rows + bm - 1) / bm;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Opt-in timing hook (moe_profile.h): an event pair around each launch of the
+// armed stage. Process-wide; used from one host thread by benchmarks.
+constexpr int kMaxProfPairs = 4096;
+struct Prof {
+  bool armed = false;
+  bool all = false;
+  char only[64] = {0};
+  hipEvent_t* ev = nullptr;
+  int max = 0, n = 0;
+  const char* names[kMaxProfPairs];
+};
+Prof g_prof;
+
+struct StageTimer {
+  int idx = -1;
+  hipStream_t s;
+  StageTimer(const char* name, hipStream_t st) : s(st) {
+    if (!g_prof.armed || g_prof.n >= g_prof.max) return;
+    if (!g_prof.all && strcmp(g_prof.only, name) != 0) return;
+    idx = g_prof.n++;
+    g_prof.names[idx] = name;
+    (void)hipEventRecord(g_prof.ev[2 * idx], s);
+  }
+  ~StageTimer() {
+    if (idx >= 0) (void)hipEventRecord(g_prof.ev[2 * idx + 1], s);
+  }
+};
+
+int gemm(const moe_config* c, moe::GemmArgs a, hipStream_t st, const char* stage) {
+  StageTimer pt(stage, st);
+  hipError_t e = c->dtype == MOE_DT_BF16 ? moe::launch_gemm_bf16(a, st) : moe::launch_gemm_f32(a, st);
+  return launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int moe_plan(const moe_config* c, moe_plan_info* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const int st = check_config(c);
+  if (st) return st;
+  const int C = capacity_of(c);
+  const int64_t R = max_rows_of(c, C);
+  out->expert_capacity = C;
+  out->f1 = c->act == MOE_ACT_SWIGLU ? 2 * c->d_ff : c->d_ff;
+  out->max_rows = R;
+  out->workspace_bytes = workspace_of(c, R);
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* c, const void* x, const float* w_router, const float* logit_offset,
+              const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  const bool empty = c->num_tokens == 0;  // token-indexed pointers may then be NULL
+  if (!w_router || (!empty && (!x || !probs || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  if (empty) return MOE_OK;
+  moe::RouterArgs a{x, w_router, logit_offset, sel_bias, probs, topk_idx, topk_w, c->num_tokens, c->d_model,
+                    c->num_experts, c->top_k, c->gate, c->renormalize ? 1 : 0, c->dtype};
+  StageTimer pt("route", (hipStream_t)stream);
+  return launch_status(moe::launch_router(a, (hipStream_t)stream));
+}
+
+int moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* slot, int32_t* row_token, void* x_perm, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  const bool empty = c->num_tokens == 0;
+  if (!expert_counts || !expert_offsets || (!empty && (!x || !topk_idx || !slot || !row_token || !x_perm)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(c);
+  const size_t need = workspace_of(c, max_rows_of(c, C));
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  moe::DispatchArgs a{x, topk_idx, expert_counts, expert_offsets, slot, row_token, x_perm, (int32_t*)ws,
+                      c->num_tokens, c->d_model, c->num_experts, c->top_k, C, elem_bytes(c)};
+  StageTimer pt("dispatch", (hipStream_t)stream);
+  return launch_status(moe::launch_dispatch(a, (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                   const void* w2, const void* x, const void* ws1, const void* ws2, void* act_saved,
+                   void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  const bool empty = c->num_tokens == 0;
+  if (!expert_offsets || !w1 || !w2 || (!empty && (!x_perm || !act_saved || !h_saved || !y_perm)))
+    return MOE_ERR_INVALID_ARG;
+  const bool sh = c->num_shared_experts > 0;
+  if (sh && (!ws1 || !ws2 || (!empty && (!x || !act_shared || !h_shared || !y_shared)))) return MOE_ERR_INVALID_ARG;
+  if (!sh && (ws1 || ws2 || act_shared || h_shared || y_shared)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_perm, w1, w2, act_saved, h_saved, y_perm};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(c);
+  const int64_t R = max_rows_of(c, C);
+  if (!ws || ws_bytes < workspace_of(c, R)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c->num_tokens, d = c->d_model, f = c->d_ff, E = c->num_experts;
+  const int f1 = c->act == MOE_ACT_SWIGLU ? 2 * f : f;
+  const int shr = sh ? T : 0;
+
+  moe::GemmArgs g1{};
+  g1.kind = 0;
+  g1.epi = c->act == MOE_ACT_SWIGLU ? moe::EPI_SWIGLU_FWD : moe::EPI_RELU_FWD;
+  g1.b_kcontig = 1;
+  g1.N = f1; g1.K = d; g1.f = f;
+  g1.has_shared = sh ? 1 : 0;
+  g1.offsets = expert_offsets; g1.E = E; g1.shared_rows = shr;
+  g1.max_row_tiles = row_tile_bound(c, R, shr);
+  g1.A = x_perm; g1.lda = d;
+  g1.B = w1; g1.ldb = d; g1.strideB = (int64_t)f1 * d;
+  g1.A_sh = x; g1.B_sh = ws1;
+  g1.C = act_saved; g1.ldc = f1; g1.C_sh = act_shared;
+  g1.C2 = h_saved; g1.ldc2 = f; g1.C2_sh = h_shared;
+  if ((st = gemm(c, g1, s, "ffn_gemm1"))) return st;
+
+  moe::GemmArgs g2{};
+  g2.kind = 0;
+  g2.epi = moe::EPI_STORE;
+  g2.b_kcontig = 1;
+  g2.N = d; g2.K = f; g2.f = f;
+  g2.has_shared = sh ? 1 : 0;
+  g2.offsets = expert_offsets; g2.E = E; g2.shared_rows = shr;
+  g2.max_row_tiles = row_tile_bound(c, R, shr);
+  g2.A = h_saved; g2.lda = f;
+  g2.B = w2; g2.ldb = f; g2.strideB = (int64_t)d * f;
+  g2.A_sh = h_shared; g2.B_sh = ws2;
+  g2.C = y_perm; g2.ldc = d; g2.C_sh = y_shared;
+  return gemm(c, g2, s, "ffn_gemm2");
+}
+
+int moe_combine(const moe_config* c, const void* x, const void* y_perm, const int32_t* slot, const float* topk_w,
+                const void* y_shared, void* y, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  const bool empty = c->num_tokens == 0;
+  if (!empty && (!x || !y_perm || !slot || !topk_w || !y)) return MOE_ERR_INVALID_ARG;
+  if (!empty && (c->num_shared_experts > 0) != (y_shared != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared_experts == 0 && y_shared) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y_perm) || !aligned16(y) || !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens == 0) return MOE_OK;
+  moe::CombineArgs a{x, y_perm, slot, topk_w, y_shared, y, c->num_tokens, c->d_model, c->top_k, c->dtype};
+  StageTimer pt("combine", (hipStream_t)stream);
+  return launch_status(moe::launch_combine(a, (hipStream_t)stream));
+}
+
+int moe_aux_loss(const moe_config* c, const float* probs, const int32_t* expert_counts, float* aux_out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (!expert_counts || !aux_out || (c->num_tokens > 0 && !probs)) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(c);
+  if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, C))) return MOE_ERR_WORKSPACE;
+  moe::AuxArgs a{probs, expert_counts, aux_out, (float*)ws, c->num_tokens, c->num_experts, c->top_k,
+                 c->aux_alpha};
+  StageTimer pt("aux", (hipStream_t)stream);
+  return launch_status(moe::launch_aux(a, (hipStream_t)stream));
+}
+
+int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const moe_weights* w,
+                 const moe_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (!sv || !w || !g) return MOE_ERR_INVALID_ARG;
+  const bool sh = c->num_shared_experts > 0;
+  const bool empty = c->num_tokens == 0;  // token- and row-indexed pointers may then be NULL
+  if (!sv->expert_counts || !sv->expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (!empty && (!dy || !sv->x || !sv->probs || !sv->topk_idx || !sv->topk_w || !sv->slot || !sv->x_perm ||
+                 !sv->act_saved || !sv->h_saved || !sv->y_perm || !g->dx))
+    return MOE_ERR_INVALID_ARG;
+  if (!w->w_router || !w->w1 || !w->w2 || !g->dw_router || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
+  if (sh && (!w->ws1 || !w->ws2 || !g->dws1 || !g->dws2 || (!empty && (!sv->act_shared || !sv->h_shared))))
+    return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {dy, sv->x, sv->x_perm, sv->act_saved, sv->h_saved, sv->y_perm, w->w_router,
+                        w->w1, w->w2, g->dx, g->dw_router, g->dw1, g->dw2};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(c);
+  const int64_t R = max_rows_of(c, C);
+  if (!ws || ws_bytes < workspace_of(c, R)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c->num_tokens, d = c->d_model, f = c->d_ff, E = c->num_experts, k = c->top_k;
+  const int f1 = c->act == MOE_ACT_SWIGLU ? 2 * f : f;
+  const int shr = sh ? T : 0;
+  const BwdWs L = bwd_layout(c, R);
+  uint8_t* base = (uint8_t*)ws;
+  void* dO = base + L.dO;
+  void* dA = base + L.dA;
+  void* dXp = base + L.dXp;
+  float* dg = (float*)(base + L.dg);
+  float* dl = (float*)(base + L.dl);
+  float* dxr = (float*)(base + L.dxr);
+  float* part = (float*)(base + L.part);
+  void* dA_sh = sh ? base + L.dA_sh : nullptr;
+  void* dX_sh = sh ? base + L.dX_sh : nullptr;
+
+  if (T > 0) {
+    moe::CombineBwdArgs cb{dy, sv->y_perm, sv->slot, sv->topk_w, dO, dg, T, d, k, c->dtype};
+    StageTimer pt("bwd_combine", s);
+    if ((st = launch_status(moe::launch_combine_bwd(cb, s)))) return st;
+  }
+  // dA = act'(dO W2_e), rows of each expert (and dy ws2 for the shared expert)
+  moe::GemmArgs a2{};
+  a2.kind = 0;
+  a2.epi = c->act == MOE_ACT_SWIGLU ? moe::EPI_SWIGLU_BWD : moe::EPI_RELU_BWD;
+  a2.b_kcontig = 0;
+  a2.N = f; a2.K = d; a2.f = f;
+  a2.has_shared = sh ? 1 : 0;
+  a2.offsets = sv->expert_offsets; a2.E = E; a2.shared_rows = shr;
+  a2.max_row_tiles = row_tile_bound(c, R, shr);
+  a2.A = dO; a2.lda = d;
+  a2.B = w->w2; a2.ldb = f; a2.strideB = (int64_t)d * f;
+  a2.A_sh = dy; a2.B_sh = w->ws2;
+  a2.C = dA; a2.ldc = f1; a2.C_sh = dA_sh;
+  a2.X = sv->act_saved; a2.ldx = f1; a2.X_sh = sv->act_shared;
+  if ((st = gemm(c, a2, s, "bwd_dgrad2"))) return st;
+  // dW2_e = dO^T h over the expert's rows
+  moe::GemmArgs w2g{};
+  w2g.kind = 1;
+  w2g.epi = moe::EPI_STORE;
+  w2g.M = d; w2g.N = f;
+  w2g.has_shared = sh ? 1 : 0;
+  w2g.offsets = sv->expert_offsets; w2g.E = E; w2g.shared_rows = shr;
+  w2g.A = dO; w2g.lda = d;
+  w2g.B = sv->h_saved; w2g.ldb = f;
+  w2g.A_sh = dy; w2g.B_sh = sv->h_shared;
+  w2g.C = g->dw2; w2g.ldc = f; w2g.strideC = (int64_t)d * f; w2g.C_sh = g->dws2;
+  if ((st = gemm(c, w2g, s, "bwd_wgrad2"))) return st;
+  // dX_perm = dA W1_e
+  moe::GemmArgs a1{};
+  a1.kind = 0;
+  a1.epi = moe::EPI_STORE;
+  a1.b_kcontig = 0;
+  a1.N = d; a1.K = f1; a1.f = f;
+  a1.has_shared = sh ? 1 : 0;
+  a1.offsets = sv->expert_offsets; a1.E = E; a1.shared_rows = shr;
+  a1.max_row_tiles = row_tile_bound(c, R, shr);
+  a1.A = dA; a1.lda = f1;
+  a1.B = w->w1; a1.ldb = d; a1.strideB = (int64_t)f1 * d;
+  a1.A_sh = dA_sh; a1.B_sh = w->ws1;
+  a1.C = dXp; a1.ldc = d; a1.C_sh = dX_sh;
+  if ((st = gemm(c, a1, s, "bwd_dgrad1"))) return st;
+  // dW1_e = dA^T x_perm over the expert's rows
+  moe::GemmArgs w1g{};
+  w1g.kind = 1;
+  w1g.epi = moe::EPI_STORE;
+  w1g.M = f1; w1g.N = d;
+  w1g.has_shared = sh ? 1 : 0;
+  w1g.offsets = sv->expert_offsets; w1g.E = E; w1g.shared_rows = shr;
+  w1g.A = dA; w1g.lda = f1;
+  w1g.B = sv->x_perm; w1g.ldb = d;
+  w1g.A_sh = dA_sh; w1g.B_sh = sv->x;
+  w1g.C = g->dw1; w1g.ldc = d; w1g.strideC = (int64_t)f1 * d; w1g.C_sh = g->dws1;
+  if ((st = gemm(c, w1g, s, "bwd_wgrad1"))) return st;
+  // router: dlogits, dW_r, dx_router
+  if (T > 0) {
+    moe::DlogitsArgs dla{sv->probs, sv->topk_idx, sv->topk_w, dg, sv->expert_counts, dl, T, E, k, c->gate,
+                         c->renormalize ? 1 : 0, c->aux_alpha};
+    StageTimer pt("bwd_dlogits", s);
+    if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;
+  }
+  moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, T, d, E, c->dtype};
+  {
+    StageTimer pt("bwd_router_grads", s);
+    if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;
+  }
+  if (T > 0) {
+    moe::UnpermuteArgs ua{dy, dXp, sv->slot, dxr, dX_sh, g->dx, T, d, k, c->dtype};
+    StageTimer pt("bwd_unpermute", s);
+    if ((st = launch_status(moe::launch_unpermute_bwd(ua, s)))) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_profile_arm(const char* stage, void* const* events, int max_pairs) {
+  if (!events || max_pairs < 1) return MOE_ERR_INVALID_ARG;
+  if (stage && strlen(stage) >= sizeof(g_prof.only)) return MOE_ERR_INVALID_ARG;
+  g_prof.all = stage == nullptr;
+  if (stage) strcpy(g_prof.only, stage);
+  g_prof.ev = (hipEvent_t*)events;
+  g_prof.max = max_pairs < kMaxProfPairs ? max_pairs : kMaxProfPairs;
+  g_prof.n = 0;
+  g_prof.armed = true;
+  return MOE_OK;
+}
+
+int moe_profile_disarm(void) {
+  g_prof.armed = false;
+  return g_prof.n;
+}
+
+const char* moe_profile_stage(int i) { return (i >= 0 && i < g_prof.n) ? g_prof.names[i] : nullptr; }
+
+}  // extern "C"

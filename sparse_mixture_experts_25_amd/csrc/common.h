@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// 16-byte vector of raw bits.
+struct alignas(16) u128 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ u128 ld128(const void* p) {
+  u128 r;
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  return r;
+}
+__device__ __forceinline__ void st128(void* p, const u128& r) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+}
+__device__ __forceinline__ u128 zero128() {
+  u128 r;
+  r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0u;
+  return r;
+}
+
+// bf16 <-> fp32. The narrowing conversion rounds to nearest even (gfx950 has a
+// hardware convert for it).
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  bf16 h = (bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Element access for the two activation types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16 bytes
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+  __device__ static void unpack(const u128& r, float* v) {
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r.w[i]);
+  }
+  __device__ static u128 pack(const float* v) {
+    u128 r;
+    for (int i = 0; i < 4; ++i) r.w[i] = __float_as_uint(v[i]);
+    return r;
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+  __device__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+  __device__ static void unpack(const u128& r, float* v) {
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r.w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static u128 pack(const float* v) {
+    u128 r;
+    for (int i = 0; i < 4; ++i) r.w[i] = pack2bf(v[2 * i], v[2 * i + 1]);
+    return r;
+  }
+};
+
+// Wave-level reductions (fixed butterfly order, so results are reproducible).
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace moe

@@ -1,0 +1,141 @@
+// Host-side launch interfaces between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  const void* x;
+  const float* w_router;
+  const float* logit_offset;
+  const float* sel_bias;
+  float* probs;
+  int32_t* topk_idx;
+  float* topk_w;
+  int T, d, E, k, gate, renorm, dtype;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+
+struct DispatchArgs {
+  const void* x;
+  const int32_t* topk_idx;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot;
+  int32_t* row_token;
+  void* x_perm;
+  int32_t* ws_chunk;   // [nchunks, E] per-chunk expert counts
+  int T, d, E, k, capacity, elem_bytes;
+};
+int dispatch_num_chunks(int T, int k);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);
+
+// One grouped matmul launch.
+//  ragged-M kind (forward and input-gradient matmuls): for each group g,
+//    C[rows_g, N] = A[rows_g, K] * op(B_g), rows_g = [off[g], off[g+1]) of A and C.
+//    B_g is [N, K] (b_kcontig) or [K, N]. An optional extra dense group (the
+//    shared expert) has rows [0, shared_rows) of A_sh / C_sh and weight B_sh.
+//  ragged-K kind (weight gradients): for each group g,
+//    C_g[M, N] = sum over rows in [off[g], off[g+1]) of A[row, :M]^T (x) B[row, :N];
+//    the extra group sums over rows [0, shared_rows) of A_sh / B_sh into C_sh.
+enum GemmEpi {
+  EPI_STORE = 0,       // C = acc
+  EPI_RELU_FWD = 1,    // C = acc (pre-activation), C2 = max(acc, 0)
+  EPI_SWIGLU_FWD = 2,  // C = [gate | up] pre-activations, C2 = silu(gate) * up
+  EPI_RELU_BWD = 3,    // C = acc * (X > 0)
+  EPI_SWIGLU_BWD = 4,  // acc = dh; X = saved [gate | up]; C = [d gate | d up]
+};
+
+struct GemmArgs {
+  int kind;       // 0 ragged-M, 1 ragged-K
+  int epi;
+  int b_kcontig;  // ragged-M only
+  int M, N, K;    // ragged-M: N, K fixed. ragged-K: M, N fixed.
+  const int32_t* offsets;
+  int E;
+  int shared_rows;
+  int has_shared;         // 1: an extra dense group exists (it may have 0 rows)
+  int64_t max_row_tiles;  // ragged-M: upper bound on the number of row tiles
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb; int64_t strideB;
+  const void* A_sh; const void* B_sh;
+  void* C; int64_t ldc; int64_t strideC; void* C_sh;
+  void* C2; int64_t ldc2; void* C2_sh;
+  const void* X; int64_t ldx; const void* X_sh;
+  int f;  // SwiGLU half width
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+
+struct CombineArgs {
+  const void* x;
+  const void* y_perm;
+  const int32_t* slot;
+  const float* topk_w;
+  const void* y_shared;
+  void* y;
+  int T, d, k, dtype;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+struct AuxArgs {
+  const float* probs;
+  const int32_t* counts;
+  float* aux_out;
+  float* ws_partial;  // [nblk, E]
+  int T, E, k;
+  float alpha;
+};
+int aux_num_blocks(int T);
+hipError_t launch_aux(const AuxArgs& a, hipStream_t st);
+
+// Backward pieces.
+struct CombineBwdArgs {
+  const void* dy;
+  const void* y_perm;
+  const int32_t* slot;
+  const float* topk_w;
+  void* dO;      // [R, d]
+  float* dg;     // [T, k]
+  int T, d, k, dtype;
+};
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st);
+
+struct DlogitsArgs {
+  const float* probs;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const float* dg;
+  const int32_t* counts;
+  float* dlogits;  // [T, E]
+  int T, E, k, gate, renorm;
+  float alpha;
+};
+hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st);
+
+struct RouterGradArgs {
+  const float* dlogits;  // [T, E]
+  const void* x;         // [T, d] act
+  const float* w_router; // [E, d]
+  float* dw_router;      // [E, d]
+  float* dx_router;      // [T, d]
+  float* ws_partial;     // [nsplit, E, d]
+  int T, d, E, dtype;
+};
+int router_grad_splits(int T);
+hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st);
+
+struct UnpermuteArgs {
+  const void* dy;
+  const void* dX_perm;
+  const int32_t* slot;
+  const float* dx_router;
+  const void* dx_shared;
+  void* dx;
+  int T, d, k, dtype;
+};
+hipError_t launch_unpermute_bwd(const UnpermuteArgs& a, hipStream_t st);
+
+}  // namespace moe

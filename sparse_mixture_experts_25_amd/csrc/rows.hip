@@ -1,0 +1,384 @@
+// Row-streaming kernels of the layer: combine, aux loss, and the backward
+// pieces around the expert matmuls (combine backward, router gradient,
+// unpermute backward).
+//
+// [SW] = "Mixture of Experts (MoE) を1から解説 — Switch Transformerのルーティングと負荷分散"
+// (ta-paperlens.web.app): eq. (2) (gate-weighted sum over the selected
+// experts; the router is trained through the gate), the capacity section
+// (dropped tokens pass through on the residual), eq. (4) and the numpy sketch
+// after it (aux loss; f is a count, P a mean probability).
+// [WIKI] = "Mixture-of-Experts" (notes.yuuk.io): sigmoid gate with a bias used
+// only for selection; shared expert.
+//
+// All of these are HBM-bound gathers/scatters of whole rows: one wave per
+// token row, 16-byte vectors, fp32 accumulation, and no atomics, so every
+// result is reproducible bit for bit.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+// y[t] = x[t] + sum_kept w[t,r] * y_perm[slot[t,r]] (+ y_shared[t])
+template <typename TX>
+__global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, const TX* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ slot,
+                                                      const float* __restrict__ topk_w,
+                                                      const TX* __restrict__ y_shared, TX* __restrict__ y,
+                                                      int T, int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int nvec = d / V;
+  for (int v = lane; v < nvec; v += 64) {
+    float acc[V], tmp[V];
+    Elem<TX>::unpack(ld128(x + (int64_t)t * d + v * V), acc);
+    for (int r = 0; r < k; ++r) {
+      const int s = slot[(int64_t)t * k + r];
+      if (s < 0) continue;
+      const float w = topk_w[(int64_t)t * k + r];
+      Elem<TX>::unpack(ld128(y_perm + (int64_t)s * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = __builtin_fmaf(w, tmp[e], acc[e]);
+    }
+    if (y_shared) {
+      Elem<TX>::unpack(ld128(y_shared + (int64_t)t * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    st128(y + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  }
+}
+
+constexpr int kAuxTok = 256;
+
+__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ probs, int T, int E,
+                                                          float* __restrict__ partial) {
+  const int t0 = blockIdx.x * kAuxTok;
+  const int t1 = min(T, t0 + kAuxTok);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float s = 0.0f;
+    for (int t = t0; t < t1; ++t) s += probs[(int64_t)t * E + e];
+    partial[(int64_t)blockIdx.x * E + e] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ partial, int nblk,
+                                                        const int32_t* __restrict__ counts, int T, int E,
+                                                        int k, float alpha, float* __restrict__ out) {
+  __shared__ float red[4];
+  float acc = 0.0f;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float P = 0.0f;
+    for (int b = 0; b < nblk; ++b) P += partial[(int64_t)b * E + e];
+    P /= (float)T;
+    const float f = (float)counts[e] / ((float)T * (float)k);
+    acc += f * P;
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float s = (red[0] + red[1]) + (red[2] + red[3]);
+    out[0] = (T == 0 || alpha == 0.0f) ? 0.0f : alpha * (float)E * s;
+  }
+}
+
+// dO[slot] = w * dy[t]; dg[t,r] = <dy[t], y_perm[slot]> (0 when dropped)
+template <typename TX>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const TX* __restrict__ dy, const TX* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ slot,
+                                                          const float* __restrict__ topk_w, TX* __restrict__ dO,
+                                                          float* __restrict__ dg, int T, int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int nvec = d / V;
+  for (int r = 0; r < k; ++r) {
+    const int s = slot[(int64_t)t * k + r];
+    if (s < 0) {
+      if (lane == 0) dg[(int64_t)t * k + r] = 0.0f;
+      continue;
+    }
+    const float w = topk_w[(int64_t)t * k + r];
+    float dot = 0.0f;
+    for (int v = lane; v < nvec; v += 64) {
+      float g[V], yv[V], o[V];
+      Elem<TX>::unpack(ld128(dy + (int64_t)t * d + v * V), g);
+      Elem<TX>::unpack(ld128(y_perm + (int64_t)s * d + v * V), yv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        dot = __builtin_fmaf(g[e], yv[e], dot);
+        o[e] = w * g[e];
+      }
+      st128(dO + (int64_t)s * d + v * V, Elem<TX>::pack(o));
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dg[(int64_t)t * k + r] = dot;
+  }
+}
+
+// Router logit gradient for one token per wave: gate path + aux path.
+__global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ probs,
+                                                      const int32_t* __restrict__ topk_idx,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ dg,
+                                                      const int32_t* __restrict__ counts,
+                                                      float* __restrict__ dlogits, int T, int E, int k, int gate,
+                                                      int renorm, float alpha) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* p = probs + (int64_t)t * E;
+  const int32_t* it = topk_idx + (int64_t)t * k;
+  const float* wt = topk_w + (int64_t)t * k;
+  const float* gt = dg + (int64_t)t * k;
+  // token-level sums over the k selected
+  float S = 0.0f, wdg = 0.0f, ssum = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    const float pe = p[it[r]];
+    S += gt[r] * pe;
+    wdg += wt[r] * gt[r];
+    ssum += pe;
+  }
+  const float c = alpha * (float)E / (float)T;
+  const float invTk = 1.0f / ((float)T * (float)k);
+  float fp = 0.0f;
+  if (alpha != 0.0f) {
+    for (int j = lane; j < E; j += 64) fp += (float)counts[j] * invTk * p[j];
+    fp = wave_sum(fp);
+  }
+  for (int j = lane; j < E; j += 64) {
+    const float pj = p[j];
+    int rsel = -1;
+    for (int r = 0; r < k; ++r)
+      if (it[r] == j) rsel = r;
+    float v = 0.0f;
+    if (gate == MOE_GATE_SOFTMAX) {
+      if (!renorm) {
+        v = (rsel >= 0 ? gt[rsel] * pj : 0.0f) - pj * S;
+      } else if (rsel >= 0) {
+        v = wt[rsel] * (gt[rsel] - wdg);
+      }
+      if (alpha != 0.0f) v += c * pj * ((float)counts[j] * invTk - fp);
+    } else {
+      if (rsel >= 0) {
+        const float ds = renorm ? (gt[rsel] - wdg) / ssum : gt[rsel];
+        v = ds * pj * (1.0f - pj);
+      }
+      if (alpha != 0.0f) v += c * (float)counts[j] * invTk * pj * (1.0f - pj);
+    }
+    dlogits[(int64_t)t * E + j] = v;
+  }
+}
+
+// C[M,N] (+)= sum_k A[k,m] * B[k,n] over one chunk of k (fp32 SIMT, 64x64 tiles).
+// A: fp32 [K][M] (row stride lda); B: TB [K][N]. Partial results per K chunk go
+// to part[split][M][N]; a second kernel sums the chunks in a fixed order.
+constexpr int kRG = 64, kRK = 16;
+template <typename TB>
+__global__ __launch_bounds__(256) void gemm_tn_split_kernel(const float* __restrict__ A, int64_t lda,
+                                                            const TB* __restrict__ B, int64_t ldb, int M,
+                                                            int N, int K, int kchunk, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float As[kRK][kRG + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[kRK][kRG + 4];
+  const int nN = (N + kRG - 1) / kRG;
+  const int mb = blockIdx.x / nN, nb = blockIdx.x % nN;
+  const int ks = blockIdx.y * kchunk, ke = min(K, ks + kchunk);
+  const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+  float acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = ks; k0 < ke; k0 += kRK) {
+    __syncthreads();
+    for (int u = tid; u < kRK * kRG; u += 256) {
+      const int kk = u / kRG, c = u % kRG;
+      const int k = k0 + kk;
+      const int m = mb * kRG + c, n = nb * kRG + c;
+      As[kk][c] = (k < ke && m < M) ? A[(int64_t)k * lda + m] : 0.0f;
+      Bs[kk][c] = (k < ke && n < N) ? Elem<TB>::load(B, (int64_t)k * ldb + n) : 0.0f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kRK; ++kk) {
+      float av[4], bv[4];
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][tm * 4 + i];
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tn * 4 + j];
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+  }
+  float* out = part + (int64_t)blockIdx.y * M * N;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int m = mb * kRG + tm * 4 + i, n = nb * kRG + tn * 4 + j;
+      if (m < M && n < N) out[(int64_t)m * N + n] = acc[i][j];
+    }
+}
+
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int nsplit,
+                                                         int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int p = 0; p < nsplit; ++p) s += part[(int64_t)p * n + i];
+  out[i] = s;
+}
+
+// C[M,N] = A[M,K] * B[K,N], all fp32 row-major (dx_router = dlogits * W_r).
+__global__ __launch_bounds__(256) void gemm_nn_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                          float* __restrict__ C, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) float As[kRK][kRG + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[kRK][kRG + 4];
+  const int nN = (N + kRG - 1) / kRG;
+  const int mb = blockIdx.x / nN, nb = blockIdx.x % nN;
+  const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+  float acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kRK) {
+    __syncthreads();
+    for (int u = tid; u < kRK * kRG; u += 256) {
+      const int kk = u % kRK, r = u / kRK;
+      const int m = mb * kRG + r, k = k0 + kk;
+      As[kk][r] = (m < M && k < K) ? A[(int64_t)m * K + k] : 0.0f;
+      const int kk2 = u / kRG, c = u % kRG;
+      const int n = nb * kRG + c, k2 = k0 + kk2;
+      Bs[kk2][c] = (n < N && k2 < K) ? B[(int64_t)k2 * N + n] : 0.0f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kRK; ++kk) {
+      float av[4], bv[4];
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][tm * 4 + i];
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tn * 4 + j];
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int m = mb * kRG + tm * 4 + i, n = nb * kRG + tn * 4 + j;
+      if (m < M && n < N) C[(int64_t)m * N + n] = acc[i][j];
+    }
+}
+
+// dx[t] = dy[t] + sum_kept dX_perm[slot] + dx_router[t] (+ dx_shared[t])
+template <typename TX>
+__global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict__ dy,
+                                                            const TX* __restrict__ dX_perm,
+                                                            const int32_t* __restrict__ slot,
+                                                            const float* __restrict__ dx_router,
+                                                            const TX* __restrict__ dx_shared, TX* __restrict__ dx,
+                                                            int T, int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int nvec = d / V;
+  for (int v = lane; v < nvec; v += 64) {
+    float acc[V], tmp[V];
+    Elem<TX>::unpack(ld128(dy + (int64_t)t * d + v * V), acc);
+    for (int r = 0; r < k; ++r) {
+      const int s = slot[(int64_t)t * k + r];
+      if (s < 0) continue;
+      Elem<TX>::unpack(ld128(dX_perm + (int64_t)s * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    if (dx_router) {
+      const float* pr = dx_router + (int64_t)t * d + v * V;
+#pragma unroll
+      for (int e = 0; e < V; e += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(pr + e);
+        acc[e] += q.x; acc[e + 1] += q.y; acc[e + 2] += q.z; acc[e + 3] += q.w;
+      }
+    }
+    if (dx_shared) {
+      Elem<TX>::unpack(ld128(dx_shared + (int64_t)t * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    st128(dx + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  const dim3 grid((a.T + 3) / 4);
+  if (a.dtype == MOE_DT_BF16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.x,
+                       (const uint16_t*)a.y_perm, a.slot, a.topk_w, (const uint16_t*)a.y_shared,
+                       (uint16_t*)a.y, a.T, a.d, a.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, (const float*)a.x, (const float*)a.y_perm,
+                       a.slot, a.topk_w, (const float*)a.y_shared, (float*)a.y, a.T, a.d, a.k);
+  return hipGetLastError();
+}
+
+int aux_num_blocks(int T) { return (T + kAuxTok - 1) / kAuxTok; }
+
+hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
+  const int nblk = (a.alpha == 0.0f) ? 0 : aux_num_blocks(a.T);
+  if (nblk > 0)
+    hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, st, a.probs, a.T, a.E, a.ws_partial);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, st, a.ws_partial, nblk, a.counts, a.T, a.E, a.k,
+                     a.alpha, a.aux_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
+  const dim3 grid((a.T + 3) / 4);
+  if (a.dtype == MOE_DT_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.dy,
+                       (const uint16_t*)a.y_perm, a.slot, a.topk_w, (uint16_t*)a.dO, a.dg, a.T, a.d, a.k);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, st, (const float*)a.dy,
+                       (const float*)a.y_perm, a.slot, a.topk_w, (float*)a.dO, a.dg, a.T, a.d, a.k);
+  return hipGetLastError();
+}
+
+hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(dlogits_kernel, dim3((a.T + 3) / 4), dim3(256), 0, st, a.probs, a.topk_idx, a.topk_w, a.dg,
+                     a.counts, a.dlogits, a.T, a.E, a.k, a.gate, a.renorm, a.alpha);
+  return hipGetLastError();
+}
+
+int router_grad_splits(int T) { return (T + 1023) / 1024; }
+
+hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
+  const int ns = router_grad_splits(a.T);
+  const int tiles = ((a.E + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
+  if (ns == 0) {
+  } else if (a.dtype == MOE_DT_BF16)
+    hipLaunchKernelGGL(gemm_tn_split_kernel<uint16_t>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits,
+                       (int64_t)a.E, (const uint16_t*)a.x, (int64_t)a.d, a.E, a.d, a.T, 1024, a.ws_partial);
+  else
+    hipLaunchKernelGGL(gemm_tn_split_kernel<float>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits, (int64_t)a.E,
+                       (const float*)a.x, (int64_t)a.d, a.E, a.d, a.T, 1024, a.ws_partial);
+  const int64_t n = (int64_t)a.E * a.d;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns, n,
+                     a.dw_router);
+  const int tiles2 = ((a.T + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
+  if (tiles2 > 0)
+    hipLaunchKernelGGL(gemm_nn_f32_kernel, dim3(tiles2), dim3(256), 0, st, a.dlogits, a.w_router, a.dx_router, a.T,
+                     a.d, a.E);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_bwd(const UnpermuteArgs& a, hipStream_t st) {
+  const dim3 grid((a.T + 3) / 4);
+  if (a.dtype == MOE_DT_BF16)
+    hipLaunchKernelGGL(unpermute_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.dy,
+                       (const uint16_t*)a.dX_perm, a.slot, a.dx_router, (const uint16_t*)a.dx_shared,
+                       (uint16_t*)a.dx, a.T, a.d, a.k);
+  else
+    hipLaunchKernelGGL(unpermute_bwd_kernel<float>, grid, dim3(256), 0, st, (const float*)a.dy,
+                       (const float*)a.dX_perm, a.slot, a.dx_router, (const float*)a.dx_shared, (float*)a.dx,
+                       a.T, a.d, a.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+"""Shared helpers for the parity tests: config conversion, the error metric,
+running the GPU path through the C ABI, and running the oracle on the same bytes."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import sparse_mixture_experts_25_amd as M
+
+TOL_BF16 = 2e-2   # bf16 activations / weights with fp32 accumulation
+TOL_F32 = 1e-5    # fp32 router outputs and the fp32 layer
+
+
+def cfg_of(c, T=None):
+    return M.make_config(c.T if T is None else T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate,
+                         act=c.act, dtype=c.dtype, alpha=c.alpha, shared=c.shared)
+
+
+def relerr(a, r, mask=None) -> float:
+    """max_i |a_i - r_i| / max(|r_i|, rms(r)) over the (optionally masked) elements."""
+    a = np.asarray(a, np.float64).reshape(-1)
+    r = np.asarray(r, np.float64).reshape(-1)
+    if mask is not None:
+        m = np.asarray(mask, bool).reshape(-1)
+        a, r = a[m], r[m]
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    den = np.maximum(np.abs(r), max(rms, 1e-30))
+    return float(np.max(np.abs(a - r) / den))
+
+
+def tol_for(c):
+    return TOL_F32 if c.dtype == "f32" else TOL_BF16
+
+
+def to_dev(inp: dict, device="cuda") -> dict:
+    return {k: v.to(device) for k, v in inp.items()}
+
+
+def host64(t) -> np.ndarray:
+    return O.f64(t)
+
+
+def run_forward(c, inp_dev: dict, backward: bool = True):
+    cfg = cfg_of(c)
+    buf = M.LayerBuffers.allocate(cfg, backward=backward)
+    M.forward(buf, inp_dev, aux=True)
+    return buf
+
+
+def run_backward(buf, inp_dev, saved=None):
+    M.backward(buf, inp_dev, inp_dev["dy"], saved=saved)
+
+
+def gpu_saved_from_oracle(c, fw: dict, info, device="cuda") -> dict:
+    """The oracle's forward tensors in the layout the ABI expects (for stage-isolated backward tests)."""
+    dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    R = max(int(info.max_rows), 1)
+    n = int(fw["n_rows"])
+
+    def rows(a, width):
+        out = torch.zeros((R, width), dtype=torch.float64)
+        if n:
+            out[:n] = torch.from_numpy(np.ascontiguousarray(a[:n]))
+        return out.to(dt).to(device)
+
+    f1 = 2 * c.f if c.act == "swiglu" else c.f
+    sv = dict(
+        probs=torch.from_numpy(fw["probs"]).float().to(device),
+        topk_idx=torch.from_numpy(fw["idx"]).to(device),
+        topk_w=torch.from_numpy(fw["w"]).float().to(device),
+        slot=torch.from_numpy(fw["slot"]).to(device),
+        expert_counts=torch.from_numpy(fw["counts"]).to(device),
+        expert_offsets=torch.from_numpy(fw["offsets"]).to(device),
+        x_perm=rows(fw["x_perm"], c.d), act_saved=rows(fw["act"], f1), h_saved=rows(fw["h"], c.f),
+        y_perm=rows(fw["y_perm"], c.d),
+    )
+    if c.shared:
+        sv["act_shared"] = torch.from_numpy(fw["act_shared"]).to(dt).to(device)
+        sv["h_shared"] = torch.from_numpy(fw["h_shared"]).to(dt).to(device)
+    return sv
+
+
+def oracle_inputs(inp: dict) -> dict:
+    return {k: host64(v) for k, v in inp.items()}

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, element by
+element, on reduced versions of the five workloads (several GEMM tiles and a
+ragged tail each), plus edge cases. Routing decisions, positions and drop masks
+must match bit for bit; floating outputs within 2e-2 (bf16 path) or 1e-5 (fp32
+router outputs, fp32 layer) in the max relative error of helpers.relerr."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_25_amd as M
+from synth import CONFIGS, SMALL, LayerConfig, make_inputs
+
+from helpers import (TOL_BF16, TOL_F32, cfg_of, gpu_saved_from_oracle, host64, oracle_inputs, relerr,
+                     run_backward, run_forward, to_dev, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+# reduced workloads, plus an fp32 variant with backward and aux loss
+CASES = dict(SMALL)
+CASES["tiny_f32_bwd"] = CONFIGS["tiny_f32"].replace(name="tiny_f32_bwd", k=2, renorm=True, fwd_only=False,
+                                                    alpha=0.01, cf=1.25)
+CASES["swiglu_f32_shared"] = SMALL["deepseek_v3"].replace(name="swiglu_f32_shared", dtype="f32", T=130)
+
+
+def _forward_both(c, seed=0):
+    inp = make_inputs(c, seed=seed)
+    dev = to_dev(inp)
+    buf = run_forward(c, dev, backward=not c.fwd_only)
+    torch.cuda.synchronize()
+    spec = O.Spec.of(c)
+    fw = O.forward(spec, oracle_inputs(inp))
+    return inp, dev, buf, spec, fw
+
+
+def _check_routing(buf, fw, n):
+    t = buf.t
+    np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), fw["idx"])
+    np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), fw["counts"])
+    np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), fw["offsets"])
+    np.testing.assert_array_equal(t["slot"].cpu().numpy(), fw["slot"])
+    np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), fw["row_token"][:n])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_parity(name):
+    c = CASES[name]
+    print(f"[forward parity] {name} T={c.T} d={c.d} f={c.f} E={c.E} k={c.k}", flush=True)
+    inp, dev, buf, spec, fw = _forward_both(c)
+    t = buf.t
+    n = int(fw["n_rows"])
+    _check_routing(buf, fw, n)
+    assert relerr(host64(t["probs"]), fw["probs"]) <= TOL_F32
+    assert relerr(host64(t["topk_w"]), fw["w"]) <= TOL_F32
+    # the permutation is a bitwise row copy
+    np.testing.assert_array_equal(host64(t["x_perm"][:n]), fw["x_perm"])
+    tol = tol_for(c)
+    assert relerr(host64(t["act_saved"][:n]), fw["act"]) <= tol
+    assert relerr(host64(t["h_saved"][:n]), fw["h"]) <= tol
+    assert relerr(host64(t["y_perm"][:n]), fw["y_perm"]) <= tol
+    assert relerr(host64(t["y"]), fw["y"]) <= tol
+    if c.shared:
+        assert relerr(host64(t["y_shared"]), fw["y_shared"]) <= tol
+    if c.alpha:
+        assert abs(float(t["aux"][0]) - fw["aux"]) <= TOL_F32 * abs(fw["aux"])
+    # tokens whose every choice was dropped leave the layer unchanged, bit for bit
+    if not c.shared:
+        gone = np.all(fw["slot"] < 0, axis=1)
+        np.testing.assert_array_equal(host64(t["y"])[gone], host64(inp["x"])[gone])
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].fwd_only])
+def test_backward_parity_stage_isolated(name):
+    """moe_backward fed the oracle's forward tensors: both sides see the same
+    saved pre-activations, so every element is comparable."""
+    c = CASES[name]
+    print(f"[backward isolated] {name}", flush=True)
+    inp, dev, buf, spec, fw = _forward_both(c)
+    saved = gpu_saved_from_oracle(c, fw, buf.info)
+    run_backward(buf, dev, saved=saved)
+    torch.cuda.synchronize()
+    bw = O.backward(spec, oracle_inputs(inp), fw, host64(inp["dy"]))
+    t = buf.t
+    tol = tol_for(c)
+    assert relerr(host64(t["dx"]), bw["dx"]) <= tol
+    assert relerr(host64(t["dw1"]), bw["dw1"]) <= tol
+    assert relerr(host64(t["dw2"]), bw["dw2"]) <= tol
+    assert relerr(host64(t["dw_router"]), bw["dw_router"]) <= TOL_F32
+    if c.shared:
+        assert relerr(host64(t["dws1"]), bw["dws1"]) <= tol
+        assert relerr(host64(t["dws2"]), bw["dws2"]) <= tol
+    # experts without rows get exact zeros
+    empty = np.diff(fw["offsets"]) == 0
+    if empty.any():
+        assert np.all(host64(t["dw1"])[empty] == 0) and np.all(host64(t["dw2"])[empty] == 0)
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].fwd_only])
+def test_backward_parity_end_to_end(name):
+    """GPU forward -> GPU backward against oracle forward -> oracle backward.
+    Where a ReLU pre-activation is within rounding of zero (|a| <= 1e-4) both
+    masks are correct results; the gradients that depend on such an element are
+    left out of the element comparison (they are covered by the stage-isolated test)."""
+    c = CASES[name]
+    print(f"[backward e2e] {name}", flush=True)
+    inp, dev, buf, spec, fw = _forward_both(c)
+    run_backward(buf, dev)
+    torch.cuda.synchronize()
+    bw = O.backward(spec, oracle_inputs(inp), fw, host64(inp["dy"]))
+    t = buf.t
+    tol = tol_for(c)
+    n = int(fw["n_rows"])
+    if c.act == "relu":
+        amb = np.abs(fw["act"]) <= 1e-4
+    else:
+        amb = np.zeros_like(fw["act"], bool)
+    row_ok = ~amb.any(1)
+    tok_ok = np.ones(c.T, bool)
+    for tt, r in zip(*np.nonzero(fw["slot"] >= 0)):
+        if not row_ok[fw["slot"][tt, r]]:
+            tok_ok[tt] = False
+    assert relerr(host64(t["dx"]), bw["dx"], np.repeat(tok_ok[:, None], c.d, 1)) <= tol
+    # dW1 rows i of expert e are comparable if no row of e is ambiguous at column i
+    f1 = fw["act"].shape[1]
+    m1 = np.ones((c.E, f1, c.d), bool)
+    for e in range(c.E):
+        a, b = fw["offsets"][e], fw["offsets"][e + 1]
+        bad_cols = amb[a:b].any(0)
+        m1[e, bad_cols, :] = False
+    assert relerr(host64(t["dw1"]), bw["dw1"], m1) <= tol
+    assert relerr(host64(t["dw2"]), bw["dw2"]) <= tol
+    assert relerr(host64(t["dw_router"]), bw["dw_router"]) <= tol
+    if c.shared:
+        assert relerr(host64(t["dws1"]), bw["dws1"]) <= tol
+        assert relerr(host64(t["dws2"]), bw["dws2"]) <= tol
+
+
+def test_determinism_bitwise():
+    c = SMALL["finegrained_top8"]
+    inp = to_dev(make_inputs(c))
+    outs = []
+    for _ in range(2):
+        buf = run_forward(c, inp)
+        run_backward(buf, inp)
+        torch.cuda.synchronize()
+        outs.append({k: v.clone() for k, v in buf.t.items() if k != "ws"})
+    for k in outs[0]:
+        if k in ("row_token", "x_perm", "act_saved", "h_saved", "y_perm"):
+            n = int(outs[0]["expert_offsets"][-1])
+            assert torch.equal(outs[0][k][:n], outs[1][k][:n]), k
+        else:
+            assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+def test_sigmoid_contract_bitwise():
+    # one-hot router rows make each logit equal an input value exactly
+    # (x*1 then + x'*0 terms are exact), so probs = sigmoid_contract(x) bit for bit
+    vals = np.linspace(-30, 30, 8 * 4096, dtype=np.float32)
+    vals = np.concatenate([vals, np.array([0, -0.0, 1e-30, -1e-30, 86, -86, 87, -87, 20, -20], np.float32)])
+    E, d = 8, 8
+    T = len(vals) // E
+    vals = vals[:T * E]
+    c = LayerConfig("sig", T=T, d=d, f=8, E=E, k=2, gate="sigmoid_bias", renorm=True, dtype="f32", cf=0.0)
+    x = torch.from_numpy(vals.reshape(T, E).copy())
+    wr = torch.eye(E, d)
+    cfg = cfg_of(c)
+    probs = torch.empty(T, E, device="cuda")
+    idx = torch.empty(T, 2, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, 2, device="cuda")
+    M.moe_route(cfg, x.cuda(), wr.cuda(), None, None, probs, idx, w)
+    torch.cuda.synchronize()
+    got = probs.cpu().numpy().reshape(-1)
+    ref = np.array([O.sigmoid_contract(float(v)) for v in vals], np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_routing_ties_lowest_index():
+    # duplicated router rows give exactly equal logits; the lower expert index wins
+    c = LayerConfig("ties", T=512, d=64, f=64, E=16, k=4, renorm=True, dtype="bf16", cf=0.0)
+    inp = make_inputs(c, seed=3)
+    wr = inp["w_router"].clone()
+    for e in range(1, 16, 2):
+        wr[e] = wr[e - 1]
+    wr[5] = 0
+    wr[9] = 0
+    inp["w_router"] = wr
+    dev = to_dev(inp)
+    buf = run_forward(c, dev, backward=False)
+    torch.cuda.synchronize()
+    fw = O.forward(O.Spec.of(c), oracle_inputs(inp))
+    _check_routing(buf, fw, int(fw["n_rows"]))
+
+
+def test_zero_router_all_to_expert0():
+    c = CONFIGS["tiny_f32"].replace(alpha=0.01)
+    inp = make_inputs(c)
+    inp["w_router"] = torch.zeros_like(inp["w_router"])
+    dev = to_dev(inp)
+    buf = run_forward(c, dev, backward=False)
+    torch.cuda.synchronize()
+    t = buf.t
+    assert float(t["aux"][0]) == np.float32(0.01)
+    assert torch.all(t["topk_idx"] == 0)
+    slot = t["slot"].cpu().numpy()[:, 0]
+    assert np.all(slot[:64] == np.arange(64)) and np.all(slot[64:] == -1)
+    assert torch.equal(t["y"][64:].cpu(), inp["x"][64:])
+
+
+def test_empty_batch():
+    c = SMALL["switch_base"].replace(T=0)
+    inp = to_dev(make_inputs(c))
+    buf = run_forward(c, inp)
+    run_backward(buf, inp)
+    torch.cuda.synchronize()
+    assert int(buf.t["expert_offsets"][-1]) == 0
+    assert torch.all(buf.t["dw1"] == 0) and torch.all(buf.t["dw2"] == 0)
+    assert torch.all(buf.t["dw_router"] == 0)
+    assert float(buf.t["aux"][0]) == 0.0
+
+
+def test_caller_supplied_routing():
+    # moe_dispatch takes any topk_idx (e.g. a replayed routing)
+    c = SMALL["gshard_top2"]
+    inp = make_inputs(c, seed=5)
+    dev = to_dev(inp)
+    cfg = cfg_of(c)
+    buf = M.LayerBuffers.allocate(cfg, backward=False)
+    g = torch.Generator().manual_seed(1)
+    idx = torch.stack([torch.randperm(c.E, generator=g)[:c.k] for _ in range(c.T)]).to(torch.int32)
+    t = buf.t
+    M.moe_dispatch(cfg, dev["x"], idx.cuda(), t["expert_counts"], t["expert_offsets"], t["slot"], t["row_token"],
+                   t["x_perm"], t["ws"])
+    torch.cuda.synchronize()
+    C = O.capacity(c.T, c.E, c.cf)
+    counts, offsets, slot, row_token = O.positions(idx.numpy(), c.E, C)
+    np.testing.assert_array_equal(t["slot"].cpu().numpy(), slot)
+    np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), offsets)
+    n = int(offsets[-1])
+    np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), row_token[:n])
