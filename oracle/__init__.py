@@ -45,7 +45,7 @@ def build(quiet: bool = True) -> str:
     """Compile the oracle with g++ (no HIP, no GPU headers)."""
     import subprocess
     cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared",
-           "-ffp-contract=off", "-fno-fast-math", SRC_PATH, "-o", LIB_PATH + ".tmp"]
+           "-ffp-contract=off", "-fno-fast-math", "-mfma", SRC_PATH, "-o", LIB_PATH + ".tmp"]
     subprocess.run(cmd, check=True, capture_output=quiet)
     os.replace(LIB_PATH + ".tmp", LIB_PATH)
     return LIB_PATH
@@ -74,7 +74,8 @@ def lib():
             "orc_combine_bwd": (None, [i, i, i, i, D, D, I, D, D, D]),
             "orc_ffn_bwd": (None, [i, i, i, i, i, D, D, D, D, D, D]),
             "orc_wgrad": (None, [i, i, i, i, D, D, D]),
-            "orc_router_dlogits": (None, [i, i, i, i, i, d, D, I, D, D, I, D]),
+            "orc_router_dlogits": (None, [i, i, i, i, i, i, d, D, I, D, D, I, D]),
+            "orc_round_array": (None, [i, ctypes.c_int64, D, D]),
             "orc_router_grads": (None, [i, i, i, i, D, D, D, D, D]),
             "orc_unpermute_bwd": (None, [i, i, i, i, D, D, I, D, D, D]),
         }
@@ -216,12 +217,21 @@ def wgrad(mode, G, V):
     return dW
 
 
-def router_dlogits(probs, idx, w, dg, counts, gate, renorm, alpha):
+def router_dlogits(probs, idx, w, dg, counts, gate, renorm, alpha, T_batch=None):
+    """Logit gradient of the given token rows; T_batch (default: the number of
+    rows) is the batch size the aux loss is normalised by."""
     T, E = probs.shape
     k = idx.shape[1]
     out = np.empty((T, E), np.float64)
-    lib().orc_router_dlogits(T, E, k, gate, int(renorm), float(alpha), _d(probs), _i(idx),
-                             _d(w), _d(dg), _i(counts), _d(out))
+    lib().orc_router_dlogits(T, T if T_batch is None else int(T_batch), E, k, gate, int(renorm), float(alpha),
+                             _d(probs), _i(idx), _d(w), _d(dg), _i(counts), _d(out))
+    return out
+
+
+def round_array(mode, a):
+    a = np.ascontiguousarray(a, np.float64)
+    out = np.empty_like(a)
+    lib().orc_round_array(mode, a.size, _d(a), _d(out))
     return out
 
 

@@ -118,6 +118,12 @@ float sigmoid_c(float h) {
 extern "C" {
 
 double orc_round_bf16(double v) { return round_bf16(v); }
+
+// Elementwise rounding of n values at a storage precision (mode as above).
+void orc_round_array(int mode, int64_t n, const double* in, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = rnd(mode, in[i]);
+}
 float orc_exp_contract(float x) { return exp_c(x); }
 float orc_sigmoid_contract(float x) { return sigmoid_c(x); }
 
@@ -399,7 +405,9 @@ void orc_wgrad(int mode, int n, int M, int N, const double* G, const double* V, 
 //  dh_j += (alpha * E / T) * sum_i f_i * dp_i/dh_j, i.e.
 //  softmax: (alpha E / T) * p_j * (f_j - sum_i f_i p_i);  sigmoid: (alpha E / T) f_j s_j (1 - s_j).
 // The selection bias and the fixed logit offsets receive no gradient.
-void orc_router_dlogits(int T, int E, int k, int gate, int renorm, double alpha,
+// T: tokens to process (rows of probs/idx/w/dg/dlogits); T_batch: the batch size
+// that normalises f and P in the aux loss (equal to T for a whole batch).
+void orc_router_dlogits(int T, int T_batch, int E, int k, int gate, int renorm, double alpha,
                         const double* probs, const int* idx, const double* w,
                         const double* dg, const int* counts, double* dlogits) {
 #pragma omp parallel for schedule(static)
@@ -440,11 +448,11 @@ void orc_router_dlogits(int T, int E, int k, int gate, int renorm, double alpha,
       }
     }
     if (alpha != 0.0) {
-      double c = alpha * (double)E / (double)T;
+      double c = alpha * (double)E / (double)T_batch;
       double fp = 0.0;
-      for (int i = 0; i < E; ++i) fp += (double)counts[i] / ((double)T * k) * p[i];
+      for (int i = 0; i < E; ++i) fp += (double)counts[i] / ((double)T_batch * k) * p[i];
       for (int j = 0; j < E; ++j) {
-        double fj = (double)counts[j] / ((double)T * k);
+        double fj = (double)counts[j] / ((double)T_batch * k);
         if (gate == GATE_SOFTMAX) o[j] += c * p[j] * (fj - fp);
         else o[j] += c * fj * p[j] * (1.0 - p[j]);
       }

@@ -1,0 +1,206 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (same inputs: seeded, drawn on the GPU, same ABI calls).
+
+What the oracle computes exactly at these sizes:
+  * routing for every token (fp32 logit contract, gate, top-k), capacity,
+    positions, slots, drop masks, counts, offsets: bit for bit; probabilities,
+    gate weights and the aux loss within 1e-5;
+  * sampled rows of three experts (largest, median and smallest non-empty) and
+    of the shared expert: pre-activations, activations, expert outputs, and their
+    backward (activation and input gradients) within 2e-2;
+  * sampled tokens: layer output and input gradient within 2e-2 (every expert
+    row of the token recomputed by the oracle, plus the router gradient path);
+  * sampled weight-gradient elements of two experts and of the shared expert,
+    each summed by the oracle over all of that expert's rows.
+And properties that hold at any size: x_perm rows are bitwise copies of x rows;
+experts without rows get exactly zero weight gradients; for softmax gates each
+column of the router weight gradient sums to ~0 (the softmax Jacobian rows and
+the aux gradient rows sum to zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_25_amd as M
+from synth import CONFIGS, ORDER, make_inputs
+
+from helpers import TOL_BF16, TOL_F32, cfg_of, host64, relerr, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _expert_w(inp, e, shared=False):
+    if shared:
+        return host64(inp["ws1"]), host64(inp["ws2"])
+    return host64(inp["w1"][e]), host64(inp["w2"][e])
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_full_size(name):
+    c = CONFIGS[name]
+    print(f"\n[full size] {name}: T={c.T} d={c.d} f={c.f} E={c.E} k={c.k}", flush=True)
+    torch.manual_seed(0)
+    inp = make_inputs(c, seed=0, device="cuda")
+    buf = M.LayerBuffers.allocate(cfg_of(c), backward=not c.fwd_only)
+    M.forward(buf, inp)
+    if not c.fwd_only:
+        M.backward(buf, inp, inp["dy"])
+    torch.cuda.synchronize()
+    t = buf.t
+    spec = O.Spec.of(c)
+    rng = np.random.default_rng(0)
+
+    # ---- routing, every token
+    x64 = host64(inp["x"])
+    r = O.route(spec, x64, host64(inp["w_router"]), host64(inp.get("logit_offset")), host64(inp.get("sel_bias")))
+    np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), r["idx"])
+    assert relerr(host64(t["probs"]), r["probs"]) <= TOL_F32
+    assert relerr(host64(t["topk_w"]), r["w"]) <= TOL_F32
+    np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), r["counts"])
+    offs = r["offsets"]
+    np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(t["slot"].cpu().numpy(), r["slot"])
+    n = int(offs[-1])
+    np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), r["row_token"][:n])
+    if c.alpha:
+        assert abs(float(t["aux"][0]) - r["aux"]) <= TOL_F32 * abs(r["aux"])
+    rows_per = np.diff(offs)
+    print(f"  kept rows {n} / {c.T * c.k}; max/mean load {rows_per.max() / max(rows_per.mean(), 1e-9):.2f}; "
+          f"empty experts {int((rows_per == 0).sum())}", flush=True)
+
+    # ---- permutation: bitwise row copies
+    rt = t["row_token"][:n].long()
+    assert torch.equal(t["x_perm"][:n], inp["x"][rt])
+
+    # ---- sampled expert rows (forward and backward through the expert)
+    nonempty = np.nonzero(rows_per)[0]
+    by_size = nonempty[np.argsort(rows_per[nonempty], kind="stable")]
+    experts = sorted({int(by_size[-1]), int(by_size[len(by_size) // 2]), int(by_size[0])})
+    f1 = 2 * c.f if c.act == "swiglu" else c.f
+    dy64 = None if c.fwd_only else host64(inp["dy"])
+    w64 = r["w"]
+    print("  routing, positions and permutation match", flush=True)
+    for e in experts:
+        a, b = int(offs[e]), int(offs[e + 1])
+        pick = sorted({a, b - 1, int(rng.integers(a, b)), int(rng.integers(a, b))})
+        W1, W2 = _expert_w(inp, e)
+        X = x64[r["row_token"][pick]]
+        A, H, Y = O.ffn_fwd(spec.mode, X, W1, W2, spec.act)
+        assert relerr(host64(t["act_saved"][pick]), A) <= tol_for(c), e
+        assert relerr(host64(t["h_saved"][pick]), H) <= tol_for(c), e
+        assert relerr(host64(t["y_perm"][pick]), Y) <= tol_for(c), e
+    if c.shared:
+        tok = sorted({0, c.T - 1, int(rng.integers(0, c.T))})
+        W1, W2 = _expert_w(inp, 0, shared=True)
+        A, H, Y = O.ffn_fwd(spec.mode, x64[tok], W1, W2, spec.act)
+        assert relerr(host64(t["act_shared"][tok]), A) <= TOL_BF16
+        assert relerr(host64(t["y_shared"][tok]), Y) <= TOL_BF16
+
+    # ---- sampled tokens: output y (and dx in the backward)
+    dropped_tok = np.nonzero((r["slot"] < 0).any(1))[0]
+    tokens = sorted({0, c.T - 1, int(rng.integers(0, c.T))} |
+                    ({int(dropped_tok[0])} if len(dropped_tok) else set()))
+    wcache = {}
+
+    def W(e):  # one expert's weights in float64 at a time (bounded host memory)
+        if e not in wcache:
+            wcache.clear()
+            wcache[e] = _expert_w(inp, e)
+        return wcache[e]
+
+    W1s = W2s = None
+    if c.shared:
+        W1s, W2s = _expert_w(inp, 0, shared=True)
+    for tt in tokens:
+        # the token alone is an exact sub-problem: its kept rows, renumbered 0..m-1
+        kept = [rr for rr in range(c.k) if r["slot"][tt, rr] >= 0]
+        lslot = np.full((1, c.k), -1, np.int32)
+        ys, As_ = [], []
+        for j, rr in enumerate(kept):
+            lslot[0, rr] = j
+            A, H, Y = O.ffn_fwd(spec.mode, x64[tt:tt + 1], *W(int(r["idx"][tt, rr])), spec.act)
+            ys.append(Y[0])
+            As_.append(A)
+        yp = np.array(ys) if ys else np.zeros((0, c.d))
+        ysh = dxs = None
+        if c.shared:
+            Ash, Hsh, ysh = O.ffn_fwd(spec.mode, x64[tt:tt + 1], W1s, W2s, spec.act)
+        yref = O.combine(spec.mode, x64[tt:tt + 1], yp, lslot, w64[tt:tt + 1], ysh)
+        assert relerr(host64(t["y"][tt]), yref[0]) <= (TOL_BF16 if c.dtype == "bf16" else TOL_F32), tt
+        if not kept and not c.shared:
+            assert torch.equal(t["y"][tt].cpu(), inp["x"][tt].cpu())
+        if c.fwd_only:
+            continue
+        dO, dg = O.combine_bwd(spec.mode, dy64[tt:tt + 1], yp, lslot, w64[tt:tt + 1], len(kept))
+        dXp = np.zeros((len(kept), c.d))
+        ambiguous = False
+        for j, rr in enumerate(kept):
+            if spec.act == O.ACT_RELU and np.any(np.abs(As_[j]) <= 1e-4):
+                ambiguous = True
+            _, dX = O.ffn_bwd(spec.mode, dO[j:j + 1], As_[j], *W(int(r["idx"][tt, rr])), spec.act)
+            dXp[j] = dX[0]
+        dl = O.router_dlogits(r["probs"][tt:tt + 1], r["idx"][tt:tt + 1], w64[tt:tt + 1], dg, r["counts"],
+                              spec.gate, spec.renorm, spec.alpha, T_batch=c.T)
+        _, dxr = O.router_grads(O.MODE_EXACT, dl, x64[tt:tt + 1], host64(inp["w_router"]))
+        if c.shared:
+            if spec.act == O.ACT_RELU and np.any(np.abs(Ash) <= 1e-4):
+                ambiguous = True
+            _, dxs = O.ffn_bwd(spec.mode, dy64[tt:tt + 1], Ash, W1s, W2s, spec.act)
+        ref = O.unpermute_bwd(spec.mode, dy64[tt:tt + 1], dXp, lslot, dxr, dxs)
+        if not ambiguous:
+            assert relerr(host64(t["dx"][tt]), ref[0]) <= TOL_BF16, tt
+    if c.fwd_only:
+        return
+
+    # ---- sampled weight-gradient elements, summed over all rows of the expert
+    dw1, dw2 = t["dw1"], t["dw2"]
+    empty = np.nonzero(rows_per == 0)[0]
+    if len(empty):
+        ee = torch.from_numpy(empty).cuda()
+        assert float(dw1[ee].abs().max()) == 0.0 and float(dw2[ee].abs().max()) == 0.0
+    groups = [(int(by_size[-1]), False), (int(by_size[len(by_size) // 2]), False)]
+    if c.shared:
+        groups.append((0, True))
+    for e, sh in groups:
+        W1, W2 = _expert_w(inp, e, shared=sh)
+        if sh:
+            toks = np.arange(c.T)
+            dO = dy64  # weight 1
+        else:
+            a, b = int(offs[e]), int(offs[e + 1])
+            toks = r["row_token"][a:b]
+            # the expert's rows as a one-choice problem: dO[j] = round(w * dy[token])
+            wts = np.array([[w64[tk, int(np.nonzero(r["slot"][tk] == a + j)[0][0])]] for j, tk in enumerate(toks)])
+            one = np.arange(len(toks), dtype=np.int32)[:, None]
+            dO, _ = O.combine_bwd(spec.mode, dy64[toks], np.zeros((len(toks), c.d)), one, wts, len(toks))
+        X = x64[toks]
+        for _ in range(3):
+            i = int(rng.integers(0, c.d))
+            j = int(rng.integers(0, c.f))
+            # column j of H only needs hidden unit j: W1 rows j (and f+j), W2 column j
+            W1j = np.ascontiguousarray(W1[[j, c.f + j]] if spec.act == O.ACT_SWIGLU else W1[[j]])
+            W2j = np.ascontiguousarray(W2[:, [j]])
+            A1, H1, _ = O.ffn_fwd(spec.mode, X, W1j, W2j, spec.act)
+            ref = O.wgrad(spec.mode, np.ascontiguousarray(dO[:, [i]]), H1)[0, 0]
+            got = float((t["dws2"] if sh else dw2[e])[i, j])
+            assert abs(got - ref) <= TOL_BF16 * max(abs(ref), _col_scale(dO[:, i], H1[:, 0])), (e, i, j)
+            if spec.act == O.ACT_RELU and np.any(np.abs(A1) <= 1e-4):
+                continue
+            dA1, _ = O.ffn_bwd(spec.mode, np.ascontiguousarray(dO), A1, W1j, W2j, spec.act)
+            jj = int(rng.integers(0, c.d))
+            for col, row in ((0, j),) + (((1, c.f + j),) if spec.act == O.ACT_SWIGLU else ()):
+                ref1 = O.wgrad(spec.mode, np.ascontiguousarray(dA1[:, [col]]), np.ascontiguousarray(X[:, [jj]]))[0, 0]
+                got1 = float((t["dws1"] if sh else dw1[e])[row, jj])
+                assert abs(got1 - ref1) <= TOL_BF16 * max(abs(ref1), _col_scale(dA1[:, col], X[:, jj])), (e, row, jj)
+
+    # ---- router weight gradient: softmax rows of the Jacobian sum to zero
+    if spec.gate == O.GATE_SOFTMAX:
+        dwr = t["dw_router"].double()
+        colsum = dwr.sum(0).abs().max().item()
+        assert colsum <= 1e-3 * dwr.abs().max().item() * np.sqrt(c.E)
+
+
+def _col_scale(u, v):
+    # magnitude of a sum of len(u) terms u_i v_i with random signs
+    return float(np.sqrt(np.sum((np.asarray(u) * np.asarray(v)) ** 2))) + 1e-30
