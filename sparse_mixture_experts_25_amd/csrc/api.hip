@@ -8,13 +8,8 @@
 #include "../../include/moe.h"
 #include "../../include/moe_profile.h"
 
-namespace moe {
-int gemm_f32_row_tile();
-}
-
 namespace {
 
-constexpr int kBf16RowTile = 128;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -83,11 +78,6 @@ size_t workspace_of(const moe_config* c, int64_t R) {
   const size_t bw = bwd_layout(c, R).total;
   if (bw > ws) ws = bw;
   return ws;
-}
-
-int64_t row_tile_bound(const moe_config* c, int64_t R, int shared_rows) {
-  const int64_t bm = c->dtype == MOE_DT_BF16 ? kBf16RowTile : moe::gemm_f32_row_tile();
-  return (R + bm - 1) / bm + c->num_experts + (shared_rows + bm - 1) / bm;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -216,7 +206,7 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g1.N = f1; g1.K = d; g1.f = f;
   g1.has_shared = sh ? 1 : 0;
   g1.offsets = expert_offsets; g1.E = E; g1.shared_rows = shr;
-  g1.max_row_tiles = row_tile_bound(c, R, shr);
+  g1.max_rows = R;
   g1.A = x_perm; g1.lda = d;
   g1.B = w1; g1.ldb = d; g1.strideB = (int64_t)f1 * d;
   g1.A_sh = x; g1.B_sh = ws1;
@@ -231,7 +221,7 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g2.N = d; g2.K = f; g2.f = f;
   g2.has_shared = sh ? 1 : 0;
   g2.offsets = expert_offsets; g2.E = E; g2.shared_rows = shr;
-  g2.max_row_tiles = row_tile_bound(c, R, shr);
+  g2.max_rows = R;
   g2.A = h_saved; g2.lda = f;
   g2.B = w2; g2.ldb = f; g2.strideB = (int64_t)d * f;
   g2.A_sh = h_shared; g2.B_sh = ws2;
@@ -317,7 +307,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a2.N = f; a2.K = d; a2.f = f;
   a2.has_shared = sh ? 1 : 0;
   a2.offsets = sv->expert_offsets; a2.E = E; a2.shared_rows = shr;
-  a2.max_row_tiles = row_tile_bound(c, R, shr);
+  a2.max_rows = R;
   a2.A = dO; a2.lda = d;
   a2.B = w->w2; a2.ldb = f; a2.strideB = (int64_t)d * f;
   a2.A_sh = dy; a2.B_sh = w->ws2;
@@ -330,6 +320,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w2g.epi = moe::EPI_STORE;
   w2g.M = d; w2g.N = f;
   w2g.has_shared = sh ? 1 : 0;
+  w2g.max_rows = R;
   w2g.offsets = sv->expert_offsets; w2g.E = E; w2g.shared_rows = shr;
   w2g.A = dO; w2g.lda = d;
   w2g.B = sv->h_saved; w2g.ldb = f;
@@ -344,7 +335,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a1.N = d; a1.K = f1; a1.f = f;
   a1.has_shared = sh ? 1 : 0;
   a1.offsets = sv->expert_offsets; a1.E = E; a1.shared_rows = shr;
-  a1.max_row_tiles = row_tile_bound(c, R, shr);
+  a1.max_rows = R;
   a1.A = dA; a1.lda = f1;
   a1.B = w->w1; a1.ldb = d; a1.strideB = (int64_t)f1 * d;
   a1.A_sh = dA_sh; a1.B_sh = w->ws1;
@@ -356,6 +347,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w1g.epi = moe::EPI_STORE;
   w1g.M = f1; w1g.N = d;
   w1g.has_shared = sh ? 1 : 0;
+  w1g.max_rows = R;
   w1g.offsets = sv->expert_offsets; w1g.E = E; w1g.shared_rows = shr;
   w1g.A = dA; w1g.lda = f1;
   w1g.B = sv->x_perm; w1g.ldb = d;

@@ -125,14 +125,15 @@ struct MnLoader {
 };
 
 template <int BM, int BN, int KIND, int B_KC, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_KC = (KIND == 0);
   constexpr int B_IS_KC = (KIND == 0) && B_KC;
   constexpr int kOperandBytes = 2 * (BM + BN) * kBK * 2;
   constexpr int CP = BN + 8;  // padded row of the staged fp32 tile
-  constexpr int kStageBytes = BM * CP * 4;
+  constexpr int HM = BM / 2;  // the fp32 tile is staged half (one wave row) at a time
+  constexpr int kStageBytes = HM * CP * 4;
   constexpr int kLds = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   __shared__ int info[4];
@@ -256,91 +257,98 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: stage the fp32 tile, then 16-byte row writes
+  // ---- epilogue: stage the fp32 tile in LDS one half (the rows of one wave
+  // row) at a time, then write 16-byte row vectors
   float* Cs = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int n = wn * WN + j * 32 + (lane & 31);
-        Cs[m * CP + n] = acc[i][j][e];
-      }
-  __syncthreads();
-
   uint16_t* C = reinterpret_cast<uint16_t*>(sh ? a.C_sh : a.C);
   uint16_t* C2 = reinterpret_cast<uint16_t*>(sh ? a.C2_sh : a.C2);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(sh ? a.X_sh : a.X);
-
-  if (EPI == EPI_SWIGLU_FWD) {
-    // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns nb*BN/2 + j
-    constexpr int U = BM * (BN / 2) / 8;
-    for (int u = tid; u < U; u += kThreads) {
-      const int m = u / (BN / 16);
-      const int j = (u % (BN / 16)) * 8;
-      const int hc = nb * (BN / 2) + j;
-      if (m >= rows - mrow0 || hc >= a.f) continue;
-      const int64_t row = r0 + mrow0 + m;
-      float gv[8], uv[8], hv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        gv[e] = Cs[m * CP + j + e];
-        uv[e] = Cs[m * CP + BN / 2 + j + e];
-        hv[e] = silu_f(gv[e]) * uv[e];
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int n = wn * WN + j * 32 + (lane & 31);
+            Cs[m * CP + n] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    const int mbase = half * HM;  // tile row of Cs row 0
+    if (EPI == EPI_SWIGLU_FWD) {
+      // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns nb*BN/2 + j
+      constexpr int U = HM * (BN / 2) / 8;
+      for (int u = tid; u < U; u += kThreads) {
+        const int ml = u / (BN / 16);
+        const int j = (u % (BN / 16)) * 8;
+        const int m = mbase + ml;
+        const int hc = nb * (BN / 2) + j;
+        if (m >= rows - mrow0 || hc >= a.f) continue;
+        const int64_t row = r0 + mrow0 + m;
+        float gv[8], uv[8], hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          gv[e] = Cs[ml * CP + j + e];
+          uv[e] = Cs[ml * CP + BN / 2 + j + e];
+          hv[e] = silu_f(gv[e]) * uv[e];
+        }
+        st128(C + row * a.ldc + hc, Elem<uint16_t>::pack(gv));
+        st128(C + row * a.ldc + a.f + hc, Elem<uint16_t>::pack(uv));
+        st128(C2 + row * a.ldc2 + hc, Elem<uint16_t>::pack(hv));
       }
-      st128(C + row * a.ldc + hc, Elem<uint16_t>::pack(gv));
-      st128(C + row * a.ldc + a.f + hc, Elem<uint16_t>::pack(uv));
-      st128(C2 + row * a.ldc2 + hc, Elem<uint16_t>::pack(hv));
-    }
-    return;
-  }
-
-  constexpr int U = BM * BN / 8;
-  for (int u = tid; u < U; u += kThreads) {
-    const int m = u / (BN / 8);
-    const int n = (u % (BN / 8)) * 8;
-    float v[8];
+    } else {
+      constexpr int U = HM * BN / 8;
+      for (int u = tid; u < U; u += kThreads) {
+        const int ml = u / (BN / 8);
+        const int n = (u % (BN / 8)) * 8;
+        const int m = mbase + ml;
+        float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = Cs[m * CP + n + e];
-    if (KIND == 1) {
-      const int mm = mb * BM + m, nn = nb * BN + n;
-      if (mm >= a.M || nn >= a.N) continue;
-      uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
-      st128(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
-      continue;
-    }
-    const int col = nb * BN + n;
-    if (m >= rows - mrow0 || col >= a.N) continue;
-    const int64_t row = r0 + mrow0 + m;
-    if (EPI == EPI_STORE) {
-      st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
-    } else if (EPI == EPI_RELU_FWD) {
-      float h[8];
+        for (int e = 0; e < 8; ++e) v[e] = Cs[ml * CP + n + e];
+        if (KIND == 1) {
+          const int mm = mb * BM + m, nn = nb * BN + n;
+          if (mm >= a.M || nn >= a.N) continue;
+          uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
+          st128(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
+          continue;
+        }
+        const int col = nb * BN + n;
+        if (m >= rows - mrow0 || col >= a.N) continue;
+        const int64_t row = r0 + mrow0 + m;
+        if (EPI == EPI_STORE) {
+          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+        } else if (EPI == EPI_RELU_FWD) {
+          float h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = fmaxf(v[e], 0.0f);
-      st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
-      st128(C2 + row * a.ldc2 + col, Elem<uint16_t>::pack(h));
-    } else if (EPI == EPI_RELU_BWD) {
-      float xs[8];
-      Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), xs);
+          for (int e = 0; e < 8; ++e) h[e] = fmaxf(v[e], 0.0f);
+          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+          st128(C2 + row * a.ldc2 + col, Elem<uint16_t>::pack(h));
+        } else if (EPI == EPI_RELU_BWD) {
+          float xs[8];
+          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), xs);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = xs[e] > 0.0f ? v[e] : 0.0f;
-      st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
-    } else if (EPI == EPI_SWIGLU_BWD) {
-      float gs[8], us[8], dg[8], du[8];
-      Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), gs);
-      Elem<uint16_t>::unpack(ld128(X + row * a.ldx + a.f + col), us);
+          for (int e = 0; e < 8; ++e) v[e] = xs[e] > 0.0f ? v[e] : 0.0f;
+          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+        } else if (EPI == EPI_SWIGLU_BWD) {
+          float gs[8], us[8], dg[8], du[8];
+          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), gs);
+          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + a.f + col), us);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = 1.0f / (1.0f + __expf(-gs[e]));
-        du[e] = v[e] * gs[e] * s;
-        dg[e] = v[e] * us[e] * s * (1.0f + gs[e] * (1.0f - s));
+          for (int e = 0; e < 8; ++e) {
+            const float s = 1.0f / (1.0f + __expf(-gs[e]));
+            du[e] = v[e] * gs[e] * s;
+            dg[e] = v[e] * us[e] * s * (1.0f + gs[e] * (1.0f - s));
+          }
+          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(dg));
+          st128(C + row * a.ldc + a.f + col, Elem<uint16_t>::pack(du));
+        }
       }
-      st128(C + row * a.ldc + col, Elem<uint16_t>::pack(dg));
-      st128(C + row * a.ldc + a.f + col, Elem<uint16_t>::pack(du));
     }
+    if (half == 0) __syncthreads();
   }
 }
 
@@ -350,7 +358,8 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   if (KIND == 0) {
     const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
     const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
-    grid = dim3((unsigned)a.max_row_tiles, (ncols + bn - 1) / bn, 1);
+    const int64_t tiles = (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
+    grid = dim3((unsigned)tiles, (ncols + bn - 1) / bn, 1);
   } else {
     const int ng = a.E + (a.has_shared ? 1 : 0);
     grid = dim3(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), ng, 1);
@@ -360,10 +369,9 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
+template <int BM, int BN>
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   if (a.kind == 1) return launch_t<BM, BN, 1, 0, EPI_STORE>(a, st);
   if (a.b_kcontig) {
     switch (a.epi) {
@@ -379,6 +387,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     case EPI_SWIGLU_BWD: return launch_t<BM, BN, 0, 0, EPI_SWIGLU_BWD>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+// Tile choice: 256x256 (each wave 128x128, one workgroup per CU) when the
+// groups are large enough to fill it on average; 128x128 otherwise (small
+// expert batches, where the weights stream from HBM and the row tile is mostly
+// padding).
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+  const int64_t groups = a.E > 0 ? a.E : 1;
+  const int64_t avg_rows = (a.kind == 0 ? a.max_rows : a.max_rows) / groups;
+  const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
+  return big ? launch_tiles<256, 256>(a, st) : launch_tiles<128, 128>(a, st);
 }
 
 }  // namespace moe

@@ -162,7 +162,8 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   if (KIND == 0) {
     const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
     const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
-    grid = dim3((unsigned)a.max_row_tiles, (ncols + bn - 1) / bn, 1);
+    const int64_t tiles = (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
+    grid = dim3((unsigned)tiles, (ncols + bn - 1) / bn, 1);
   } else {
     const int ng = a.E + (a.has_shared ? 1 : 0);
     grid = dim3(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), ng, 1);
@@ -174,7 +175,6 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int gemm_f32_row_tile() { return BM; }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
   if (a.kind == 1) return launch_t<1, 0, EPI_STORE>(a, st);

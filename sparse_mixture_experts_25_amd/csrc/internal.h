@@ -57,7 +57,7 @@ struct GemmArgs {
   int E;
   int shared_rows;
   int has_shared;         // 1: an extra dense group exists (it may have 0 rows)
-  int64_t max_row_tiles;  // ragged-M: upper bound on the number of row tiles
+  int64_t max_rows;       // upper bound on the routed rows (sum over groups)
   const void* A; int64_t lda;
   const void* B; int64_t ldb; int64_t strideB;
   const void* A_sh; const void* B_sh;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, 
   }
 }
 
-constexpr int kAuxTok = 256;
+constexpr int kAuxTok = 32;  // tokens per partial-sum block
 
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ probs, int T, int E,
                                                           float* __restrict__ partial) {
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   const int t1 = min(T, t0 + kAuxTok);
   for (int e = threadIdx.x; e < E; e += 256) {
     float s = 0.0f;
+#pragma unroll 8
     for (int t = t0; t < t1; ++t) s += probs[(int64_t)t * E + e];
     partial[(int64_t)blockIdx.x * E + e] = s;
   }
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict_
   float acc = 0.0f;
   for (int e = threadIdx.x; e < E; e += 256) {
     float P = 0.0f;
+#pragma unroll 8
     for (int b = 0; b < nblk; ++b) P += partial[(int64_t)b * E + e];
     P /= (float)T;
     const float f = (float)counts[e] / ((float)T * (float)k);
