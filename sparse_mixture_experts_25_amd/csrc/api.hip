@@ -49,13 +49,13 @@ int64_t max_rows_of(const moe_config* c, int C) {
 
 // Backward workspace layout.
 struct BwdWs {
-  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, total;
+  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, total;
 };
 BwdWs bwd_layout(const moe_config* c, int64_t R) {
   const int64_t T = c->num_tokens, d = c->d_model, E = c->num_experts, k = c->top_k;
   const int64_t f1 = c->act == MOE_ACT_SWIGLU ? 2 * (int64_t)c->d_ff : c->d_ff;
   const int64_t eb = elem_bytes(c);
-  const int64_t ns = moe::router_grad_splits((int)T);
+  const int64_t ns = moe::router_grad_splits((int)T, (int)E, (int)d);
   BwdWs w;
   size_t o = 0;
   w.dO = o; o += align_up(R * d * eb);
@@ -67,6 +67,7 @@ BwdWs bwd_layout(const moe_config* c, int64_t R) {
   w.part = o; o += align_up(ns * E * d * 4);
   w.dA_sh = o; o += c->num_shared_experts ? align_up(T * f1 * eb) : 0;
   w.dX_sh = o; o += c->num_shared_experts ? align_up(T * d * eb) : 0;
+  w.order = o; o += align_up((E + 1) * 4);
   w.total = o;
   return w;
 }
@@ -293,6 +294,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   float* part = (float*)(base + L.part);
   void* dA_sh = sh ? base + L.dA_sh : nullptr;
   void* dX_sh = sh ? base + L.dX_sh : nullptr;
+  int32_t* order = (int32_t*)(base + L.order);
 
   if (T > 0) {
     moe::CombineBwdArgs cb{dy, sv->y_perm, sv->slot, sv->topk_w, dO, dg, T, d, k, c->dtype};
@@ -314,6 +316,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a2.C = dA; a2.ldc = f1; a2.C_sh = dA_sh;
   a2.X = sv->act_saved; a2.ldx = f1; a2.X_sh = sv->act_shared;
   if ((st = gemm(c, a2, s, "bwd_dgrad2"))) return st;
+  // weight gradients run the experts with the most rows first
+  if ((st = launch_status(moe::launch_group_order(sv->expert_offsets, E, shr, sh ? 1 : 0, order, s)))) return st;
   // dW2_e = dO^T h over the expert's rows
   moe::GemmArgs w2g{};
   w2g.kind = 1;
@@ -321,6 +325,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w2g.M = d; w2g.N = f;
   w2g.has_shared = sh ? 1 : 0;
   w2g.max_rows = R;
+  w2g.order = order;
   w2g.offsets = sv->expert_offsets; w2g.E = E; w2g.shared_rows = shr;
   w2g.A = dO; w2g.lda = d;
   w2g.B = sv->h_saved; w2g.ldb = f;
@@ -348,6 +353,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w1g.M = f1; w1g.N = d;
   w1g.has_shared = sh ? 1 : 0;
   w1g.max_rows = R;
+  w1g.order = order;
   w1g.offsets = sv->expert_offsets; w1g.E = E; w1g.shared_rows = shr;
   w1g.A = dA; w1g.lda = f1;
   w1g.B = sv->x_perm; w1g.ldb = d;

@@ -7,19 +7,30 @@
 //
 // One kernel template covers the six matmuls of the layer:
 //   ragged-M (forward, and the input gradients): the row count of each group
-//     comes from the device offsets; a linear row-tile index is decoded into
-//     (group, row) in-kernel, so no host round trip is needed and empty
-//     workgroups exit at once.
+//     comes from the device offsets; the workgroup id is decoded in-kernel into
+//     (group, row tile, column tile), so no host round trip is needed.
 //   ragged-K (weight gradients): a fixed [M, N] output per group, contracted
-//     over that group's rows; a group without rows writes zeros.
-// Operands are staged in LDS as [rows][BK] with the K axis contiguous and the
-// 16-byte chunks of each row XOR-swizzled by (row & 7) so that the fragment
-// reads are bank-conflict free. An operand whose K axis is the slow one in
-// memory ([K][MN], as in the gradient matmuls) is loaded as 4(k) x 8(mn)
-// blocks and transposed in registers before the LDS store. Each of the four
-// waves owns a (BM/2) x (BN/2) sub-tile computed with v_mfma_f32_32x32x16_bf16
-// (fp32 accumulation). The epilogue stages the fp32 tile in LDS and writes
-// 16-byte rows, fusing the activation (forward) or its derivative (backward).
+//     over that group's rows; a group without rows writes zeros. Groups run
+//     largest first.
+//
+// Main loop: an NS-stage pipeline over 64-deep K steps. Every full step is
+// brought into LDS with direct global->LDS 16-byte loads (each wave fills
+// 1 KB blocks; lane i of a load lands at +16*i, so the XOR swizzle of the LDS
+// layout is applied by choosing which global chunk each lane fetches). Up to
+// NS-1 steps are in flight while the matrix cores work on the current one; a
+// per-wave vmcnt wait plus one barrier per step publishes a stage. A ragged
+// K tail (last partial step) goes through registers with zero fill.
+//   K-contiguous operand ([rows][K] in memory): LDS rows of 64 k, 16-byte
+//     chunk c of row r at c ^ (r & 7); fragments read with ds_read_b128.
+//   MN-contiguous operand ([K][rows] in memory, the gradient matmuls): LDS
+//     k-rows as in memory, chunk c of k-row k at (c & ~7) | ((c ^ k) & 7);
+//     fragments read with the gfx950 LDS transpose read (ds_read_b64_tr_b16),
+//     which turns a 4(k) x 16(mn) block into per-lane k-vectors.
+// Four waves, each owning a (BM/2) x (BN/2) sub-tile computed with
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Rows or columns past the end
+// of a group read clamped (finite) data and are never stored. The epilogue
+// stages the fp32 tile in LDS (half at a time) and writes 16-byte rows, fusing
+// the activation (forward) or its derivative (backward).
 #include "gemm_common.h"
 
 namespace moe {
@@ -29,117 +40,142 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------ LDS layouts
+// offsets in elements
+__device__ __forceinline__ int kc_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 3); }
 template <int R>
-struct TileLoad {
-  // registers staged between the global load and the LDS store
-  static constexpr int kUnitsKC = R * kBK / 8 / kThreads;   // 16-byte units per thread (K-contig)
-  static constexpr int kUnitsMN = (R / 8) * (kBK / 4) / kThreads;  // 4x8 blocks per thread (MN-contig)
-};
+__device__ __forceinline__ int mn_off(int k, int c) {
+  return k * R + (((c & ~7) | ((c ^ k) & 7)) << 3);
+}
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// ------------------------------------------------------------ direct loads
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-// K-contiguous operand: element (r, k) at base[r * ld + k]; rows >= rows_valid
-// or k >= K read as zero. `rowmap` (SwiGLU weights) sends tile row r to a
-// different source row.
-template <int R, int MAP>
-struct KcLoader {
-  u128 reg[TileLoad<R>::kUnitsKC];
-  __device__ void load(const uint16_t* base, int64_t ld, int rows_valid, int K, int k0, int map_half,
-                       int map_f, int map_h0) {
+// One 16-byte global->LDS load per lane; the 64 lanes of the wave fill the
+// 1 KB block at LDS byte address `lds_block` (wave-uniform), lane i at +16*i.
+// M0 holds the LDS address for the instruction and is restored afterwards.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_block) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_block))
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `steps` later pipeline steps (L loads each) are in flight
+template <int L>
+__device__ __forceinline__ void wait_steps(int steps) {
+  if (steps <= 0) wait_vm<0>();
+  else if (steps == 1) wait_vm<L>();
+  else wait_vm<2 * L>();
+}
+
+// K-contiguous tile, R rows x 64 k. rowptr(r) = global address of (row r, k0).
+template <int R, typename RowPtr>
+__device__ __forceinline__ void dma_kc(uint32_t lds_tile, int wave, int lane, RowPtr rowptr) {
 #pragma unroll
-    for (int i = 0; i < TileLoad<R>::kUnitsKC; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int r = u / (kBK / 8);
-      const int c = u % (kBK / 8);
-      const int k = k0 + c * 8;
-      int64_t src;
-      bool ok;
-      if (MAP) {
-        // tile rows [0, half) -> gate rows h0 + r; [half, R) -> up rows f + h0 + r - half
-        const int hc = map_h0 + (r < map_half ? r : r - map_half);
-        ok = hc < map_f && k < K;
-        src = (int64_t)(r < map_half ? hc : map_f + hc) * ld + k;
-      } else {
-        ok = r < rows_valid && k < K;
-        src = (int64_t)r * ld + k;
-      }
-      reg[i] = ok ? ld128(base + src) : zero128();
-    }
+  for (int q = 0; q < R / 32; ++q) {
+    const int blk = wave * (R / 32) + q;
+    const int p = blk * 64 + lane;
+    const int r = p >> 3, pc = p & 7;
+    const int c = pc ^ (r & 7);
+    dma16(rowptr(r) + 8 * c, lds_tile + blk * 1024);
   }
-  __device__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < TileLoad<R>::kUnitsKC; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int r = u / (kBK / 8);
-      const int c = u % (kBK / 8);
-      st128(lds + swz(r, c), reg[i]);
-    }
-  }
-};
+}
 
-// MN-contiguous operand: element (r, k) at base[k * ld + r]; k >= k_valid or
-// r >= rows_valid read as zero. Loaded as 4 (k) x 8 (r) blocks.
+// MN-contiguous tile, 64 k-rows x R. kptr(kr) = global address of (k0 + kr, mn0);
+// column chunks at or past `cvalid` read the last valid chunk.
+template <int R, typename KPtr>
+__device__ __forceinline__ void dma_mn(uint32_t lds_tile, int wave, int lane, KPtr kptr, int cvalid) {
+  constexpr int CPR = R / 8;
+#pragma unroll
+  for (int q = 0; q < R / 32; ++q) {
+    const int blk = wave * (R / 32) + q;
+    const int p = blk * 64 + lane;
+    const int kr = p / CPR, pc = p % CPR;
+    const int c = (pc & ~7) | ((pc ^ kr) & 7);
+    const int cc = c < cvalid ? c : cvalid - 1;
+    dma16(kptr(kr) + 8 * cc, lds_tile + blk * 1024);
+  }
+}
+
+// Zero-filled register path for a partial K step (k >= kvalid reads as zero).
+template <int R, typename RowPtr>
+__device__ __forceinline__ void tail_kc(uint16_t* tile, RowPtr rowptr, int rvalid, int kvalid) {
+  for (int u = threadIdx.x; u < R * 8; u += kThreads) {
+    const int r = u >> 3, c = u & 7;
+    const u128 v = (r < rvalid && 8 * c < kvalid) ? ld128(rowptr(r) + 8 * c) : zero128();
+    st128(tile + kc_off(r, c), v);
+  }
+}
+template <int R, typename KPtr>
+__device__ __forceinline__ void tail_mn(uint16_t* tile, KPtr kptr, int cvalid, int kvalid) {
+  for (int u = threadIdx.x; u < 64 * (R / 8); u += kThreads) {
+    const int kr = u / (R / 8), c = u % (R / 8);
+    const u128 v = (kr < kvalid && c < cvalid) ? ld128(kptr(kr) + 8 * c) : zero128();
+    st128(tile + mn_off<R>(kr, c), v);
+  }
+}
+
+// ------------------------------------------------------------ fragments
+// A/B fragment of v_mfma_f32_32x32x16_bf16: lane l holds 8 consecutive k
+// (8*(l/32) .. +7 of the 16-k step s) of row/column (base + l % 32).
+__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* tile, int base, int s, int lane) {
+  return *reinterpret_cast<const bf16x8*>(tile + kc_off(base + (lane & 31), 2 * s + (lane >> 5)));
+}
+
+__device__ __forceinline__ shortx4 read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
+}
+
+// From a [64 k][R] tile: per 16-lane group, the transpose read gives lane i
+// the 4 k-values of column c0 + i when source lane j reads 4 columns
+// c0 + 4*(j & 3) .. +3 of k-row k0 + (j >> 2). Two reads cover 8 k.
 template <int R>
-struct MnLoader {
-  static constexpr int kU = TileLoad<R>::kUnitsMN;
-  u128 reg[kU][4];
-  __device__ void load(const uint16_t* base, int64_t ld, int rows_valid, int k_valid, int k0) {
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int ru = u % (R / 8);
-      const int ku = u / (R / 8);
-      const int r = ru * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = k0 + ku * 4 + j;
-        const bool ok = r < rows_valid && k < k_valid;
-        reg[i][j] = ok ? ld128(base + (int64_t)k * ld + r) : zero128();
-      }
-    }
-  }
-  __device__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int ru = u % (R / 8);
-      const int ku = u / (R / 8);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int j = m >> 1;
-        uint32_t d0, d1;
-        if ((m & 1) == 0) {
-          d0 = (reg[i][0].w[j] & 0xFFFFu) | (reg[i][1].w[j] << 16);
-          d1 = (reg[i][2].w[j] & 0xFFFFu) | (reg[i][3].w[j] << 16);
-        } else {
-          d0 = (reg[i][0].w[j] >> 16) | (reg[i][1].w[j] & 0xFFFF0000u);
-          d1 = (reg[i][2].w[j] >> 16) | (reg[i][3].w[j] & 0xFFFF0000u);
-        }
-        const int row = ru * 8 + m;
-        const int kk = ku * 4;  // k offset inside the tile: chunk kk/8, half (kk/4)&1
-        uint16_t* dst = lds + swz(row, kk >> 3) + (kk & 4);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(d0, d1);
-      }
-    }
-  }
-};
+__device__ __forceinline__ bf16x8 frag_mn(const uint16_t* tile, int base, int s, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int col = base + 16 * (g & 1) + 4 * (j & 3);
+  const int k = 16 * s + 8 * (g >> 1) + (j >> 2);
+  const shortx4 lo = read_tr(tile + mn_off<R>(k, col >> 3) + (col & 7));
+  const shortx4 hi = read_tr(tile + mn_off<R>(k + 4, col >> 3) + (col & 7));
+  const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
-template <int BM, int BN, int KIND, int B_KC, int EPI>
-__global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(GemmArgs a) {
+// ------------------------------------------------------------ kernel
+template <int BM, int BN, int NS, int KIND, int B_KC, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_KC = (KIND == 0);
   constexpr int B_IS_KC = (KIND == 0) && B_KC;
-  constexpr int kOperandBytes = 2 * (BM + BN) * kBK * 2;
+  constexpr int kStage = (BM + BN) * kBK;  // elements
+  constexpr int kOperandBytes = NS * kStage * 2;
   constexpr int CP = BN + 8;  // padded row of the staged fp32 tile
   constexpr int HM = BM / 2;  // the fp32 tile is staged half (one wave row) at a time
   constexpr int kStageBytes = HM * CP * 4;
   constexpr int kLds = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
-  __shared__ int info[4];
+  constexpr int L = BM / 32 + BN / 32;  // direct loads per wave per K step
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+  __shared__ __attribute__((aligned(16))) int info[12];
 
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Bs = As + 2 * BM * kBK;
+  uint16_t* stages = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t lds0 = lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -149,15 +185,21 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
   int g, rows, mrow0 = 0, nb, mb = 0;
   int64_t r0;
   if (KIND == 0) {
-    TileInfo ti = decode_row_tile<BM>(a, blockIdx.x, info);
-    if (ti.g < 0) return;
+    const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
+    const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
+    TileInfo ti;
+    if (!locate_ragged_m<BM>(a, (ncols + bn - 1) / bn, 8, info, ti, nb)) return;
     g = ti.g; r0 = ti.r0; rows = ti.rows; mrow0 = ti.m0;
-    nb = blockIdx.y;
   } else {
-    g = blockIdx.y;
-    const int nN = (a.N + BN - 1) / BN;
-    mb = blockIdx.x / nN;
-    nb = blockIdx.x % nN;
+    // groups in the given order (largest first), tiles of one group
+    // consecutive with the row block fastest
+    const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
+    const int64_t per_g = (int64_t)nM * nN;
+    const int rank = (int)(blockIdx.x / per_g);
+    const int t = (int)(blockIdx.x % per_g);
+    g = a.order ? a.order[rank] : rank;
+    mb = t % nM;
+    nb = t / nM;
     if (g < a.E) {
       r0 = a.offsets[g];
       rows = a.offsets[g + 1] - a.offsets[g];
@@ -169,31 +211,65 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
   const bool sh = g >= a.E;
   const uint16_t* Ab = reinterpret_cast<const uint16_t*>(sh ? a.A_sh : a.A);
   const uint16_t* Bb = reinterpret_cast<const uint16_t*>(sh ? a.B_sh : a.B);
-  if (!sh) Bb += (KIND == 0) ? (int64_t)g * a.strideB : 0;
+  if (!sh && KIND == 0) Bb += (int64_t)g * a.strideB;
 
-  // K extent and operand origins
-  int K;
+  // K extent, operand origins and valid extents
+  const int K = (KIND == 0) ? a.K : rows;
   const uint16_t* Aorig;
   const uint16_t* Borig;
-  int a_rows_valid, b_rows_valid;
+  int a_valid, b_valid;  // KC: valid rows of the tile; MN: valid 8-column chunks
   if (KIND == 0) {
-    K = a.K;
     Aorig = Ab + (r0 + mrow0) * a.lda;
-    a_rows_valid = rows - mrow0;
+    a_valid = min(rows - mrow0, BM);
     if (B_KC) {
-      Borig = Bb + (EPI == EPI_SWIGLU_FWD ? 0 : (int64_t)nb * BN * a.ldb);
-      b_rows_valid = a.N - nb * BN;
+      Borig = Bb;
+      b_valid = (EPI == EPI_SWIGLU_FWD) ? 0 : min(a.N - nb * BN, BN);
     } else {
       Borig = Bb + (int64_t)nb * BN;  // [K][N]
-      b_rows_valid = a.N - nb * BN;
+      b_valid = min(a.N - nb * BN, BN) / 8;
     }
   } else {
-    K = rows;
     Aorig = Ab + r0 * a.lda + (int64_t)mb * BM;  // [rows][M]
     Borig = Bb + r0 * a.ldb + (int64_t)nb * BN;  // [rows][N]
-    a_rows_valid = a.M - mb * BM;
-    b_rows_valid = a.N - nb * BN;
+    a_valid = min(a.M - mb * BM, BM) / 8;
+    b_valid = min(a.N - nb * BN, BN) / 8;
   }
+  const int h0 = nb * (BN / 2);  // SwiGLU: first h column of this tile
+
+  // global address of (tile row r, k0) for the K-contiguous operands
+  auto a_row = [&](int r, int k0) {
+    return Aorig + (int64_t)(r < a_valid ? r : a_valid - 1) * a.lda + k0;
+  };
+  auto b_row = [&](int r, int k0) {
+    int64_t src;
+    if (EPI == EPI_SWIGLU_FWD) {
+      // tile rows [0, BN/2) -> gate rows h0 + r; [BN/2, BN) -> up rows f + h0 + r - BN/2
+      const int hc0 = h0 + (r < BN / 2 ? r : r - BN / 2);
+      const int hc = hc0 < a.f ? hc0 : a.f - 1;
+      src = r < BN / 2 ? hc : a.f + hc;
+    } else {
+      src = nb * BN + (r < b_valid ? r : b_valid - 1);
+    }
+    return Borig + src * a.ldb + k0;
+  };
+
+  auto dma_step = [&](int stage, int k0) {
+    const uint32_t sa = lds0 + stage * kStage * 2;
+    const uint32_t sb = sa + BM * kBK * 2;
+    if (A_KC) dma_kc<BM>(sa, wave, lane, [&](int r) { return a_row(r, k0); });
+    else dma_mn<BM>(sa, wave, lane, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid);
+    if (B_IS_KC) dma_kc<BN>(sb, wave, lane, [&](int r) { return b_row(r, k0); });
+    else dma_mn<BN>(sb, wave, lane, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid);
+  };
+  auto tail_step = [&](int stage, int k0) {
+    uint16_t* ta = stages + stage * kStage;
+    uint16_t* tb = ta + BM * kBK;
+    const int kv = K - k0;
+    if (A_KC) tail_kc<BM>(ta, [&](int r) { return a_row(r, k0); }, BM, kv);
+    else tail_mn<BM>(ta, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid, kv);
+    if (B_IS_KC) tail_kc<BN>(tb, [&](int r) { return b_row(r, k0); }, BN, kv);
+    else tail_mn<BN>(tb, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid, kv);
+  };
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -203,59 +279,40 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  KcLoader<BM, 0> la_kc;
-  MnLoader<BM> la_mn;
-  KcLoader<BN, (EPI == EPI_SWIGLU_FWD)> lb_kc;
-  MnLoader<BN> lb_mn;
-  const int map_half = BN / 2, map_h0 = nb * (BN / 2);
-
-  auto load_tiles = [&](int k0) {
-    if (A_KC) la_kc.load(Aorig, a.lda, a_rows_valid, K, k0, 0, 0, 0);
-    else la_mn.load(Aorig, a.lda, a_rows_valid, K, k0);
-    if (B_IS_KC) lb_kc.load(Borig, a.ldb, b_rows_valid, K, k0, map_half, a.f, map_h0);
-    else lb_mn.load(Borig, a.ldb, b_rows_valid, K, k0);
-  };
-  auto store_tiles = [&](int buf) {
-    if (A_KC) la_kc.store(As + buf * BM * kBK);
-    else la_mn.store(As + buf * BM * kBK);
-    if (B_IS_KC) lb_kc.store(Bs + buf * BN * kBK);
-    else lb_mn.store(Bs + buf * BN * kBK);
-  };
-
-  const int nk = (K + kBK - 1) / kBK;
-  if (nk > 0) {
-    load_tiles(0);
-    store_tiles(0);
-  }
-  __syncthreads();
+  const int nfull = K / kBK;
+  const int nk = nfull + ((K % kBK) ? 1 : 0);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nfull) dma_step(s, s * kBK);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
-    const uint16_t* Ab_l = As + buf * BM * kBK;
-    const uint16_t* Bb_l = Bs + buf * BN * kBK;
+    const int stage = kt % NS;
+    if (kt < nfull) {
+      const int later = min(NS - 2, nfull - 1 - kt);  // steps issued after kt, maybe in flight
+      wait_steps<L>(later);
+    } else {
+      tail_step(stage, kt * kBK);
+    }
+    __syncthreads();
+    if (kt + NS - 1 < nfull) dma_step((kt + NS - 1) % NS, (kt + NS - 1) * kBK);
+    const uint16_t* ta = stages + stage * kStage;
+    const uint16_t* tb = ta + BM * kBK;
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(Ab_l + swz(row, chunk));
-      }
+      for (int i = 0; i < FM; ++i)
+        af[i] = A_KC ? frag_kc(ta, wm * WM + i * 32, s, lane) : frag_mn<BM>(ta, wm * WM + i * 32, s, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bb_l + swz(row, chunk));
-      }
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = B_IS_KC ? frag_kc(tb, wn * WN + j * 32, s, lane) : frag_mn<BN>(tb, wn * WN + j * 32, s, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tiles(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---- epilogue: stage the fp32 tile in LDS one half (the rows of one wave
   // row) at a time, then write 16-byte row vectors
@@ -280,13 +337,13 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
     __syncthreads();
     const int mbase = half * HM;  // tile row of Cs row 0
     if (EPI == EPI_SWIGLU_FWD) {
-      // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns nb*BN/2 + j
+      // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns h0 + j
       constexpr int U = HM * (BN / 2) / 8;
       for (int u = tid; u < U; u += kThreads) {
         const int ml = u / (BN / 16);
         const int j = (u % (BN / 16)) * 8;
         const int m = mbase + ml;
-        const int hc = nb * (BN / 2) + j;
+        const int hc = h0 + j;
         if (m >= rows - mrow0 || hc >= a.f) continue;
         const int64_t row = r0 + mrow0 + m;
         float gv[8], uv[8], hv[8];
@@ -352,54 +409,79 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
   }
 }
 
-template <int BM, int BN, int KIND, int B_KC, int EPI>
+template <int BM, int BN, int NS, int KIND, int B_KC, int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  dim3 grid;
+  int64_t n;
   if (KIND == 0) {
     const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
     const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
-    const int64_t tiles = (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
-    grid = dim3((unsigned)tiles, (ncols + bn - 1) / bn, 1);
+    n = raster_grid(row_tile_bound(a, BM), (ncols + bn - 1) / bn);
   } else {
     const int ng = a.E + (a.has_shared ? 1 : 0);
-    grid = dim3(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), ng, 1);
+    n = (int64_t)ng * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   }
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, KIND, B_KC, EPI>), grid, dim3(kThreads), 0, st, a);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NS, KIND, B_KC, EPI>), dim3((unsigned)n), dim3(kThreads), 0, st,
+                     a);
   return hipGetLastError();
 }
 
-
-template <int BM, int BN>
+template <int BM, int BN, int NS>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
-  if (a.kind == 1) return launch_t<BM, BN, 1, 0, EPI_STORE>(a, st);
+  if (a.kind == 1) return launch_t<BM, BN, NS, 1, 0, EPI_STORE>(a, st);
   if (a.b_kcontig) {
     switch (a.epi) {
-      case EPI_STORE: return launch_t<BM, BN, 0, 1, EPI_STORE>(a, st);
-      case EPI_RELU_FWD: return launch_t<BM, BN, 0, 1, EPI_RELU_FWD>(a, st);
-      case EPI_SWIGLU_FWD: return launch_t<BM, BN, 0, 1, EPI_SWIGLU_FWD>(a, st);
+      case EPI_STORE: return launch_t<BM, BN, NS, 0, 1, EPI_STORE>(a, st);
+      case EPI_RELU_FWD: return launch_t<BM, BN, NS, 0, 1, EPI_RELU_FWD>(a, st);
+      case EPI_SWIGLU_FWD: return launch_t<BM, BN, NS, 0, 1, EPI_SWIGLU_FWD>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
   switch (a.epi) {
-    case EPI_STORE: return launch_t<BM, BN, 0, 0, EPI_STORE>(a, st);
-    case EPI_RELU_BWD: return launch_t<BM, BN, 0, 0, EPI_RELU_BWD>(a, st);
-    case EPI_SWIGLU_BWD: return launch_t<BM, BN, 0, 0, EPI_SWIGLU_BWD>(a, st);
+    case EPI_STORE: return launch_t<BM, BN, NS, 0, 0, EPI_STORE>(a, st);
+    case EPI_RELU_BWD: return launch_t<BM, BN, NS, 0, 0, EPI_RELU_BWD>(a, st);
+    case EPI_SWIGLU_BWD: return launch_t<BM, BN, NS, 0, 0, EPI_SWIGLU_BWD>(a, st);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Rank of each group by row count (largest first, ties by lower index): the
+// weight-gradient launches then start the longest contractions first.
+__global__ __launch_bounds__(512) void group_order_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int shared_rows, int has_shared,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int rows_s[1024];
+  const int G = E + has_shared;
+  for (int g = threadIdx.x; g < G; g += 512) rows_s[g] = g < E ? offsets[g + 1] - offsets[g] : shared_rows;
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += 512) {
+    const int r = rows_s[g];
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const int rh = rows_s[h];
+      rank += (rh > r) || (rh == r && h < g);
+    }
+    order[rank] = g;
   }
 }
 
 }  // namespace
 
-// Tile choice: 256x256 (each wave 128x128, one workgroup per CU) when the
-// groups are large enough to fill it on average; 128x128 otherwise (small
-// expert batches, where the weights stream from HBM and the row tile is mostly
-// padding).
+hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, int has_shared, int32_t* order,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(group_order_kernel, dim3(1), dim3(512), 0, st, offsets, E, shared_rows, has_shared, order);
+  return hipGetLastError();
+}
+
+// Tile choice: 256x256 (each wave 128x128, two stages in flight) when the
+// groups are large enough to fill it on average; 128x128 with four stages
+// otherwise (small expert batches, where the weights stream from HBM and the
+// row tile is mostly padding).
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
-  const int64_t avg_rows = (a.kind == 0 ? a.max_rows : a.max_rows) / groups;
+  const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
-  return big ? launch_tiles<256, 256>(a, st) : launch_tiles<128, 128>(a, st);
+  return big ? launch_tiles<256, 256, 2>(a, st) : launch_tiles<128, 128, 4>(a, st);
 }
 
 }  // namespace moe

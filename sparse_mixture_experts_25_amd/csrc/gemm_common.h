@@ -15,19 +15,75 @@ struct TileInfo {
   int m0;       // first tile row inside the group (ragged-M)
 };
 
-// Ragged-M: map a linear row-tile index to (group, first row) by an exclusive
-// scan of ceil(rows_g / BM) over the groups. Wave 0 does the scan; the result
-// goes through LDS to the whole workgroup.
+// Upper bound on the number of row tiles of a ragged-M launch: sum over the
+// groups of ceil(rows_g / BM) <= ceil(R / BM) + E (+ the shared group's tiles).
+__host__ __device__ inline int64_t row_tile_bound(const GemmArgs& a, int BM) {
+  return (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
+}
+
+// XCD-aware grouped rasterization. The dispatcher hands workgroup ids to the
+// 8 XCDs round-robin (id % 8), and each XCD has its own L2. Workgroup ids are
+// remapped so that each XCD owns one contiguous range of logical tiles, and the
+// logical order walks groups of GM row tiles across all column tiles, so that
+// concurrently running workgroups on one XCD share operand tiles in its L2.
+// The grid is 1-D with nrow * ncol rounded up to a multiple of 8.
+constexpr int kXcds = 8;
+__host__ __device__ inline int64_t raster_grid(int64_t nrow, int64_t ncol) {
+  return (nrow * ncol + kXcds - 1) / kXcds * kXcds;
+}
+__device__ inline bool raster_tile(int64_t nrow, int64_t ncol, int GM, int64_t& row, int64_t& col) {
+  const int64_t total = nrow * ncol;
+  const int64_t per = raster_grid(nrow, ncol) / kXcds;
+  const int64_t bid = blockIdx.x;
+  const int64_t L = (bid % kXcds) * per + bid / kXcds;
+  if (L >= total) return false;
+  const int64_t gsize = (int64_t)GM * ncol;
+  const int64_t first = (L / gsize) * GM;
+  const int64_t gm = (nrow - first) < GM ? (nrow - first) : GM;
+  const int64_t local = L % gsize;
+  row = first + local % gm;
+  col = local / gm;
+  return true;
+}
+
+// Ragged-M tile placement. Wave 0 scans ceil(rows_g / BM) over the groups
+// (each lane owns a run of groups) to get the actual number of row tiles; the
+// workgroup id is then mapped XCD-aware over (actual row tiles) x ncol (see
+// raster_tile), and the owning lane resolves the row tile to (group, first row).
+// Everything goes through LDS to the whole workgroup. Returns false when this
+// workgroup has no tile.
 template <int BM>
-__device__ TileInfo decode_row_tile(const GemmArgs& a, int64_t tile, int* lds4) {
+__device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* lds, TileInfo& ti, int& col) {
   const int ngroups = a.E + (a.shared_rows > 0 ? 1 : 0);
+  const int per = (ngroups + 63) / 64;
+  int64_t* lds64 = reinterpret_cast<int64_t*>(lds + 8);  // [0]: total row tiles
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const int per = (ngroups + 63) / 64;
-    const int g0 = lane * per;
     int64_t local = 0;
     for (int i = 0; i < per; ++i) {
-      const int g = g0 + i;
+      const int g = lane * per + i;
+      if (g < ngroups) {
+        const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
+        local += (rows + BM - 1) / BM;
+      }
+    }
+    int64_t incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t n = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += n;
+    }
+    if (lane == 63) lds64[0] = incl;
+    if (lane == 0) lds[0] = -1;
+  }
+  __syncthreads();
+  const int64_t nrow = lds64[0];
+  int64_t row, c;
+  const bool have = raster_tile(nrow, ncol, GM, row, c);
+  if (have && threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int64_t local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int g = lane * per + i;
       if (g < ngroups) {
         const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
         local += (rows + BM - 1) / BM;
@@ -39,32 +95,31 @@ __device__ TileInfo decode_row_tile(const GemmArgs& a, int64_t tile, int* lds4) 
       if (lane >= o) incl += n;
     }
     const int64_t excl = incl - local;
-    if (lane == 0) lds4[0] = -1;
-    // exactly one lane owns the tile (if it exists)
-    if (tile >= excl && tile < incl) {
-      int64_t acc = excl;
+    if (row >= excl && row < incl) {
+      int64_t accum = excl;
       for (int i = 0; i < per; ++i) {
-        const int g = g0 + i;
+        const int g = lane * per + i;
         const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
         const int64_t nt = (rows + BM - 1) / BM;
-        if (tile < acc + nt) {
-          lds4[0] = g;
-          lds4[1] = (g < a.E) ? a.offsets[g] : 0;
-          lds4[2] = rows;
-          lds4[3] = (int)(tile - acc) * BM;
+        if (row < accum + nt) {
+          lds[0] = g;
+          lds[1] = (g < a.E) ? a.offsets[g] : 0;
+          lds[2] = rows;
+          lds[3] = (int)(row - accum) * BM;
           break;
         }
-        acc += nt;
+        accum += nt;
       }
     }
   }
   __syncthreads();
-  TileInfo ti;
-  ti.g = lds4[0];
-  ti.r0 = lds4[1];
-  ti.rows = lds4[2];
-  ti.m0 = lds4[3];
-  return ti;
+  if (!have || lds[0] < 0) return false;
+  ti.g = lds[0];
+  ti.r0 = lds[1];
+  ti.rows = lds[2];
+  ti.m0 = lds[3];
+  col = (int)c;
+  return true;
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }

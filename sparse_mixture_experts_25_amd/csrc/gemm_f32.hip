@@ -20,22 +20,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float As[BK][kP];
   __shared__ __attribute__((aligned(16))) float Bs[BK][kP];
   __shared__ __attribute__((aligned(16))) float Cs[BM][BN + 1];
-  __shared__ int info[4];
+  __shared__ __attribute__((aligned(16))) int info[12];
   const int tid = threadIdx.x;
   const int tm = tid / 16, tn = tid % 16;
 
   int g, rows, mrow0 = 0, nb, mb = 0;
   int64_t r0;
   if (KIND == 0) {
-    TileInfo ti = decode_row_tile<BM>(a, blockIdx.x, info);
-    if (ti.g < 0) return;
+    const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
+    const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
+    TileInfo ti;
+    if (!locate_ragged_m<BM>(a, (ncols + bn - 1) / bn, 8, info, ti, nb)) return;
     g = ti.g; r0 = ti.r0; rows = ti.rows; mrow0 = ti.m0;
-    nb = blockIdx.y;
   } else {
-    g = blockIdx.y;
-    const int nN = (a.N + BN - 1) / BN;
-    mb = blockIdx.x / nN;
-    nb = blockIdx.x % nN;
+    // groups in the given order (largest first), tiles of one group
+    // consecutive with the row block fastest
+    const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
+    const int64_t per_g = (int64_t)nM * nN;
+    const int rank = (int)(blockIdx.x / per_g);
+    const int t = (int)(blockIdx.x % per_g);
+    g = a.order ? a.order[rank] : rank;
+    mb = t % nM;
+    nb = t / nM;
     if (g < a.E) {
       r0 = a.offsets[g];
       rows = a.offsets[g + 1] - a.offsets[g];
@@ -158,17 +164,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 template <int KIND, int B_KC, int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  dim3 grid;
+  int64_t n;
   if (KIND == 0) {
     const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
     const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
-    const int64_t tiles = (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
-    grid = dim3((unsigned)tiles, (ncols + bn - 1) / bn, 1);
+    n = raster_grid(row_tile_bound(a, BM), (ncols + bn - 1) / bn);
   } else {
     const int ng = a.E + (a.has_shared ? 1 : 0);
-    grid = dim3(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), ng, 1);
+    n = (int64_t)ng * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   }
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)n);
   hipLaunchKernelGGL((gemm_f32_kernel<KIND, B_KC, EPI>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

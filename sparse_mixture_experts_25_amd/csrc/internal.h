@@ -58,6 +58,7 @@ struct GemmArgs {
   int shared_rows;
   int has_shared;         // 1: an extra dense group exists (it may have 0 rows)
   int64_t max_rows;       // upper bound on the routed rows (sum over groups)
+  const int32_t* order;   // ragged-K: processing order of the groups (nullable: 0..G-1)
   const void* A; int64_t lda;
   const void* B; int64_t ldb; int64_t strideB;
   const void* A_sh; const void* B_sh;
@@ -67,6 +68,10 @@ struct GemmArgs {
   int f;  // SwiGLU half width
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+// order[0..E(+1)): groups sorted by row count, largest first (ties: lower index;
+// the shared group, index E, counts shared_rows rows).
+hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, int has_shared, int32_t* order,
+                              hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 
 struct CombineArgs {
@@ -124,7 +129,7 @@ struct RouterGradArgs {
   float* ws_partial;     // [nsplit, E, d]
   int T, d, E, dtype;
 };
-int router_grad_splits(int T);
+int router_grad_splits(int T, int E, int d);
 hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st);
 
 struct UnpermuteArgs {

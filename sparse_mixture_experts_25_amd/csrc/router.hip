@@ -5,13 +5,15 @@
 // "Mixture-of-Experts" (notes.yuuk.io), bullets on sigmoid gating with a
 // per-expert bias that only steers the selection.
 //
-// Each workgroup owns 32 tokens and all E experts. The logits are a SIMT fp32
-// register-tiled product: every thread owns 4 tokens x EPT experts and walks
-// the d_model axis in ascending order with one fused multiply-add per term, so
-// each logit is the fixed-order fp32 sum the routing decision is defined on
-// (no split of the sum, no matrix cores, no reassociation). The x chunk and the
-// router weight chunk are staged through LDS, transposed so that the per-step
-// reads are conflict-free. The gate then runs one wave per token.
+// Each workgroup owns TT (16 or 32) tokens and all E experts. The logits are a
+// SIMT fp32 register-tiled product: every thread owns TT/8 tokens x EPT experts
+// and walks the d_model axis in ascending order with one fused multiply-add per
+// term, so each logit is the fixed-order fp32 sum the routing decision is
+// defined on (no split of the sum, no matrix cores, no reassociation). The x
+// chunk and the router weight chunk are staged through two LDS stages,
+// transposed so that the per-step reads are conflict-free; the next chunk is
+// fetched into registers while the current one is consumed. The gate then runs
+// one wave per token.
 #include "common.h"
 #include "internal.h"
 
@@ -19,7 +21,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kTT = 32;   // tokens per workgroup
 constexpr int kKC = 32;   // d_model chunk staged in LDS
 
 #pragma clang fp contract(off)
@@ -58,74 +59,106 @@ __device__ __forceinline__ float sigmoid_c(float h) {
 }
 #pragma clang fp contract(on)
 
-template <typename TX, int EPT>
+template <typename TX, int EPT, int TT>
 __global__ __launch_bounds__(256) void router_fwd_kernel(
     const TX* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ offset,
     const float* __restrict__ sel_bias, float* __restrict__ probs, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int T, int d, int E, int k, int gate, int renorm) {
-  // Ws[j][e] (router weight chunk, transposed) and later Ls[t][e] (logits).
+  // Two LDS stages, each Ws[j][e] (router weight chunk, transposed) + Xs[j][t];
+  // after the loop Ls[t][e] (logits) reuses stage 0.
+  constexpr int TPT = TT / 8;         // tokens per thread
+  constexpr int XP = TT + 4;
+  constexpr int WU = (EPT * 32) * (kKC / 4) / 256;  // float4 units of W per thread (E rounded up)
+  constexpr int XU = TT * kKC / 256;                // x elements per thread
   extern __shared__ float smem[];
   const int Ep = E + 1;
-  float* Ws = smem;                       // kKC * Ep
-  float* Xs = smem + kKC * Ep;            // kKC * (kTT + 4)
-  constexpr int XP = kTT + 4;
+  const int stage_floats = kKC * Ep + kKC * XP;
 
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kTT;
-  const int tg = tid >> 5;   // token group: tokens tg*4 .. tg*4+3
+  const int t0 = blockIdx.x * TT;
+  const int tg = tid >> 5;   // token group: tokens tg*TPT .. tg*TPT+TPT-1
   const int el = tid & 31;   // expert lane: experts el + 32*j
 
-  float acc[4][EPT];
+  float acc[TPT][EPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TPT; ++i)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0f;
 
-  for (int k0 = 0; k0 < d; k0 += kKC) {
+  float4 wreg[WU];
+  float xreg[XU];
+  auto fetch = [&](int k0) {
     const int kc = min(kKC, d - k0);
-    __syncthreads();
-    // router weight chunk: E rows x kKC columns, read along the row (4 floats),
-    // stored transposed
-    for (int u = tid; u < E * (kKC / 4); u += 256) {
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      const int u = tid + i * 256;
       const int e = u / (kKC / 4);
       const int j4 = (u % (kKC / 4)) * 4;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (j4 < kc) {
-        const float4 q = *reinterpret_cast<const float4*>(wr + (int64_t)e * d + k0 + j4);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-      }
+      wreg[i] = (e < E && j4 < kc) ? *reinterpret_cast<const float4*>(wr + (int64_t)e * d + k0 + j4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ws[(j4 + i) * Ep + e] = v[i];
-    }
-    // token chunk: kTT rows x kKC columns
-    for (int u = tid; u < kTT * kKC; u += 256) {
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + i * 256;
       const int t = u / kKC, j = u % kKC;
-      float v = 0.0f;
-      if (t0 + t < T && j < kc) v = Elem<TX>::load(x, (int64_t)(t0 + t) * d + k0 + j);
-      Xs[j * XP + t] = v;
+      xreg[i] = (t0 + t < T && j < kc) ? Elem<TX>::load(x, (int64_t)(t0 + t) * d + k0 + j) : 0.0f;
     }
-    __syncthreads();
+  };
+  auto stash = [&](float* st) {
+    float* Ws = st;
+    float* Xs = st + kKC * Ep;
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      const int u = tid + i * 256;
+      const int e = u / (kKC / 4);
+      const int j4 = (u % (kKC / 4)) * 4;
+      if (e < E) {
+        Ws[(j4 + 0) * Ep + e] = wreg[i].x;
+        Ws[(j4 + 1) * Ep + e] = wreg[i].y;
+        Ws[(j4 + 2) * Ep + e] = wreg[i].z;
+        Ws[(j4 + 3) * Ep + e] = wreg[i].w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + i * 256;
+      Xs[(u % kKC) * XP + u / kKC] = xreg[i];
+    }
+  };
+
+  const int nch = (d + kKC - 1) / kKC;
+  fetch(0);
+  stash(smem);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    float* st = smem + (c & 1) * stage_floats;
+    if (c + 1 < nch) fetch((c + 1) * kKC);  // in flight during this chunk's FMAs
+    const float* Ws = st;
+    const float* Xs = st + kKC * Ep;
+    const int kc = min(kKC, d - c * kKC);
     for (int j = 0; j < kc; ++j) {
-      const float4 xv = *reinterpret_cast<const float4*>(&Xs[j * XP + tg * 4]);
-      const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+      float xs[TPT];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) xs[i] = Xs[j * XP + tg * TPT + i];
 #pragma unroll
       for (int jj = 0; jj < EPT; ++jj) {
         const int e = el + 32 * jj;
         const float w = (e < E) ? Ws[j * Ep + e] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][jj] = __builtin_fmaf(xs[i], w, acc[i][jj]);
+        for (int i = 0; i < TPT; ++i) acc[i][jj] = __builtin_fmaf(xs[i], w, acc[i][jj]);
       }
     }
+    if (c + 1 < nch) stash(smem + ((c + 1) & 1) * stage_floats);
+    __syncthreads();
   }
-  __syncthreads();
-  float* Ls = smem;  // kTT * Ep
+  float* Ls = smem;  // TT * Ep
 #pragma unroll
   for (int jj = 0; jj < EPT; ++jj) {
     const int e = el + 32 * jj;
     if (e < E) {
       const float off = offset ? offset[e] : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ls[(tg * 4 + i) * Ep + e] = offset ? acc[i][jj] + off : acc[i][jj];
+      for (int i = 0; i < TPT; ++i) Ls[(tg * TPT + i) * Ep + e] = offset ? acc[i][jj] + off : acc[i][jj];
     }
   }
   __syncthreads();
@@ -133,7 +166,7 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(
   // gate + top-k: one wave per token
   const int wave = tid >> 6, lane = tid & 63;
   constexpr int Q = (EPT * 32 + 63) / 64;  // experts per lane: e = lane + 64*q
-  for (int t = wave; t < kTT; t += 4) {
+  for (int t = wave; t < TT; t += 4) {
     const int tt = t0 + t;
     if (tt >= T) break;
     float p[Q], key[Q];
@@ -219,30 +252,38 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(
   }
 }
 
-template <typename TX, int EPT>
+template <typename TX, int EPT, int TT>
 hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
   const int Ep = a.E + 1;
-  const size_t lds = (size_t)(kKC * Ep + kKC * (kTT + 4)) * sizeof(float);
-  const int blocks = (a.T + kTT - 1) / kTT;
+  const size_t lds = 2 * (size_t)(kKC * Ep + kKC * (TT + 4)) * sizeof(float);
+  const int blocks = (a.T + TT - 1) / TT;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void*)router_fwd_kernel<TX, EPT>,
+    const hipError_t e = hipFuncSetAttribute((const void*)router_fwd_kernel<TX, EPT, TT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((router_fwd_kernel<TX, EPT>), dim3(blocks), dim3(256), lds, st,
-                     (const TX*)a.x, a.w_router, a.logit_offset, a.sel_bias, a.probs, a.topk_idx,
-                     a.topk_w, a.T, a.d, a.E, a.k, a.gate, a.renorm);
+  hipLaunchKernelGGL((router_fwd_kernel<TX, EPT, TT>), dim3(blocks), dim3(256), lds, st, (const TX*)a.x,
+                     a.w_router, a.logit_offset, a.sel_bias, a.probs, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k,
+                     a.gate, a.renorm);
   return hipGetLastError();
+}
+
+// 32 tokens per workgroup when that still gives at least two workgroups per CU
+// of a 256-CU part, else 16 (more workgroups in flight for smaller batches).
+template <typename TX, int EPT>
+hipError_t launch_router_tt(const RouterArgs& a, hipStream_t st) {
+  if ((a.T + 31) / 32 >= 512) return launch_router_t<TX, EPT, 32>(a, st);
+  return launch_router_t<TX, EPT, 16>(a, st);
 }
 
 template <typename TX>
 hipError_t launch_router_e(const RouterArgs& a, hipStream_t st) {
   const int ept = (a.E + 31) / 32;
-  if (ept <= 1) return launch_router_t<TX, 1>(a, st);
-  if (ept <= 2) return launch_router_t<TX, 2>(a, st);
-  if (ept <= 4) return launch_router_t<TX, 4>(a, st);
-  if (ept <= 8) return launch_router_t<TX, 8>(a, st);
-  return launch_router_t<TX, 16>(a, st);
+  if (ept <= 1) return launch_router_tt<TX, 1>(a, st);
+  if (ept <= 2) return launch_router_tt<TX, 2>(a, st);
+  if (ept <= 4) return launch_router_tt<TX, 4>(a, st);
+  if (ept <= 8) return launch_router_tt<TX, 8>(a, st);
+  return launch_router_tt<TX, 16>(a, st);
 }
 
 }  // namespace

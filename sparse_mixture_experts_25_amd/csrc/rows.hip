@@ -348,18 +348,35 @@ hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-int router_grad_splits(int T) { return (T + 1023) / 1024; }
+// dW_r is split over the token axis: chunks of at most 1024 tokens (each chunk
+// is summed sequentially in fp32, the chunk sums in a fixed order), and enough
+// chunks that the split kernel has about 1024 workgroups.
+static int router_grad_chunk(int T, int E, int d) {
+  const int tiles = ((E + kRG - 1) / kRG) * ((d + kRG - 1) / kRG);
+  const int want = (1024 + tiles - 1) / tiles;
+  int chunk = (T + want - 1) / want;
+  chunk = (chunk + 15) / 16 * 16;
+  if (chunk > 1024) chunk = 1024;
+  if (chunk < 64) chunk = 64;
+  return chunk;
+}
+
+int router_grad_splits(int T, int E, int d) {
+  const int c = router_grad_chunk(T, E, d);
+  return (T + c - 1) / c;
+}
 
 hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
-  const int ns = router_grad_splits(a.T);
+  const int chunk = router_grad_chunk(a.T, a.E, a.d);
+  const int ns = router_grad_splits(a.T, a.E, a.d);
   const int tiles = ((a.E + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
   if (ns == 0) {
   } else if (a.dtype == MOE_DT_BF16)
     hipLaunchKernelGGL(gemm_tn_split_kernel<uint16_t>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits,
-                       (int64_t)a.E, (const uint16_t*)a.x, (int64_t)a.d, a.E, a.d, a.T, 1024, a.ws_partial);
+                       (int64_t)a.E, (const uint16_t*)a.x, (int64_t)a.d, a.E, a.d, a.T, chunk, a.ws_partial);
   else
     hipLaunchKernelGGL(gemm_tn_split_kernel<float>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits, (int64_t)a.E,
-                       (const float*)a.x, (int64_t)a.d, a.E, a.d, a.T, 1024, a.ws_partial);
+                       (const float*)a.x, (int64_t)a.d, a.E, a.d, a.T, chunk, a.ws_partial);
   const int64_t n = (int64_t)a.E * a.d;
   hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns, n,
                      a.dw_router);
