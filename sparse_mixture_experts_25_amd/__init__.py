@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIB may point at another build of the same library (same C ABI)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = 0, 1

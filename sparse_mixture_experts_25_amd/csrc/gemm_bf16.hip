@@ -13,14 +13,14 @@
 //     over that group's rows; a group without rows writes zeros. Groups run
 //     largest first.
 //
-// Main loop: an NS-stage pipeline over 64-deep K steps. Every full step is
+// Main loop: an NS-stage pipeline over BK-deep K steps. Every full step is
 // brought into LDS with direct global->LDS 16-byte loads (each wave fills
 // 1 KB blocks; lane i of a load lands at +16*i, so the XOR swizzle of the LDS
 // layout is applied by choosing which global chunk each lane fetches). Up to
 // NS-1 steps are in flight while the matrix cores work on the current one; a
 // per-wave vmcnt wait plus one barrier per step publishes a stage. A ragged
 // K tail (last partial step) goes through registers with zero fill.
-//   K-contiguous operand ([rows][K] in memory): LDS rows of 64 k, 16-byte
+//   K-contiguous operand ([rows][K] in memory): LDS rows of BK k, 16-byte
 //     chunk c of row r at c ^ (r & 7); fragments read with ds_read_b128.
 //   MN-contiguous operand ([K][rows] in memory, the gradient matmuls): LDS
 //     k-rows as in memory, chunk c of k-row k at (c & ~7) | ((c ^ k) & 7);
@@ -31,13 +31,14 @@
 // of a group read clamped (finite) data and are never stored. The epilogue
 // stages the fp32 tile in LDS (half at a time) and writes 16-byte rows, fusing
 // the activation (forward) or its derivative (backward).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -45,10 +46,15 @@ typedef short shortx8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ LDS layouts
 // offsets in elements
-__device__ __forceinline__ int kc_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 3); }
+// K-contiguous rows hold BK/8 chunks; the swizzle permutes chunks within a row
+template <int BK>
+__device__ __forceinline__ int kc_swz(int r) { return r & (BK / 8 - 1); }
+__device__ __forceinline__ int mn_swz(int k) { return k & 7; }
+template <int BK>
+__device__ __forceinline__ int kc_off(int r, int c) { return r * BK + ((c ^ kc_swz<BK>(r)) << 3); }
 template <int R>
 __device__ __forceinline__ int mn_off(int k, int c) {
-  return k * R + (((c & ~7) | ((c ^ k) & 7)) << 3);
+  return k * R + (((c & ~7) | ((c ^ mn_swz(k)) & 7)) << 3);
 }
 
 // ------------------------------------------------------------ direct loads
@@ -58,17 +64,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One 16-byte global->LDS load per lane; the 64 lanes of the wave fill the
 // 1 KB block at LDS byte address `lds_block` (wave-uniform), lane i at +16*i.
+// The global address is a per-lane 32-bit byte offset (VGPR) plus a
+// wave-uniform 64-bit base (SGPR pair), so a K step only moves the base.
 // M0 holds the LDS address for the instruction and is restored afterwards.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_block) {
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds_block) {
+  // readfirstlane returns int: widen through uint32_t, never sign-extend a half
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_block))
+      : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_block))
       : "memory");
 }
 
@@ -82,50 +95,61 @@ template <int L>
 __device__ __forceinline__ void wait_steps(int steps) {
   if (steps <= 0) wait_vm<0>();
   else if (steps == 1) wait_vm<L>();
-  else wait_vm<2 * L>();
+  else if (steps == 2) wait_vm<2 * L>();
+  else if (steps == 3) wait_vm<3 * L>();
+  else wait_vm<4 * L>();
 }
 
-// K-contiguous tile, R rows x 64 k. rowptr(r) = global address of (row r, k0).
-template <int R, typename RowPtr>
-__device__ __forceinline__ void dma_kc(uint32_t lds_tile, int wave, int lane, RowPtr rowptr) {
+// Per-lane byte offsets of the direct loads of one tile, computed once per
+// workgroup (they depend on the tile, not on the K step).
+template <int R, int BK>
+struct DmaPlan {
+  static constexpr int NB = R * BK * 2 / 1024;  // 1 KB blocks in the tile
+  static constexpr int Q = NB / 4;               // blocks per wave
+  uint32_t voff[Q];
+  // K-contiguous: rowidx(r) = source row (clamped / remapped) of tile row r
+  template <typename RowIdx>
+  __device__ void make_kc(int wave, int lane, int64_t ld, RowIdx rowidx) {
+    constexpr int CPR = BK / 8;
 #pragma unroll
-  for (int q = 0; q < R / 32; ++q) {
-    const int blk = wave * (R / 32) + q;
-    const int p = blk * 64 + lane;
-    const int r = p >> 3, pc = p & 7;
-    const int c = pc ^ (r & 7);
-    dma16(rowptr(r) + 8 * c, lds_tile + blk * 1024);
+    for (int q = 0; q < Q; ++q) {
+      const int p = (wave * Q + q) * 64 + lane;
+      const int r = p / CPR, pc = p % CPR;
+      const int c = pc ^ kc_swz<BK>(r);
+      voff[q] = (uint32_t)(((int64_t)rowidx(r) * ld + 8 * c) * 2);
+    }
   }
-}
-
-// MN-contiguous tile, 64 k-rows x R. kptr(kr) = global address of (k0 + kr, mn0);
-// column chunks at or past `cvalid` read the last valid chunk.
-template <int R, typename KPtr>
-__device__ __forceinline__ void dma_mn(uint32_t lds_tile, int wave, int lane, KPtr kptr, int cvalid) {
-  constexpr int CPR = R / 8;
+  // MN-contiguous: k-row kr at kr * ld, column chunks clamped to cvalid
+  __device__ void make_mn(int wave, int lane, int64_t ld, int cvalid) {
+    constexpr int CPR = R / 8;
 #pragma unroll
-  for (int q = 0; q < R / 32; ++q) {
-    const int blk = wave * (R / 32) + q;
-    const int p = blk * 64 + lane;
-    const int kr = p / CPR, pc = p % CPR;
-    const int c = (pc & ~7) | ((pc ^ kr) & 7);
-    const int cc = c < cvalid ? c : cvalid - 1;
-    dma16(kptr(kr) + 8 * cc, lds_tile + blk * 1024);
+    for (int q = 0; q < Q; ++q) {
+      const int p = (wave * Q + q) * 64 + lane;
+      const int kr = p / CPR, pc = p % CPR;
+      const int c = (pc & ~7) | ((pc ^ mn_swz(kr)) & 7);
+      const int cc = c < cvalid ? c : cvalid - 1;
+      voff[q] = (uint32_t)(((int64_t)kr * ld + 8 * cc) * 2);
+    }
   }
-}
+  __device__ void issue(const uint16_t* base, uint32_t lds_tile, int wave) const {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) dma16s(voff[q], base, lds_tile + (wave * Q + q) * 1024);
+  }
+};
 
 // Zero-filled register path for a partial K step (k >= kvalid reads as zero).
-template <int R, typename RowPtr>
+template <int R, int BK, typename RowPtr>
 __device__ __forceinline__ void tail_kc(uint16_t* tile, RowPtr rowptr, int rvalid, int kvalid) {
-  for (int u = threadIdx.x; u < R * 8; u += kThreads) {
-    const int r = u >> 3, c = u & 7;
+  constexpr int CPR = BK / 8;
+  for (int u = threadIdx.x; u < R * CPR; u += kThreads) {
+    const int r = u / CPR, c = u % CPR;
     const u128 v = (r < rvalid && 8 * c < kvalid) ? ld128(rowptr(r) + 8 * c) : zero128();
-    st128(tile + kc_off(r, c), v);
+    st128(tile + kc_off<BK>(r, c), v);
   }
 }
-template <int R, typename KPtr>
+template <int R, int BK, typename KPtr>
 __device__ __forceinline__ void tail_mn(uint16_t* tile, KPtr kptr, int cvalid, int kvalid) {
-  for (int u = threadIdx.x; u < 64 * (R / 8); u += kThreads) {
+  for (int u = threadIdx.x; u < BK * (R / 8); u += kThreads) {
     const int kr = u / (R / 8), c = u % (R / 8);
     const u128 v = (kr < kvalid && c < cvalid) ? ld128(kptr(kr) + 8 * c) : zero128();
     st128(tile + mn_off<R>(kr, c), v);
@@ -135,15 +159,16 @@ __device__ __forceinline__ void tail_mn(uint16_t* tile, KPtr kptr, int cvalid, i
 // ------------------------------------------------------------ fragments
 // A/B fragment of v_mfma_f32_32x32x16_bf16: lane l holds 8 consecutive k
 // (8*(l/32) .. +7 of the 16-k step s) of row/column (base + l % 32).
+template <int BK>
 __device__ __forceinline__ bf16x8 frag_kc(const uint16_t* tile, int base, int s, int lane) {
-  return *reinterpret_cast<const bf16x8*>(tile + kc_off(base + (lane & 31), 2 * s + (lane >> 5)));
+  return *reinterpret_cast<const bf16x8*>(tile + kc_off<BK>(base + (lane & 31), 2 * s + (lane >> 5)));
 }
 
 __device__ __forceinline__ shortx4 read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
 }
 
-// From a [64 k][R] tile: per 16-lane group, the transpose read gives lane i
+// From a [BK k][R] tile: per 16-lane group, the transpose read gives lane i
 // the 4 k-values of column c0 + i when source lane j reads 4 columns
 // c0 + 4*(j & 3) .. +3 of k-row k0 + (j >> 2). Two reads cover 8 k.
 template <int R>
@@ -158,8 +183,10 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t* tile, int base, int s,
 }
 
 // ------------------------------------------------------------ kernel
-template <int BM, int BN, int NS, int KIND, int B_KC, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, (BM * BN >= 65536 ? 1 : 2)))) void gemm_bf16_kernel(
+    GemmArgs a) {
+  constexpr int kBK = BK;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_KC = (KIND == 0);
@@ -170,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int HM = BM / 2;  // the fp32 tile is staged half (one wave row) at a time
   constexpr int kStageBytes = HM * CP * 4;
   constexpr int kLds = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
-  constexpr int L = BM / 32 + BN / 32;  // direct loads per wave per K step
+  constexpr int L = (BM + BN) * BK * 2 / 1024 / 4;  // direct loads per wave per K step
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
   __shared__ __attribute__((aligned(16))) int info[12];
 
@@ -253,22 +280,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     return Borig + src * a.ldb + k0;
   };
 
+  DmaPlan<BM, BK> pa;
+  DmaPlan<BN, BK> pb;
+  if (A_KC) pa.make_kc(wave, lane, a.lda, [&](int r) { return r < a_valid ? r : a_valid - 1; });
+  else pa.make_mn(wave, lane, a.lda, a_valid);
+  if (B_IS_KC)
+    pb.make_kc(wave, lane, a.ldb, [&](int r) {
+      if (EPI == EPI_SWIGLU_FWD) {
+        const int hc0 = h0 + (r < BN / 2 ? r : r - BN / 2);
+        const int hc = hc0 < a.f ? hc0 : a.f - 1;
+        return r < BN / 2 ? hc : a.f + hc;
+      }
+      return nb * BN + (r < b_valid ? r : b_valid - 1);
+    });
+  else pb.make_mn(wave, lane, a.ldb, b_valid);
   auto dma_step = [&](int stage, int k0) {
     const uint32_t sa = lds0 + stage * kStage * 2;
     const uint32_t sb = sa + BM * kBK * 2;
-    if (A_KC) dma_kc<BM>(sa, wave, lane, [&](int r) { return a_row(r, k0); });
-    else dma_mn<BM>(sa, wave, lane, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid);
-    if (B_IS_KC) dma_kc<BN>(sb, wave, lane, [&](int r) { return b_row(r, k0); });
-    else dma_mn<BN>(sb, wave, lane, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid);
+    pa.issue(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
+    pb.issue(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
   auto tail_step = [&](int stage, int k0) {
     uint16_t* ta = stages + stage * kStage;
     uint16_t* tb = ta + BM * kBK;
     const int kv = K - k0;
-    if (A_KC) tail_kc<BM>(ta, [&](int r) { return a_row(r, k0); }, BM, kv);
-    else tail_mn<BM>(ta, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid, kv);
-    if (B_IS_KC) tail_kc<BN>(tb, [&](int r) { return b_row(r, k0); }, BN, kv);
-    else tail_mn<BN>(tb, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid, kv);
+    if (A_KC) tail_kc<BM, BK>(ta, [&](int r) { return a_row(r, k0); }, BM, kv);
+    else tail_mn<BM, BK>(ta, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid, kv);
+    if (B_IS_KC) tail_kc<BN, BK>(tb, [&](int r) { return b_row(r, k0); }, BN, kv);
+    else tail_mn<BN, BK>(tb, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid, kv);
   };
 
   floatx16 acc[FM][FN];
@@ -279,38 +318,86 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nfull = K / kBK;
-  const int nk = nfull + ((K % kBK) ? 1 : 0);
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nfull) dma_step(s, s * kBK);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt % NS;
-    if (kt < nfull) {
-      const int later = min(NS - 2, nfull - 1 - kt);  // steps issued after kt, maybe in flight
-      wait_steps<L>(later);
-    } else {
-      tail_step(stage, kt * kBK);
-    }
-    __syncthreads();
-    if (kt + NS - 1 < nfull) dma_step((kt + NS - 1) % NS, (kt + NS - 1) * kBK);
+  // Main loop, pipelined at the granularity of one 16-deep MFMA sub-step: while
+  // the MFMAs of sub-step (k, s) run, the fragments of the next sub-step are
+  // read from LDS into the other register set, so the matrix cores do not wait
+  // on LDS. Before the first fragments of step k+1 are read, that step is
+  // published (its direct loads waited for, one barrier); the LDS slot of step
+  // k is then free (all its fragments are in registers) and receives step k+NS.
+  constexpr int SUB = kBK / 16;  // even: sub-step s always uses register set s & 1
+  constexpr int RD = FM * (A_KC ? 1 : 2) + FN * (B_IS_KC ? 1 : 2);  // LDS reads per sub-step
+  constexpr int MF = FM * FN;                                         // MFMAs per sub-step
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](auto set, int stage, int s) {
+    constexpr int S = decltype(set)::value;
     const uint16_t* ta = stages + stage * kStage;
     const uint16_t* tb = ta + BM * kBK;
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i)
+      fa[S][i] = A_KC ? frag_kc<BK>(ta, wm * WM + i * 32, s, lane) : frag_mn<BM>(ta, wm * WM + i * 32, s, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = A_KC ? frag_kc(ta, wm * WM + i * 32, s, lane) : frag_mn<BM>(ta, wm * WM + i * 32, s, lane);
+    for (int j = 0; j < FN; ++j)
+      fb[S][j] = B_IS_KC ? frag_kc<BK>(tb, wn * WN + j * 32, s, lane) : frag_mn<BN>(tb, wn * WN + j * 32, s, lane);
+  };
+  auto mfmas = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = B_IS_KC ? frag_kc(tb, wn * WN + j * 32, s, lane) : frag_mn<BN>(tb, wn * WN + j * 32, s, lane);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S][i], fb[S][j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+    // one LDS read, then a share of the MFMAs, RD times
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int r = 0; r < RD; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (MF + RD - 1) / RD, 0);
     }
+  };
+
+  const int nfull = K / kBK;
+  const int nk = nfull + ((K % kBK) ? 1 : 0);
+  // Direct loads issued before publish(k): steps 0 .. min(NS-1, nfull-1) for
+  // k = 0 (prologue); steps 0 .. min(k+NS-2, nfull-1) for k >= 1. The wait lets
+  // the later ones stay in flight.
+  auto publish = [&](int k) {
+    if (k < nfull) wait_steps<L>(k == 0 ? min(NS - 1, nfull - 1) : min(NS - 2, nfull - 1 - k));
+    else tail_step(k % NS, k * kBK);
+    __syncthreads();
+  };
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nfull) dma_step(s, s * kBK);
+  // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
+  auto inner = [&](int stage) {
+#pragma unroll
+    for (int s = 0; s + 1 < SUB; ++s) {
+      if (s & 1) {
+        read_frags(std::integral_constant<int, 0>(), stage, s + 1);
+        mfmas(std::integral_constant<int, 1>());
+      } else {
+        read_frags(std::integral_constant<int, 1>(), stage, s + 1);
+        mfmas(std::integral_constant<int, 0>());
+      }
+      interleave();
+    }
+  };
+  if (nk > 0) {
+    publish(0);
+    read_frags(std::integral_constant<int, 0>(), 0, 0);
+    for (int k = 0; k + 1 < nk; ++k) {
+      const int stage = k % NS;
+      inner(stage);
+      // last sub-step of step k (set 1, SUB is even) overlaps the first reads of step k+1
+      publish(k + 1);
+      if (k + NS < nfull) dma_step(stage, (k + NS) * kBK);
+      read_frags(std::integral_constant<int, 0>(), (k + 1) % NS, 0);
+      mfmas(std::integral_constant<int, 1>());
+      interleave();
+    }
+    inner((nk - 1) % NS);
+    mfmas(std::integral_constant<int, 1>());
   }
   __syncthreads();
 
@@ -409,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int NS, int KIND, int B_KC, int EPI>
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   int64_t n;
   if (KIND == 0) {
@@ -421,26 +508,31 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     n = (int64_t)ng * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   }
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NS, KIND, B_KC, EPI>), dim3((unsigned)n), dim3(kThreads), 0, st,
-                     a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI>), dim3((unsigned)n), dim3(kThreads), 0,
+                     st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int BK, int NS>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
-  if (a.kind == 1) return launch_t<BM, BN, NS, 1, 0, EPI_STORE>(a, st);
+  // the direct loads address each operand as base + 32-bit per-lane byte offset
+  const int64_t lim = int64_t(1) << 32;
+  const int64_t b_rows = a.kind == 0 && a.b_kcontig ? (a.epi == EPI_SWIGLU_FWD ? 2 * (int64_t)a.f : a.N) : BK;
+  const int64_t a_rows = a.kind == 0 ? BM : BK;
+  if (a_rows * a.lda * 2 >= lim || b_rows * a.ldb * 2 >= lim) return hipErrorInvalidValue;
+  if (a.kind == 1) return launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE>(a, st);
   if (a.b_kcontig) {
     switch (a.epi) {
-      case EPI_STORE: return launch_t<BM, BN, NS, 0, 1, EPI_STORE>(a, st);
-      case EPI_RELU_FWD: return launch_t<BM, BN, NS, 0, 1, EPI_RELU_FWD>(a, st);
-      case EPI_SWIGLU_FWD: return launch_t<BM, BN, NS, 0, 1, EPI_SWIGLU_FWD>(a, st);
+      case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE>(a, st);
+      case EPI_RELU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_RELU_FWD>(a, st);
+      case EPI_SWIGLU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_SWIGLU_FWD>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
   switch (a.epi) {
-    case EPI_STORE: return launch_t<BM, BN, NS, 0, 0, EPI_STORE>(a, st);
-    case EPI_RELU_BWD: return launch_t<BM, BN, NS, 0, 0, EPI_RELU_BWD>(a, st);
-    case EPI_SWIGLU_BWD: return launch_t<BM, BN, NS, 0, 0, EPI_SWIGLU_BWD>(a, st);
+    case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE>(a, st);
+    case EPI_RELU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_RELU_BWD>(a, st);
+    case EPI_SWIGLU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_SWIGLU_BWD>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -473,15 +565,19 @@ hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, in
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 (each wave 128x128, two stages in flight) when the
-// groups are large enough to fill it on average; 128x128 with four stages
-// otherwise (small expert batches, where the weights stream from HBM and the
-// row tile is mostly padding).
+// Tile choice: 256x256 (each wave 128x128; 32-deep K steps, four stages, one
+// workgroup per CU) when the groups are large enough to fill it on average;
+// otherwise 128x128 (64-deep K steps, two stages, 64 KB of LDS so that two
+// workgroups share a CU and one's loads overlap the other's matrix work: small
+// expert batches, where the weights stream from HBM and the row tile is mostly
+// padding). A 256x256 tile with 64-deep steps does not fit the register file
+// with the transposed-operand fragment reads (the accumulators spill).
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
-  return big ? launch_tiles<256, 256, 2>(a, st) : launch_tiles<128, 128, 4>(a, st);
+  return big ? launch_tiles<256, 256, 32, 4>(a, st)
+             : launch_tiles<128, 128, 64, 2>(a, st);
 }
 
 }  // namespace moe
