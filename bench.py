@@ -28,6 +28,39 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # flop/s, dense bf16 matrix cores
 PEAK_F32_VALU = 78.6e12    # flop/s, fp32 vector FMA without packed-fp32 instructions
 
+# Kernel sources whose hash a measured HBM-traffic figure is tied to.
+GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "internal.h", "common.h", "api.hip")
+
+
+def sources_sha(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_25_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from the committed counter summary
+    profiles/hbm_traffic_<workload>.txt (FETCH_SIZE + WRITE_SIZE per dispatch,
+    scaled by the same counters' reading for a plain copy of known size), or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    sha, val = None, None
+    with open(path) as fh:
+        for ln in fh:
+            parts = ln.split()
+            if len(parts) >= 2 and parts[0] == "sources_sha":
+                sha = parts[1]
+            if len(parts) >= 2 and parts[0] == f"{stage}_bytes_per_launch":
+                val = float(parts[1])
+    if val is None or sha != sources_sha(GEMM_SOURCES):
+        return None
+    return val
+
 
 class HipEvents:
     """Raw HIP events (for the library's stage timing hook)."""
@@ -105,13 +138,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="switch_base")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (a known-size "
+                         "kernel to scale HBM counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the layer on one GPU only; --gpus {args.gpus} is not supported "
-              f"(multi-GPU sharding is a design note, not an implementation).", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -180,7 +216,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": by / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(c.name, dom)
     roof["kernel"] = dom
     roof["launch_ms"] = dom_ms
 
@@ -203,6 +239,14 @@ def main():
                    "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12},
         "roofline": roof,
     }
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.stages:
         print(json.dumps({"stage_ms": per_stage}), file=sys.stderr)
     line["stage_ms"] = {k: round(v, 4) for k, v in per_stage.items()}
