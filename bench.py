@@ -26,7 +26,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # flop/s, dense bf16 matrix cores
-PEAK_F32_VALU = 78.6e12    # flop/s, fp32 vector FMA without packed-fp32 instructions
+# flop/s, fp32 vector FMA without packed-fp32 instructions: 256 CUs x 64 FMA lanes
+# per clock x 2 flop x 2.4 GHz (packed fp32 would double it; it is not generated)
+PEAK_F32_VALU = 78.6e12
 
 # Kernel sources whose hash a measured HBM-traffic figure is tied to.
 GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "internal.h", "common.h", "api.hip")
@@ -210,7 +212,11 @@ def main():
     ne = int(((offs[1:] - offs[:-1]) > 0).sum())
     work = stage_work(c, rows, ne)
     fl, by = work[dom]
-    if fl and fl / max(by, 1) > PEAK_BF16 / PEAK_HBM and dom.startswith(("ffn", "bwd_dgrad", "bwd_wgrad")):
+    if dom in ("route", "bwd_router_grads"):
+        # exact fp32 router: sequential fp32 FMA on the vector units
+        roof = {"bound": "alu", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12,
+                "unit": "TFLOP/s"}
+    elif fl and fl / max(by, 1) > PEAK_BF16 / PEAK_HBM and dom.startswith(("ffn", "bwd_dgrad", "bwd_wgrad")):
         roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
     else:
