@@ -184,7 +184,7 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t* tile, int base, int s,
 
 // ------------------------------------------------------------ kernel
 template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, (BM * BN >= 65536 ? 1 : 2)))) void gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM * BN >= 65536 ? 1 : 3), (BM * BN >= 65536 ? 1 : 3)))) void gemm_bf16_kernel(
     GemmArgs a) {
   constexpr int kBK = BK;
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -567,17 +567,17 @@ hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, in
 
 // Tile choice: 256x256 (each wave 128x128; 32-deep K steps, four stages, one
 // workgroup per CU) when the groups are large enough to fill it on average;
-// otherwise 128x128 (64-deep K steps, two stages, 64 KB of LDS so that two
-// workgroups share a CU and one's loads overlap the other's matrix work: small
-// expert batches, where the weights stream from HBM and the row tile is mostly
-// padding). A 256x256 tile with 64-deep steps does not fit the register file
+// otherwise 128x128 (32-deep K steps, three stages, 48 KB of LDS and at most
+// 168 registers per lane, so that three workgroups share a CU and their loads
+// overlap each other's matrix work and epilogues: small expert batches, where
+// the weights stream from HBM and the row tile is mostly padding). A 256x256 tile with 64-deep steps does not fit the register file
 // with the transposed-operand fragment reads (the accumulators spill).
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
   return big ? launch_tiles<256, 256, 32, 4>(a, st)
-             : launch_tiles<128, 128, 64, 2>(a, st);
+             : launch_tiles<128, 128, 32, 3>(a, st);
 }
 
 }  // namespace moe

@@ -26,7 +26,10 @@ __host__ __device__ inline int64_t row_tile_bound(const GemmArgs& a, int BM) {
 // remapped so that each XCD owns one contiguous range of logical tiles, and the
 // logical order walks groups of GM row tiles across all column tiles, so that
 // concurrently running workgroups on one XCD share operand tiles in its L2.
-// The grid is 1-D with nrow * ncol rounded up to a multiple of 8.
+// The grid is 1-D with at least nrow * ncol rounded up to a multiple of 8
+// workgroups (a ragged-M launch sizes it from an upper bound on nrow). The map
+// bid -> L is a bijection from the workgroups with bid / 8 < per onto
+// [0, 8 * per); every other workgroup has no tile.
 constexpr int kXcds = 8;
 __host__ __device__ inline int64_t raster_grid(int64_t nrow, int64_t ncol) {
   return (nrow * ncol + kXcds - 1) / kXcds * kXcds;
@@ -35,6 +38,7 @@ __device__ inline bool raster_tile(int64_t nrow, int64_t ncol, int GM, int64_t& 
   const int64_t total = nrow * ncol;
   const int64_t per = raster_grid(nrow, ncol) / kXcds;
   const int64_t bid = blockIdx.x;
+  if (bid / kXcds >= per) return false;
   const int64_t L = (bid % kXcds) * per + bid / kXcds;
   if (L >= total) return false;
   const int64_t gsize = (int64_t)GM * ncol;
