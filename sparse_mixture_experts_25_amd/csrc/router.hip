@@ -5,23 +5,22 @@
 // "Mixture-of-Experts" (notes.yuuk.io), bullets on sigmoid gating with a
 // per-expert bias that only steers the selection.
 //
-// Each workgroup owns TT (16 or 32) tokens and all E experts. The logits are a
-// SIMT fp32 register-tiled product: every thread owns TT/8 tokens x EPT experts
-// and walks the d_model axis in ascending order with one fused multiply-add per
-// term, so each logit is the fixed-order fp32 sum the routing decision is
-// defined on (no split of the sum, no matrix cores, no reassociation). The x
-// chunk and the router weight chunk are staged through two LDS stages,
-// transposed so that the per-step reads are conflict-free; the next chunk is
-// fetched into registers while the current one is consumed. The gate then runs
-// one wave per token.
+// The logit h[t,e] is the fp32 sum over j = 0..d-1 in ascending order of one
+// fused multiply-add per term, starting from +0, so each lane owns whole dot
+// products (no split of the sum, no matrix cores, no reassociation).
+//
+// Work split (two kernels). Logits: a wave owns 64 tokens (one per lane) and
+// four experts. For a given j the router weight of an expert is the same for
+// all 64 lanes, so the weights are read with scalar loads into SGPRs and enter
+// each v_fma_f32 as its scalar operand; each lane streams its own x row with
+// vector loads. The logits go to the probabilities buffer. Gate and top-k
+// then run one wave per token on that row.
 #include "common.h"
 #include "internal.h"
 
 namespace moe {
 
 namespace {
-
-constexpr int kKC = 32;   // d_model chunk staged in LDS
 
 #pragma clang fp contract(off)
 // Fixed-operation fp32 exponential: Cody-Waite range reduction (Cody & Waite,
@@ -59,238 +58,462 @@ __device__ __forceinline__ float sigmoid_c(float h) {
 }
 #pragma clang fp contract(on)
 
-template <typename TX, int EPT, int TT>
-__global__ __launch_bounds__(256) void router_fwd_kernel(
+// Gate and top-k of one token whose logits h[q] (expert lane + 64 q) sit in
+// the registers of the wave.
+template <int QE>
+__device__ __forceinline__ void gate_topk(const float* h, const float* __restrict__ sel_bias, int lane, int E,
+                                          int k, int gate, int renorm, int64_t tt, float* __restrict__ probs,
+                                          int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  float p[QE], key[QE];
+  if (gate == MOE_GATE_SOFTMAX) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+      const int e = lane + 64 * q;
+      key[q] = (e < E) ? h[q] : -__builtin_inff();
+      m = fmaxf(m, key[q]);
+    }
+    m = wave_max(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+      const int e = lane + 64 * q;
+      p[q] = (e < E) ? expf(key[q] - m) : 0.0f;
+      s += p[q];
+    }
+    s = wave_sum(s);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int q = 0; q < QE; ++q) p[q] *= inv;
+  } else {
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) {
+        p[q] = sigmoid_c(h[q]);
+        key[q] = sel_bias ? p[q] + sel_bias[e] : p[q];
+      } else {
+        p[q] = 0.0f;
+        key[q] = -__builtin_inff();
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QE; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) probs[tt * E + e] = p[q];
+  }
+  // top-k: k rounds of a wave argmax on (key desc, index asc)
+  uint32_t taken = 0;
+  int my_idx = 0;
+  float my_p = 0.0f, psum = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    float bk = -__builtin_inff();
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E && !(taken & (1u << q)) && (key[q] > bk || be == 0x7fffffff)) {
+        bk = key[q];
+        be = e;
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ok > bk || (ok == bk && oe < be)) {
+        bk = ok;
+        be = oe;
+      }
+    }
+    // be is now wave-uniform
+    const int qw = be >> 6;
+    float pv = 0.0f;
+#pragma unroll
+    for (int q = 0; q < QE; ++q)
+      if (q == qw) pv = p[q];
+    pv = __shfl(pv, be & 63, kWave);
+    if ((be & 63) == lane) taken |= 1u << qw;
+    if (lane == r) {
+      my_idx = be;
+      my_p = pv;
+    }
+    psum += pv;
+  }
+  if (lane < k) {
+    topk_idx[tt * k + lane] = my_idx;
+    topk_w[tt * k + lane] = renorm ? my_p / psum : my_p;
+  }
+}
+
+// 8 consecutive x values of one token as fp32 (16 bytes of bf16, or two
+// 16-byte fp32 loads).
+template <typename TX>
+struct X8;
+template <>
+struct X8<uint16_t> {
+  uint4 r;
+  __device__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ float get(int i) const {
+    const uint32_t w = i < 2 ? r.x : i < 4 ? r.y : i < 6 ? r.z : r.w;
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct X8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ float get(int i) const {
+    return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w : i == 4 ? b.x : i == 5 ? b.y : i == 6 ? b.z : b.w;
+  }
+};
+
+// Four router weights of one expert (wave-uniform address, read into SGPRs).
+struct W4 {
+  float v[4];
+  __device__ void load(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+
+constexpr int kEW = 4;   // experts per wave
+constexpr int kWaves = 4;
+
+// Logits: lane = token (64 per wave), the wave's kEW experts are uniform. Each
+// lane streams its own x row (vector loads, two 8-wide blocks ahead); the
+// weights of the wave's experts come through scalar loads one block ahead.
+// Writes h (without the offset) to out[T, E].
+template <typename TX>
+__global__ __launch_bounds__(256) void router_logits_kernel(const TX* __restrict__ x, const float* __restrict__ wr,
+                                                            float* __restrict__ out, int T, int d, int E) {
+  // 1-D grid, XCD-aware: workgroups go to the 8 XCDs round-robin, and each
+  // XCD takes a contiguous range of (token tile, expert group) pairs with the
+  // expert group fastest, so all expert groups of a 64-token x tile run on one
+  // XCD back to back and the tile is read from HBM once.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int neg = (E + kEW * kWaves - 1) / (kEW * kWaves);
+  const int64_t total = (int64_t)((T + 63) / 64) * neg;
+  const int64_t per = (total + 7) / 8;
+  if ((int64_t)blockIdx.x / 8 >= per) return;
+  const int64_t L = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (L >= total) return;
+  const int t = (int)(L / neg) * 64 + lane;
+  const int e0 = ((int)(L % neg) * kWaves + wave) * kEW;
+  if (e0 >= E) return;
+  const TX* xr = x + (int64_t)min(t, T - 1) * d;
+  const float* wbase = wr + (int64_t)e0 * d;  // rows e0 .. e0 + kEW - 1 (clamped below)
+  const int64_t wstep[kEW] = {0, (int64_t)min(1, E - 1 - e0) * d, (int64_t)min(2, E - 1 - e0) * d,
+                              (int64_t)min(3, E - 1 - e0) * d};
+
+  float acc[kEW];
+#pragma unroll
+  for (int i = 0; i < kEW; ++i) acc[i] = 0.0f;
+
+  // Blocks of 4 along d with ping-pong weight buffers (4 experts x 4 values =
+  // 16 SGPRs each). Scalar loads may complete out of order, so the only wait
+  // for them is lgkmcnt(0), placed by the compiler before the first use: each
+  // block starts with its first multiply-adds (waiting for its own weights,
+  // issued one block earlier) and only then issues the next block's scalar
+  // loads, which stay in flight during the rest of the block. x is read 8
+  // values at a time, one 16-byte vector load per lane, two loads ahead.
+  const int nb = d / 4;
+  W4 w0[kEW], w1[kEW];
+  auto loadw = [&](W4* w, int blk) {
+#pragma unroll
+    for (int i = 0; i < kEW; ++i) w[i].load(wbase + wstep[i] + 4 * blk);
+  };
+  auto fma_j = [&](float xv, const W4* wc, int j) {
+#pragma unroll
+    for (int i = 0; i < kEW; ++i) acc[i] = __builtin_fmaf(xv, wc[i].v[j], acc[i]);
+  };
+  auto block = [&](const X8<TX>& xc, int half, const W4* wc, W4* wn, int nxt) {
+    fma_j(xc.get(4 * half), wc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nxt < nb) loadw(wn, nxt);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) fma_j(xc.get(4 * half + j), wc, j);
+  };
+  X8<TX> x0, x1;
+  x0.load(xr);
+  if (nb > 2) x1.load(xr + 8);
+  loadw(w0, 0);
+  // nb is even (d is a multiple of 8): 8 values of x per pair of blocks
+  for (int b = 0; b < nb; b += 4) {
+    block(x0, 0, w0, w1, b + 1);
+    block(x0, 1, w1, w0, b + 2);
+    if (b + 4 < nb) x0.load(xr + 4 * (b + 4));
+    if (b + 2 >= nb) break;
+    block(x1, 0, w0, w1, b + 3);
+    block(x1, 1, w1, w0, b + 4);
+    if (b + 6 < nb) x1.load(xr + 4 * (b + 6));
+  }
+  if (t < T) {
+    float* o = out + (int64_t)t * E + e0;
+    if (e0 + kEW <= E && (E & 3) == 0) {  // 16-byte aligned row segment
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEW; ++i)
+        if (e0 + i < E) o[i] = acc[i];
+    }
+  }
+}
+
+// Gate and top-k, one wave per token: reads the logits from probs, adds the
+// offset (one fp32 add), overwrites probs with the gate values.
+template <int QE>
+__global__ __launch_bounds__(256) void router_gate_kernel(const float* __restrict__ offset,
+                                                          const float* __restrict__ sel_bias, float* probs,
+                                                          int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                          int T, int E, int k, int gate, int renorm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tt >= T) return;
+  float h[QE];
+#pragma unroll
+  for (int q = 0; q < QE; ++q) {
+    const int e = lane + 64 * q;
+    h[q] = 0.0f;
+    if (e < E) {
+      h[q] = probs[tt * E + e];
+      if (offset) h[q] = h[q] + offset[e];
+    }
+  }
+  gate_topk<QE>(h, sel_bias, lane, E, k, gate, renorm, tt, probs, topk_idx, topk_w);
+}
+
+// Register-tiled variant for wide d_model, where streaming x once per
+// workgroup matters more than occupancy. A workgroup owns TT = TG * TPT tokens
+// and every expert; thread (tg, eg) owns tokens tg*TPT .. +TPT-1 and experts
+// 4*(eg + EG*h) + 0..3 (h < NE4), one dot product per (token, expert) walked
+// in ascending j as above. The x chunk (Xs[j][t]) and the router weight chunk
+// (Ws[j][e]) are staged through two LDS stages, transposed so that a thread's
+// TPT tokens and each of its 4-expert groups are one 16-byte LDS read; the
+// next chunk is fetched into registers while the current one is consumed.
+// The logits then go through LDS to one wave per token for the gate.
+template <typename TX>
+struct XV;
+template <>
+struct XV<uint16_t> {  // 8 bf16 per 16 bytes
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* v) {
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct XV<float> {  // 4 fp32 per 16 bytes
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* v) {
+    const float4 r = *reinterpret_cast<const float4*>(p);
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+};
+
+template <typename TX, int TPT, int NE4, int EG>
+__global__ __launch_bounds__(256) void router_tile_kernel(
     const TX* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ offset,
     const float* __restrict__ sel_bias, float* __restrict__ probs, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int T, int d, int E, int k, int gate, int renorm) {
-  // Two LDS stages, each Ws[j][e] (router weight chunk, transposed) + Xs[j][t];
-  // after the loop Ls[t][e] (logits) reuses stage 0.
-  constexpr int TPT = TT / 8;         // tokens per thread
-  constexpr int XP = TT + 4;
-  constexpr int WU = (EPT * 32) * (kKC / 4) / 256;  // float4 units of W per thread (E rounded up)
-  constexpr int XU = TT * kKC / 256;                // x elements per thread
+  constexpr int TG = 256 / EG;
+  constexpr int TT = TG * TPT;
+  constexpr int EPT = 4 * NE4;
+  constexpr int EMAX = 4 * EG * NE4;
+  constexpr int KC = 32;
+  constexpr int XP = TT + 4;    // x row (16-byte aligned)
+  constexpr int EP = EMAX + 4;  // weight row (16-byte aligned)
+  constexpr int STAGE = KC * (EP + XP);
+  constexpr int NX = XV<TX>::N;
+  constexpr int XUNITS = TT * KC / NX;     // 16-byte x loads of a chunk
+  constexpr int XU = (XUNITS + 255) / 256;  // per thread
+  constexpr int WU = EMAX * KC / 4 / 256;   // float4 weight loads per thread
+  static_assert(WU >= 1, "tile too small");
   extern __shared__ float smem[];
-  const int Ep = E + 1;
-  const int stage_floats = kKC * Ep + kKC * XP;
 
   const int tid = threadIdx.x;
+  const int eg = tid % EG, tg = tid / EG;
   const int t0 = blockIdx.x * TT;
-  const int tg = tid >> 5;   // token group: tokens tg*TPT .. tg*TPT+TPT-1
-  const int el = tid & 31;   // expert lane: experts el + 32*j
 
   float acc[TPT][EPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0f;
+    for (int c = 0; c < EPT; ++c) acc[i][c] = 0.0f;
 
+  float xreg[XU][NX];
   float4 wreg[WU];
-  float xreg[XU];
   auto fetch = [&](int k0) {
-    const int kc = min(kKC, d - k0);
-#pragma unroll
-    for (int i = 0; i < WU; ++i) {
-      const int u = tid + i * 256;
-      const int e = u / (kKC / 4);
-      const int j4 = (u % (kKC / 4)) * 4;
-      wreg[i] = (e < E && j4 < kc) ? *reinterpret_cast<const float4*>(wr + (int64_t)e * d + k0 + j4)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
-      const int u = tid + i * 256;
-      const int t = u / kKC, j = u % kKC;
-      xreg[i] = (t0 + t < T && j < kc) ? Elem<TX>::load(x, (int64_t)(t0 + t) * d + k0 + j) : 0.0f;
+      const int u = tid + 256 * i;
+      const int t = u / (KC / NX), j = (u % (KC / NX)) * NX;
+      if (u < XUNITS && k0 + j < d) {
+        XV<TX>::load(x + (int64_t)min(t0 + t, T - 1) * d + k0 + j, xreg[i]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NX; ++c) xreg[i][c] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      const int v = tid + 256 * i;
+      const int e = v / (KC / 4), j4 = (v % (KC / 4)) * 4;
+      wreg[i] = (e < E && k0 + j4 < d) ? *reinterpret_cast<const float4*>(wr + (int64_t)e * d + k0 + j4)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto stash = [&](float* st) {
     float* Ws = st;
-    float* Xs = st + kKC * Ep;
+    float* Xs = st + KC * EP;
 #pragma unroll
-    for (int i = 0; i < WU; ++i) {
-      const int u = tid + i * 256;
-      const int e = u / (kKC / 4);
-      const int j4 = (u % (kKC / 4)) * 4;
-      if (e < E) {
-        Ws[(j4 + 0) * Ep + e] = wreg[i].x;
-        Ws[(j4 + 1) * Ep + e] = wreg[i].y;
-        Ws[(j4 + 2) * Ep + e] = wreg[i].z;
-        Ws[(j4 + 3) * Ep + e] = wreg[i].w;
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + 256 * i;
+      const int t = u / (KC / NX), j = (u % (KC / NX)) * NX;
+      if (u < XUNITS) {
+#pragma unroll
+        for (int c = 0; c < NX; ++c) Xs[(j + c) * XP + t] = xreg[i][c];
       }
     }
 #pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int u = tid + i * 256;
-      Xs[(u % kKC) * XP + u / kKC] = xreg[i];
+    for (int i = 0; i < WU; ++i) {
+      const int v = tid + 256 * i;
+      const int e = v / (KC / 4), j4 = (v % (KC / 4)) * 4;
+      Ws[(j4 + 0) * EP + e] = wreg[i].x;
+      Ws[(j4 + 1) * EP + e] = wreg[i].y;
+      Ws[(j4 + 2) * EP + e] = wreg[i].z;
+      Ws[(j4 + 3) * EP + e] = wreg[i].w;
     }
   };
 
-  const int nch = (d + kKC - 1) / kKC;
+  const int nch = (d + KC - 1) / KC;
   fetch(0);
   stash(smem);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    float* st = smem + (c & 1) * stage_floats;
-    if (c + 1 < nch) fetch((c + 1) * kKC);  // in flight during this chunk's FMAs
-    const float* Ws = st;
-    const float* Xs = st + kKC * Ep;
-    const int kc = min(kKC, d - c * kKC);
+  for (int ch = 0; ch < nch; ++ch) {
+    const float* Ws = smem + (ch & 1) * STAGE;
+    const float* Xs = Ws + KC * EP;
+    if (ch + 1 < nch) fetch((ch + 1) * KC);  // in flight during this chunk's multiply-adds
+    const int kc = min(KC, d - ch * KC);
     for (int j = 0; j < kc; ++j) {
-      float xs[TPT];
+      float xs[TPT], ws[EPT];
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) xs[i] = Xs[j * XP + tg * TPT + i];
-#pragma unroll
-      for (int jj = 0; jj < EPT; ++jj) {
-        const int e = el + 32 * jj;
-        const float w = (e < E) ? Ws[j * Ep + e] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) acc[i][jj] = __builtin_fmaf(xs[i], w, acc[i][jj]);
+      for (int i = 0; i < TPT / 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(Xs + j * XP + tg * TPT + 4 * i);
+        xs[4 * i] = v.x; xs[4 * i + 1] = v.y; xs[4 * i + 2] = v.z; xs[4 * i + 3] = v.w;
       }
+#pragma unroll
+      for (int h = 0; h < NE4; ++h) {
+        const float4 v = *reinterpret_cast<const float4*>(Ws + j * EP + 4 * (eg + EG * h));
+        ws[4 * h] = v.x; ws[4 * h + 1] = v.y; ws[4 * h + 2] = v.z; ws[4 * h + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) acc[i][c] = __builtin_fmaf(xs[i], ws[c], acc[i][c]);
     }
-    if (c + 1 < nch) stash(smem + ((c + 1) & 1) * stage_floats);
+    if (ch + 1 < nch) stash(smem + ((ch + 1) & 1) * STAGE);
     __syncthreads();
   }
-  float* Ls = smem;  // TT * Ep
-#pragma unroll
-  for (int jj = 0; jj < EPT; ++jj) {
-    const int e = el + 32 * jj;
-    if (e < E) {
-      const float off = offset ? offset[e] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) Ls[(tg * TPT + i) * Ep + e] = offset ? acc[i][jj] + off : acc[i][jj];
-    }
-  }
-  __syncthreads();
 
-  // gate + top-k: one wave per token
+  // logits (+ offset, one fp32 add) to LDS, then the gate, one wave per token
+  float* Ls = smem;  // [TT][E + 1]
+  const int LP = E + 1;
+#pragma unroll
+  for (int h = 0; h < NE4; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * (eg + EG * h) + c;
+      if (e < E) {
+        const float off = offset ? offset[e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const float v = acc[i][4 * h + c];
+          Ls[(tg * TPT + i) * LP + e] = offset ? v + off : v;
+        }
+      }
+    }
+  __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  constexpr int Q = (EPT * 32 + 63) / 64;  // experts per lane: e = lane + 64*q
+  constexpr int QE = EMAX / 64;
   for (int t = wave; t < TT; t += 4) {
     const int tt = t0 + t;
     if (tt >= T) break;
-    float p[Q], key[Q];
-    if (gate == MOE_GATE_SOFTMAX) {
-      float m = -__builtin_inff();
+    float h[QE];
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        key[q] = (e < E) ? Ls[t * Ep + e] : -__builtin_inff();
-        m = fmaxf(m, key[q]);
-      }
-      m = wave_max(m);
-      float s = 0.0f;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        p[q] = (e < E) ? expf(key[q] - m) : 0.0f;
-        s += p[q];
-      }
-      s = wave_sum(s);
-      const float inv = 1.0f / s;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) p[q] *= inv;
-    } else {
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        if (e < E) {
-          p[q] = sigmoid_c(Ls[t * Ep + e]);
-          key[q] = sel_bias ? p[q] + sel_bias[e] : p[q];
-        } else {
-          p[q] = 0.0f;
-          key[q] = -__builtin_inff();
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
+    for (int q = 0; q < QE; ++q) {
       const int e = lane + 64 * q;
-      if (e < E) probs[(int64_t)tt * E + e] = p[q];
+      h[q] = (e < E) ? Ls[t * LP + e] : 0.0f;
     }
-    // top-k: k rounds of a wave argmax on (key desc, index asc)
-    uint32_t taken = 0;
-    int my_idx = 0;
-    float my_p = 0.0f, psum = 0.0f;
-    for (int r = 0; r < k; ++r) {
-      float bk = -__builtin_inff();
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        if (e < E && !(taken & (1u << q)) && (key[q] > bk || be == 0x7fffffff)) {
-          bk = key[q];
-          be = e;
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ok = __shfl_xor(bk, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ok > bk || (ok == bk && oe < be)) {
-          bk = ok;
-          be = oe;
-        }
-      }
-      // be is now wave-uniform
-      const int qw = be >> 6;
-      float pv = 0.0f;
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (q == qw) pv = p[q];
-      pv = __shfl(pv, be & 63, kWave);
-      if ((be & 63) == lane) taken |= 1u << qw;
-      if (lane == r) {
-        my_idx = be;
-        my_p = pv;
-      }
-      psum += pv;
-    }
-    if (lane < k) {
-      topk_idx[(int64_t)tt * k + lane] = my_idx;
-      topk_w[(int64_t)tt * k + lane] = renorm ? my_p / psum : my_p;
-    }
+    gate_topk<QE>(h, sel_bias, lane, E, k, gate, renorm, tt, probs, topk_idx, topk_w);
   }
 }
 
-template <typename TX, int EPT, int TT>
-hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
-  const int Ep = a.E + 1;
-  const size_t lds = 2 * (size_t)(kKC * Ep + kKC * (TT + 4)) * sizeof(float);
-  const int blocks = (a.T + TT - 1) / TT;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void*)router_fwd_kernel<TX, EPT, TT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((router_fwd_kernel<TX, EPT, TT>), dim3(blocks), dim3(256), lds, st, (const TX*)a.x,
-                     a.w_router, a.logit_offset, a.sel_bias, a.probs, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k,
-                     a.gate, a.renorm);
+template <typename TX, int TPT, int NE4>
+hipError_t launch_router_tile(const RouterArgs& a, hipStream_t st) {
+  constexpr int EG = 32;
+  constexpr int TT = (256 / EG) * TPT;
+  constexpr int KC = 32;
+  const size_t stage = (size_t)KC * ((4 * EG * NE4 + 4) + (TT + 4));
+  const size_t logits = (size_t)TT * (a.E + 1);
+  const size_t lds = (2 * stage > logits ? 2 * stage : logits) * sizeof(float);
+  const hipError_t e = hipFuncSetAttribute((const void*)router_tile_kernel<TX, TPT, NE4, EG>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((router_tile_kernel<TX, TPT, NE4, EG>), dim3((a.T + TT - 1) / TT), dim3(256), lds, st,
+                     (const TX*)a.x, a.w_router, a.logit_offset, a.sel_bias, a.probs, a.topk_idx, a.topk_w, a.T,
+                     a.d, a.E, a.k, a.gate, a.renorm);
   return hipGetLastError();
 }
 
-// 32 tokens per workgroup when that still gives at least two workgroups per CU
-// of a 256-CU part, else 16 (more workgroups in flight for smaller batches).
-template <typename TX, int EPT>
-hipError_t launch_router_tt(const RouterArgs& a, hipStream_t st) {
-  if ((a.T + 31) / 32 >= 512) return launch_router_t<TX, EPT, 32>(a, st);
-  return launch_router_t<TX, EPT, 16>(a, st);
-}
-
 template <typename TX>
-hipError_t launch_router_e(const RouterArgs& a, hipStream_t st) {
-  const int ept = (a.E + 31) / 32;
-  if (ept <= 1) return launch_router_tt<TX, 1>(a, st);
-  if (ept <= 2) return launch_router_tt<TX, 2>(a, st);
-  if (ept <= 4) return launch_router_tt<TX, 4>(a, st);
-  if (ept <= 8) return launch_router_tt<TX, 8>(a, st);
-  return launch_router_tt<TX, 16>(a, st);
+hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
+  const int64_t total = (int64_t)((a.T + 63) / 64) * ((a.E + kEW * kWaves - 1) / (kEW * kWaves));
+  const dim3 g1((unsigned)((total + 7) / 8 * 8));
+  hipLaunchKernelGGL(router_logits_kernel<TX>, g1, dim3(256), 0, st, (const TX*)a.x, a.w_router, a.probs, a.T,
+                     a.d, a.E);
+  const int qe = (a.E + 63) / 64;
+  const dim3 g2((a.T + 3) / 4);
+#define MOE_GATE_LAUNCH(Q)                                                                                   \
+  hipLaunchKernelGGL(router_gate_kernel<Q>, g2, dim3(256), 0, st, a.logit_offset, a.sel_bias, a.probs,      \
+                     a.topk_idx, a.topk_w, a.T, a.E, a.k, a.gate, a.renorm)
+  if (qe <= 1) MOE_GATE_LAUNCH(1);
+  else if (qe <= 2) MOE_GATE_LAUNCH(2);
+  else if (qe <= 4) MOE_GATE_LAUNCH(4);
+  else MOE_GATE_LAUNCH(8);
+#undef MOE_GATE_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Narrow d_model: the scalar-operand logits kernel (more waves in flight; x
+// rows are short). Wide d_model: the register-tiled kernel, which streams x
+// once per 32 or 64 tokens and reuses each LDS read over 4-8 tokens.
+template <typename TX>
+hipError_t launch_router_wide(const RouterArgs& a, hipStream_t st) {
+  const bool big = (a.T + 63) / 64 >= 256;  // 64-token tiles still cover every CU
+  if (a.E <= 128) return big ? launch_router_tile<TX, 8, 1>(a, st) : launch_router_tile<TX, 4, 1>(a, st);
+  if (a.E <= 256) return big ? launch_router_tile<TX, 8, 2>(a, st) : launch_router_tile<TX, 4, 2>(a, st);
+  return launch_router_tile<TX, 4, 4>(a, st);
+}
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
-  if (a.dtype == MOE_DT_BF16) return launch_router_e<uint16_t>(a, st);
-  return launch_router_e<float>(a, st);
+  if (a.d <= 1024) {
+    if (a.dtype == MOE_DT_BF16) return launch_router_t<uint16_t>(a, st);
+    return launch_router_t<float>(a, st);
+  }
+  if (a.dtype == MOE_DT_BF16) return launch_router_wide<uint16_t>(a, st);
+  return launch_router_wide<float>(a, st);
 }
 
 }  // namespace moe

@@ -174,6 +174,40 @@ def test_sigmoid_contract_bitwise():
     np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+# Router shapes that reach every launch path of moe_route: narrow d_model
+# (scalar-operand kernel; expert counts not a multiple of 4, partial 64-token
+# tiles) and wide d_model (register-tiled kernel with 128, 256 and 512-expert
+# tiles, a ragged last d chunk, bf16 and fp32 activations, sigmoid and softmax).
+ROUTER_SHAPES = [
+    dict(T=130, d=136, E=6, k=2, gate="sigmoid_bias", renorm=True, dtype="f32", sel_bias="uniform"),
+    dict(T=333, d=1024, E=64, k=2, gate="softmax", renorm=True, dtype="bf16", logit_offset="normal"),
+    dict(T=300, d=1032, E=200, k=3, gate="softmax", renorm=True, dtype="bf16", logit_offset="normal"),
+    dict(T=200, d=2056, E=130, k=1, gate="softmax", renorm=False, dtype="f32"),
+    dict(T=97, d=1104, E=100, k=8, gate="sigmoid_bias", renorm=True, dtype="bf16", sel_bias="uniform"),
+    dict(T=100, d=1096, E=400, k=2, gate="sigmoid_bias", renorm=False, dtype="bf16", sel_bias="uniform"),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(ROUTER_SHAPES)))
+def test_router_shapes(shape):
+    kw = dict(ROUTER_SHAPES[shape])
+    print(f"\n[router] {kw}", flush=True)
+    c = LayerConfig("router", f=8, cf=0.0, **kw)
+    inp = make_inputs(c, seed=11 + shape)
+    dev = to_dev(inp)
+    cfg = cfg_of(c)
+    probs = torch.empty(c.T, c.E, device="cuda")
+    idx = torch.empty(c.T, c.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(c.T, c.k, device="cuda")
+    M.moe_route(cfg, dev["x"], dev["w_router"], dev.get("logit_offset"), dev.get("sel_bias"), probs, idx, w)
+    torch.cuda.synchronize()
+    r = O.route(O.Spec.of(c), host64(inp["x"]), host64(inp["w_router"]), host64(inp.get("logit_offset")),
+                host64(inp.get("sel_bias")))
+    np.testing.assert_array_equal(idx.cpu().numpy(), r["idx"])
+    assert relerr(host64(probs), r["probs"]) <= TOL_F32
+    assert relerr(host64(w), r["w"]) <= TOL_F32
+
+
 def test_routing_ties_lowest_index():
     # duplicated router rows give exactly equal logits; the lower expert index wins
     c = LayerConfig("ties", T=512, d=64, f=64, E=16, k=4, renorm=True, dtype="bf16", cf=0.0)
