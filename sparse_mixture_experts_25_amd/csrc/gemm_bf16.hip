@@ -219,14 +219,20 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     g = ti.g; r0 = ti.r0; rows = ti.rows; mrow0 = ti.m0;
   } else {
     // groups in the given order (largest first), tiles of one group
-    // consecutive with the row block fastest
+    // consecutive. 128x128 tiles (short, weight-streaming contractions) are
+    // placed on the XCDs by k_tile; 256x256 tiles (compute-bound) keep the row
+    // block fastest.
     const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
-    const int64_t per_g = (int64_t)nM * nN;
+    const int64_t per_g = (BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN;
     const int rank = (int)(blockIdx.x / per_g);
-    const int t = (int)(blockIdx.x % per_g);
+    if (BM < 256) {
+      if (!k_tile(blockIdx.x % per_g, nM, nN, mb, nb)) return;
+    } else {
+      const int t = (int)(blockIdx.x % per_g);
+      mb = t % nM;
+      nb = t / nM;
+    }
     g = a.order ? a.order[rank] : rank;
-    mb = t % nM;
-    nb = t / nM;
     if (g < a.E) {
       r0 = a.offsets[g];
       rows = a.offsets[g + 1] - a.offsets[g];
@@ -505,7 +511,8 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     n = raster_grid(row_tile_bound(a, BM), (ncols + bn - 1) / bn);
   } else {
     const int ng = a.E + (a.has_shared ? 1 : 0);
-    n = (int64_t)ng * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
+    n = (int64_t)ng * ((BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN);
   }
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI>), dim3((unsigned)n), dim3(kThreads), 0,
@@ -576,8 +583,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
-  return big ? launch_tiles<256, 256, 32, 4>(a, st)
-             : launch_tiles<128, 128, 32, 3>(a, st);
+  if (big) return launch_tiles<256, 256, 32, 4>(a, st);
+  // short contractions (one or two K steps per tile): two stages suffice
+  if (a.kind == 1) return launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
+  return launch_tiles<128, 128, 32, 3>(a, st);
 }
 
 }  // namespace moe

@@ -126,6 +126,29 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
   return true;
 }
 
+// Ragged-K tile placement. Workgroups of one group are consecutive and the
+// per-group count is a multiple of 8, so workgroup t of a group runs on XCD
+// t % 8. The group's tiles are numbered with the block index of the larger
+// output dimension slowest, and XCD x takes the x-th eighth of that range
+// (balanced to one tile): each block of the larger dimension, whose operand
+// panel is the larger one, is read into at most two XCDs' L2s.
+__host__ __device__ inline int64_t ragged_k_per_group(int nM, int nN) {
+  return (((int64_t)nM * nN + 7) / 8) * 8;
+}
+__device__ inline bool k_tile(int64_t t, int nM, int nN, int& mb, int& nb) {
+  const int64_t per = ((int64_t)nM * nN + 7) / 8;
+  const int64_t L = (t % 8) * per + t / 8;
+  if (L >= (int64_t)nM * nN) return false;
+  if (nM <= nN) {
+    nb = (int)(L / nM);
+    mb = (int)(L % nM);
+  } else {
+    mb = (int)(L / nN);
+    nb = (int)(L % nN);
+  }
+  return true;
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 // Epilogue for 8 consecutive output columns of one row (bf16 outputs), or
