@@ -91,13 +91,20 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // wait until at most `steps` later pipeline steps (L loads each) are in flight
-template <int L>
-__device__ __forceinline__ void wait_steps(int steps) {
-  if (steps <= 0) wait_vm<0>();
-  else if (steps == 1) wait_vm<L>();
-  else if (steps == 2) wait_vm<2 * L>();
-  else if (steps == 3) wait_vm<3 * L>();
-  else wait_vm<4 * L>();
+// Wait until at most steps * L + X vector-memory instructions of this wave
+// are outstanding (X: younger non-step loads, 0 or NT).
+template <int L, int X>
+__device__ __forceinline__ void wait_steps_x(int steps) {
+  if (steps <= 0) wait_vm<X>();
+  else if (steps == 1) wait_vm<L + X>();
+  else if (steps == 2) wait_vm<2 * L + X>();
+  else if (steps == 3) wait_vm<3 * L + X>();
+  else wait_vm<4 * L + X>();
+}
+template <int L, int NT>
+__device__ __forceinline__ void wait_steps(int steps, bool tail_younger) {
+  if (tail_younger) wait_steps_x<L, NT>(steps);
+  else wait_steps_x<L, 0>(steps);
 }
 
 // Per-lane byte offsets of the direct loads of one tile, computed once per
@@ -136,25 +143,6 @@ struct DmaPlan {
     for (int q = 0; q < Q; ++q) dma16s(voff[q], base, lds_tile + (wave * Q + q) * 1024);
   }
 };
-
-// Zero-filled register path for a partial K step (k >= kvalid reads as zero).
-template <int R, int BK, typename RowPtr>
-__device__ __forceinline__ void tail_kc(uint16_t* tile, RowPtr rowptr, int rvalid, int kvalid) {
-  constexpr int CPR = BK / 8;
-  for (int u = threadIdx.x; u < R * CPR; u += kThreads) {
-    const int r = u / CPR, c = u % CPR;
-    const u128 v = (r < rvalid && 8 * c < kvalid) ? ld128(rowptr(r) + 8 * c) : zero128();
-    st128(tile + kc_off<BK>(r, c), v);
-  }
-}
-template <int R, int BK, typename KPtr>
-__device__ __forceinline__ void tail_mn(uint16_t* tile, KPtr kptr, int cvalid, int kvalid) {
-  for (int u = threadIdx.x; u < BK * (R / 8); u += kThreads) {
-    const int kr = u / (R / 8), c = u % (R / 8);
-    const u128 v = (kr < kvalid && c < cvalid) ? ld128(kptr(kr) + 8 * c) : zero128();
-    st128(tile + mn_off<R>(kr, c), v);
-  }
-}
 
 // ------------------------------------------------------------ fragments
 // A/B fragment of v_mfma_f32_32x32x16_bf16: lane l holds 8 consecutive k
@@ -306,14 +294,66 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     pa.issue(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
     pb.issue(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
-  auto tail_step = [&](int stage, int k0) {
+  // A partial last K step (k >= K reads as zero) goes through registers. For
+  // the weight gradients (a partial step in almost every group) its loads are
+  // issued in the prologue, right after the first direct loads, and written to
+  // LDS when the step is published; elsewhere (only ragged test shapes have a
+  // partial step) they are issued then, keeping registers free for occupancy.
+  // Every lane issues exactly UA + UB loads (clamped, in-bounds addresses; the
+  // value is masked afterwards), so the per-wave vmcnt accounting of the
+  // direct loads stays exact.
+  constexpr bool kPrefetchTail = (KIND == 1);
+  constexpr int UA = BM * BK / 8 / kThreads, UB = BN * BK / 8 / kThreads;
+  constexpr int NT = UA + UB;
+  u128 tra[UA], trb[UB];
+  auto tail_load = [&](int k0) {
+    const int kv = K - k0;
+#pragma unroll
+    for (int i = 0; i < UA; ++i) {
+      const int u = tid + i * kThreads;
+      if (A_KC) {
+        const int r = u / (BK / 8), c = u % (BK / 8);
+        const bool ok = 8 * c < kv;
+        const u128 v = ld128(a_row(r, k0) + 8 * (ok ? c : 0));
+        tra[i] = ok ? v : zero128();
+      } else {
+        const int kr = u / (BM / 8), c = u % (BM / 8);
+        const bool ok = kr < kv && c < a_valid;
+        const u128 v = ld128(Aorig + (int64_t)(k0 + (kr < kv ? kr : kv - 1)) * a.lda + 8 * (c < a_valid ? c : a_valid - 1));
+        tra[i] = ok ? v : zero128();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      const int u = tid + i * kThreads;
+      if (B_IS_KC) {
+        const int r = u / (BK / 8), c = u % (BK / 8);
+        const bool ok = 8 * c < kv;
+        const u128 v = ld128(b_row(r, k0) + 8 * (ok ? c : 0));
+        trb[i] = ok ? v : zero128();
+      } else {
+        const int kr = u / (BN / 8), c = u % (BN / 8);
+        const bool ok = kr < kv && c < b_valid;
+        const u128 v = ld128(Borig + (int64_t)(k0 + (kr < kv ? kr : kv - 1)) * a.ldb + 8 * (c < b_valid ? c : b_valid - 1));
+        trb[i] = ok ? v : zero128();
+      }
+    }
+  };
+  auto tail_store = [&](int stage) {
     uint16_t* ta = stages + stage * kStage;
     uint16_t* tb = ta + BM * kBK;
-    const int kv = K - k0;
-    if (A_KC) tail_kc<BM, BK>(ta, [&](int r) { return a_row(r, k0); }, BM, kv);
-    else tail_mn<BM, BK>(ta, [&](int kr) { return Aorig + (int64_t)(k0 + kr) * a.lda; }, a_valid, kv);
-    if (B_IS_KC) tail_kc<BN, BK>(tb, [&](int r) { return b_row(r, k0); }, BN, kv);
-    else tail_mn<BN, BK>(tb, [&](int kr) { return Borig + (int64_t)(k0 + kr) * a.ldb; }, b_valid, kv);
+#pragma unroll
+    for (int i = 0; i < UA; ++i) {
+      const int u = tid + i * kThreads;
+      if (A_KC) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), tra[i]);
+      else st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), tra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      const int u = tid + i * kThreads;
+      if (B_IS_KC) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), trb[i]);
+      else st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), trb[i]);
+    }
   };
 
   floatx16 acc[FM][FN];
@@ -367,14 +407,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
   // Direct loads issued before publish(k): steps 0 .. min(NS-1, nfull-1) for
   // k = 0 (prologue); steps 0 .. min(k+NS-2, nfull-1) for k >= 1. The wait lets
   // the later ones stay in flight.
+  // The tail loads (if any) follow the prologue's direct loads, so they are
+  // younger than steps 0 .. NS-1 and older than every later step.
+  const bool has_tail = nk > nfull;
   auto publish = [&](int k) {
-    if (k < nfull) wait_steps<L>(k == 0 ? min(NS - 1, nfull - 1) : min(NS - 2, nfull - 1 - k));
-    else tail_step(k % NS, k * kBK);
+    if (k < nfull) {
+      wait_steps<L, NT>(k == 0 ? min(NS - 1, nfull - 1) : min(NS - 2, nfull - 1 - k),
+                        kPrefetchTail && has_tail && k < NS);
+    } else {
+      if (!kPrefetchTail) tail_load(k * kBK);
+      tail_store(k % NS);
+    }
     __syncthreads();
   };
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nfull) dma_step(s, s * kBK);
+  if (kPrefetchTail && has_tail) tail_load(nfull * kBK);
   // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
   auto inner = [&](int stage) {
 #pragma unroll
