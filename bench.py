@@ -140,7 +140,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="switch_base")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
