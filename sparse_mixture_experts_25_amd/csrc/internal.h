@@ -131,6 +131,10 @@ struct RouterGradArgs {
 };
 int router_grad_splits(int T, int E, int d);
 hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st);
+// matrix-core router gradients for bf16 activations (split-fp32 operands)
+hipError_t launch_router_dw_mfma(const float* g, const uint16_t* x, int T, int E, int d, int chunk, int nsplit,
+                                 float* part, hipStream_t st);
+hipError_t launch_router_dx_mfma(const float* g, const float* w, int T, int E, int d, float* dxr, hipStream_t st);
 
 struct UnpermuteArgs {
   const void* dy;

@@ -370,14 +370,19 @@ hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
   const int chunk = router_grad_chunk(a.T, a.E, a.d);
   const int ns = router_grad_splits(a.T, a.E, a.d);
   const int tiles = ((a.E + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
-  if (ns == 0) {
-  } else if (a.dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(gemm_tn_split_kernel<uint16_t>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits,
-                       (int64_t)a.E, (const uint16_t*)a.x, (int64_t)a.d, a.E, a.d, a.T, chunk, a.ws_partial);
-  else
+  const int64_t n = (int64_t)a.E * a.d;
+  if (a.dtype == MOE_DT_BF16) {
+    // matrix cores on exactly split fp32 operands
+    hipError_t e = launch_router_dw_mfma(a.dlogits, (const uint16_t*)a.x, a.T, a.E, a.d, chunk, ns, a.ws_partial,
+                                         st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns,
+                       n, a.dw_router);
+    return launch_router_dx_mfma(a.dlogits, a.w_router, a.T, a.E, a.d, a.dx_router, st);
+  }
+  if (ns > 0)
     hipLaunchKernelGGL(gemm_tn_split_kernel<float>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits, (int64_t)a.E,
                        (const float*)a.x, (int64_t)a.d, a.E, a.d, a.T, chunk, a.ws_partial);
-  const int64_t n = (int64_t)a.E * a.d;
   hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns, n,
                      a.dw_router);
   const int tiles2 = ((a.T + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
