@@ -118,7 +118,7 @@ struct DmaPlan {
     for (int q = 0; q < Q; ++q) {
       const int p = (wave * Q + q) * 64 + lane;
       const int kr = p / CPR, pc = p % CPR;
-      const int c = (pc & ~7) | ((pc ^ mn_swz(kr)) & 7);
+      const int c = mn_chunk<R>(kr, pc);  // the swizzle is an involution
       const int cc = c < cvalid ? c : cvalid - 1;
       voff[q] = (uint32_t)(((int64_t)kr * ld + 8 * cc) * 2);
     }

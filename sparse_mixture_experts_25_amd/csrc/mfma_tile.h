@@ -10,17 +10,35 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ LDS layouts
-// offsets in elements
-// K-contiguous rows hold BK/8 chunks; the swizzle permutes chunks within a row
+// Offsets in elements; a chunk is 16 bytes (8 bf16). The XOR swizzles are
+// chosen so that the fragment reads below hit distinct LDS banks whether the
+// LDS serves 8 lanes x 16 bytes or 16 lanes x 16 bytes per cycle (direct
+// loads write whole 1 KB blocks and are conflict-free either way).
+//
+// K-contiguous tile: rows of BK elements. A fragment read touches one chunk
+// of 32 consecutive rows; with 64-byte rows (BK = 32) rows r, r+2, r+4, r+6
+// share a 128-byte bank window and r, r+4, r+8, r+12 a 256-byte one, so the
+// chunk is XORed with ((r >> 1) ^ (r >> 2)) & 3, which differs within both
+// sets. With 128-byte rows (BK = 64) it is XORed with r & 7.
 template <int BK>
-__device__ __forceinline__ int kc_swz(int r) { return r & (BK / 8 - 1); }
-__device__ __forceinline__ int mn_swz(int k) { return k & 7; }
+__device__ __forceinline__ int kc_swz(int r) {
+  return BK == 32 ? (((r >> 1) ^ (r >> 2)) & 3) : (r & (BK / 8 - 1));
+}
 template <int BK>
 __device__ __forceinline__ int kc_off(int r, int c) { return r * BK + ((c ^ kc_swz<BK>(r)) << 3); }
+// MN-contiguous tile: k-rows of R elements. A transpose read touches, per 16
+// lanes, chunk pairs of 4 consecutive k-rows (k & 3 = 0..3), and per 32 lanes
+// 4 consecutive chunks of them. For R >= 128 (16 or more chunks per k-row) the
+// low 4 bits of the chunk index are XORed with 0, 4, 10, 14 for k & 3 = 0..3,
+// which puts those reads on distinct banks in both bank models; for R = 64 the
+// low 3 bits are XORed with k & 7.
 template <int R>
-__device__ __forceinline__ int mn_off(int k, int c) {
-  return k * R + (((c & ~7) | ((c ^ mn_swz(k)) & 7)) << 3);
+__device__ __forceinline__ int mn_chunk(int k, int c) {
+  if (R >= 128) return (c & ~15) | ((c ^ (((k & 1) << 2) | (((k >> 1) & 1) * 10))) & 15);
+  return (c & ~7) | ((c ^ k) & 7);
 }
+template <int R>
+__device__ __forceinline__ int mn_off(int k, int c) { return k * R + (mn_chunk<R>(k, c) << 3); }
 
 // ------------------------------------------------------------ fragments
 // A/B fragment of v_mfma_f32_32x32x16_bf16: lane l holds 8 consecutive k
