@@ -21,6 +21,13 @@ CASES = dict(SMALL)
 CASES["tiny_f32_bwd"] = CONFIGS["tiny_f32"].replace(name="tiny_f32_bwd", k=2, renorm=True, fwd_only=False,
                                                     alpha=0.01, cf=1.25)
 CASES["swiglu_f32_shared"] = SMALL["deepseek_v3"].replace(name="swiglu_f32_shared", dtype="f32", T=130)
+# groups averaging >= 256 rows select the 256x256 tiles; d and f are not multiples of
+# 32 (partial K steps in every matmul, partial column tiles), plus a shared expert
+CASES["big_tiles_swiglu"] = LayerConfig("big_tiles_swiglu", T=2048, d=264, f=392, E=8, k=2, gate="softmax",
+                                        renorm=True, act="swiglu", cf=0.0, alpha=0.01, shared=1,
+                                        logit_offset="normal")
+CASES["big_tiles_relu_drops"] = LayerConfig("big_tiles_relu_drops", T=2048, d=296, f=520, E=4, k=1,
+                                            act="relu", cf=1.1, alpha=0.01, logit_offset="normal")
 
 
 def _forward_both(c, seed=0):
