@@ -40,7 +40,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
 
 // ------------------------------------------------------------ direct loads
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -94,10 +93,10 @@ __device__ __forceinline__ void wait_steps(int steps, bool tail_younger) {
 
 // Per-lane byte offsets of the direct loads of one tile, computed once per
 // workgroup (they depend on the tile, not on the K step).
-template <int R, int BK>
+template <int R, int BK, int NW>
 struct DmaPlan {
   static constexpr int NB = R * BK * 2 / 1024;  // 1 KB blocks in the tile
-  static constexpr int Q = NB / 4;               // blocks per wave
+  static constexpr int Q = NB / NW;              // blocks per wave
   uint32_t voff[Q];
   // K-contiguous: rowidx(r) = source row (clamped / remapped) of tile row r
   template <typename RowIdx>
@@ -130,11 +129,19 @@ struct DmaPlan {
 };
 
 // ------------------------------------------------------------ kernel
-template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM * BN >= 65536 ? 1 : 3), (BM * BN >= 65536 ? 1 : 3)))) void gemm_bf16_kernel(
+// WGN waves along N (2 along M): 4 waves for 128x128 tiles (three workgroups
+// per CU) and for 256x256 tiles with 128x128 per wave (one wave per SIMD), or 8
+// waves for 256x256 tiles with 128x64 per wave (two waves per SIMD, so one
+// wave's matrix work covers the other's waits).
+template <int WGN, int BM, int BN>
+constexpr int waves_per_simd() { return WGN == 4 ? 2 : (BM * BN >= 65536 ? 1 : 3); }
+
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN>
+__global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, BM, BN>(), waves_per_simd<WGN, BM, BN>()))) void gemm_bf16_kernel(
     GemmArgs a) {
   constexpr int kBK = BK;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NW = 2 * WGN, NTH = 64 * NW;  // waves, threads
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_KC = (KIND == 0);
   constexpr int B_IS_KC = (KIND == 0) && B_KC;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
   constexpr int HM = BM / 2;  // the fp32 tile is staged half (one wave row) at a time
   constexpr int kStageBytes = HM * CP * 4;
   constexpr int kLds = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
-  constexpr int L = (BM + BN) * BK * 2 / 1024 / 4;  // direct loads per wave per K step
+  constexpr int L = (BM + BN) * BK * 2 / 1024 / NW;  // direct loads per wave per K step
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
   __shared__ __attribute__((aligned(16))) int info[12];
 
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- locate the tile
   int g, rows, mrow0 = 0, nb, mb = 0;
@@ -233,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     return Borig + src * a.ldb + k0;
   };
 
-  DmaPlan<BM, BK> pa;
-  DmaPlan<BN, BK> pb;
+  DmaPlan<BM, BK, NW> pa;
+  DmaPlan<BN, BK, NW> pb;
   if (A_KC) pa.make_kc(wave, lane, a.lda, [&](int r) { return r < a_valid ? r : a_valid - 1; });
   else pa.make_mn(wave, lane, a.lda, a_valid);
   if (B_IS_KC)
@@ -262,14 +269,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
   // value is masked afterwards), so the per-wave vmcnt accounting of the
   // direct loads stays exact.
   constexpr bool kPrefetchTail = (KIND == 1);
-  constexpr int UA = BM * BK / 8 / kThreads, UB = BN * BK / 8 / kThreads;
+  constexpr int UA = BM * BK / 8 / NTH, UB = BN * BK / 8 / NTH;
   constexpr int NT = UA + UB;
   u128 tra[UA], trb[UB];
   auto tail_load = [&](int k0) {
     const int kv = K - k0;
 #pragma unroll
     for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid + i * NTH;
       if (A_KC) {
         const int r = u / (BK / 8), c = u % (BK / 8);
         const bool ok = 8 * c < kv;
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     }
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid + i * NTH;
       if (B_IS_KC) {
         const int r = u / (BK / 8), c = u % (BK / 8);
         const bool ok = 8 * c < kv;
@@ -303,13 +310,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     uint16_t* tb = ta + BM * kBK;
 #pragma unroll
     for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid + i * NTH;
       if (A_KC) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), tra[i]);
       else st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), tra[i]);
     }
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid + i * NTH;
       if (B_IS_KC) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), trb[i]);
       else st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), trb[i]);
     }
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
     if (EPI == EPI_SWIGLU_FWD) {
       // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns h0 + j
       constexpr int U = HM * (BN / 2) / 8;
-      for (int u = tid; u < U; u += kThreads) {
+      for (int u = tid; u < U; u += NTH) {
         const int ml = u / (BN / 16);
         const int j = (u % (BN / 16)) * 8;
         const int m = mbase + ml;
@@ -460,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
       }
     } else {
       constexpr int U = HM * BN / 8;
-      for (int u = tid; u < U; u += kThreads) {
+      for (int u = tid; u < U; u += NTH) {
         const int ml = u / (BN / 8);
         const int n = (u % (BN / 8)) * 8;
         const int m = mbase + ml;
@@ -510,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu((BM
   }
 }
 
-template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI>
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN = 2>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   int64_t n;
   if (KIND == 0) {
@@ -523,31 +530,31 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     n = (int64_t)ng * ((BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN);
   }
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI>), dim3((unsigned)n), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI, WGN>), dim3((unsigned)n), dim3(128 * WGN), 0,
                      st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, int WGN = 2>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // the direct loads address each operand as base + 32-bit per-lane byte offset
   const int64_t lim = int64_t(1) << 32;
   const int64_t b_rows = a.kind == 0 && a.b_kcontig ? (a.epi == EPI_SWIGLU_FWD ? 2 * (int64_t)a.f : a.N) : BK;
   const int64_t a_rows = a.kind == 0 ? BM : BK;
   if (a_rows * a.lda * 2 >= lim || b_rows * a.ldb * 2 >= lim) return hipErrorInvalidValue;
-  if (a.kind == 1) return launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE>(a, st);
+  if (a.kind == 1) return launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN>(a, st);
   if (a.b_kcontig) {
     switch (a.epi) {
-      case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE>(a, st);
-      case EPI_RELU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_RELU_FWD>(a, st);
-      case EPI_SWIGLU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_SWIGLU_FWD>(a, st);
+      case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE, WGN>(a, st);
+      case EPI_RELU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_RELU_FWD, WGN>(a, st);
+      case EPI_SWIGLU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_SWIGLU_FWD, WGN>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
   switch (a.epi) {
-    case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE>(a, st);
-    case EPI_RELU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_RELU_BWD>(a, st);
-    case EPI_SWIGLU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_SWIGLU_BWD>(a, st);
+    case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE, WGN>(a, st);
+    case EPI_RELU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_RELU_BWD, WGN>(a, st);
+    case EPI_SWIGLU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_SWIGLU_BWD, WGN>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -591,7 +598,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
-  if (big) return launch_tiles<256, 256, 32, 4>(a, st);
+  if (big) return launch_tiles<256, 256, 32, 4, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
   if (a.kind == 1) return launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
   return launch_tiles<128, 128, 32, 3>(a, st);
