@@ -587,18 +587,19 @@ hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, in
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 (each wave 128x128; 32-deep K steps, four stages, one
-// workgroup per CU) when the groups are large enough to fill it on average;
-// otherwise 128x128 (32-deep K steps, three stages, 48 KB of LDS and at most
-// 168 registers per lane, so that three workgroups share a CU and their loads
-// overlap each other's matrix work and epilogues: small expert batches, where
-// the weights stream from HBM and the row tile is mostly padding). A 256x256 tile with 64-deep steps does not fit the register file
-// with the transposed-operand fragment reads (the accumulators spill).
+// Tile choice: 256x256 on eight waves (128x64 each, two waves per SIMD;
+// 32-deep K steps, three stages, one workgroup per CU) when the groups are
+// large enough to fill it on average; otherwise 128x128 on four waves
+// (32-deep K steps, three stages, 48 KB of LDS and at most 168 registers per
+// lane, so that three workgroups share a CU and their loads overlap each
+// other's matrix work and epilogues: small expert batches, where the weights
+// stream from HBM and the row tile is mostly padding). 64-deep K steps do not
+// fit the register file with the transposed-operand fragment reads.
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
-  if (big) return launch_tiles<256, 256, 32, 4, 4>(a, st);
+  if (big) return launch_tiles<256, 256, 32, 3, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
   if (a.kind == 1) return launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
   return launch_tiles<128, 128, 32, 3>(a, st);
