@@ -49,7 +49,7 @@ int64_t max_rows_of(const moe_config* c, int C) {
 
 // Backward workspace layout.
 struct BwdWs {
-  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, total;
+  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, gx, wsp, offs2, total;
 };
 BwdWs bwd_layout(const moe_config* c, int64_t R) {
   const int64_t T = c->num_tokens, d = c->d_model, E = c->num_experts, k = c->top_k;
@@ -68,6 +68,10 @@ BwdWs bwd_layout(const moe_config* c, int64_t R) {
   w.dA_sh = o; o += c->num_shared_experts ? align_up(T * f1 * eb) : 0;
   w.dX_sh = o; o += c->num_shared_experts ? align_up(T * d * eb) : 0;
   w.order = o; o += align_up((E + 1) * 4);
+  const int64_t kp = moe::router_dx_k((int)E);
+  w.gx = o; o += c->dtype == MOE_DT_BF16 ? align_up(T * kp * 2) : 0;
+  w.wsp = o; o += c->dtype == MOE_DT_BF16 ? align_up(kp * d * 2) : 0;
+  w.offs2 = o; o += align_up(2 * 4);
   w.total = o;
   return w;
 }
@@ -367,7 +371,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
     StageTimer pt("bwd_dlogits", s);
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;
   }
-  moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, T, d, E, c->dtype};
+  moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, (uint16_t*)(base + L.gx),
+                         (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs2), T, d, E, c->dtype};
   {
     StageTimer pt("bwd_router_grads", s);
     if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;

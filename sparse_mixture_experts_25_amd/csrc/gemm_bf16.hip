@@ -486,6 +486,10 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         const int64_t row = r0 + mrow0 + m;
         if (EPI == EPI_STORE) {
           st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+        } else if (EPI == EPI_STORE_F32) {
+          float* Cf = reinterpret_cast<float*>(sh ? a.C_sh : a.C) + row * a.ldc + col;
+          reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
         } else if (EPI == EPI_RELU_FWD) {
           float h[8];
 #pragma unroll
@@ -555,6 +559,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
     case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE, WGN>(a, st);
     case EPI_RELU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_RELU_BWD, WGN>(a, st);
     case EPI_SWIGLU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_SWIGLU_BWD, WGN>(a, st);
+    case EPI_STORE_F32: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE_F32, WGN>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

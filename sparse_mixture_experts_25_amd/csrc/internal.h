@@ -46,6 +46,7 @@ enum GemmEpi {
   EPI_SWIGLU_FWD = 2,  // C = [gate | up] pre-activations, C2 = silu(gate) * up
   EPI_RELU_BWD = 3,    // C = acc * (X > 0)
   EPI_SWIGLU_BWD = 4,  // acc = dh; X = saved [gate | up]; C = [d gate | d up]
+  EPI_STORE_F32 = 5,   // C (fp32) = acc (ragged-M, B MN-contiguous)
 };
 
 struct GemmArgs {
@@ -127,14 +128,20 @@ struct RouterGradArgs {
   float* dw_router;      // [E, d]
   float* dx_router;      // [T, d]
   float* ws_partial;     // [nsplit, E, d]
+  uint16_t* gx;          // bf16 [T, router_dx_k(E)] split dlogits (bf16 layers)
+  uint16_t* wsplit;      // bf16 [router_dx_k(E), d] split router weights (bf16 layers)
+  int32_t* offs2;        // [2] row range of the single dx group
   int T, d, E, dtype;
 };
+// contraction length of the split dx_router product: 3E rounded up to 8
+inline int router_dx_k(int E) { return (3 * E + 7) / 8 * 8; }
 int router_grad_splits(int T, int E, int d);
 hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st);
 // matrix-core router gradients for bf16 activations (split-fp32 operands)
 hipError_t launch_router_dw_mfma(const float* g, const uint16_t* x, int T, int E, int d, int chunk, int nsplit,
                                  float* part, hipStream_t st);
 hipError_t launch_router_dx_mfma(const float* g, const float* w, int T, int E, int d, float* dxr, hipStream_t st);
+hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st);
 
 struct UnpermuteArgs {
   const void* dy;

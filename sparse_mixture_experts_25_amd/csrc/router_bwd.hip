@@ -168,7 +168,92 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
   }
 }
 
+// Operands of dx_r as one contraction of length Kp = router_dx_k(E):
+//   gx[t]  = [g_hi | g_hi | g_mid | 0 ...]      (bf16 [T][Kp])
+//   wsp    = [W_hi ; W_mid ; W_hi ; 0 ...]      (bf16 [Kp][d])
+// so gx[t] . wsp[:, j] = hi.hi + hi.mid + mid.hi of g[t] . W[:, j]. One
+// thread per 8 output elements; also writes the single group's row range.
+__global__ __launch_bounds__(256) void router_dx_split_kernel(const float* __restrict__ g, const float* __restrict__ w,
+                                                              int T, int E, int d, int kp, uint16_t* __restrict__ gx,
+                                                              uint16_t* __restrict__ wsp, int32_t* __restrict__ offs2) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t ng = (int64_t)T * (kp / 8);
+  if (u == 0) {
+    offs2[0] = 0;
+    offs2[1] = T;
+  }
+  if (u < ng) {
+    const int t = (int)(u / (kp / 8)), c0 = (int)(u % (kp / 8)) * 8;
+    u128 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t h[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = c0 + 2 * i + q;
+        const int e = c % E, part = c / E;
+        uint16_t v = 0;
+        if (part < 3) {
+          const Split3 sp = split3(g[(int64_t)t * E + e]);
+          v = part == 2 ? sp.m : sp.h;
+        }
+        h[q] = v;
+      }
+      o.w[i] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    }
+    st128(gx + (int64_t)t * kp + c0, o);
+    return;
+  }
+  const int64_t v = u - ng;
+  if (v >= (int64_t)kp * (d / 8)) return;
+  const int r = (int)(v / (d / 8)), j0 = (int)(v % (d / 8)) * 8;
+  const int e = r % E, part = r / E;
+  u128 o = zero128();
+  if (part < 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Split3 a = split3(w[(int64_t)e * d + j0 + 2 * i]), b = split3(w[(int64_t)e * d + j0 + 2 * i + 1]);
+      const uint16_t x0 = part == 1 ? a.m : a.h, x1 = part == 1 ? b.m : b.h;
+      o.w[i] = (uint32_t)x0 | ((uint32_t)x1 << 16);
+    }
+  }
+  st128(wsp + (int64_t)r * d + j0, o);
+}
+
 }  // namespace
+
+// dx_r on the grouped matmul: one ragged-M group of T rows, K = Kp, N = d,
+// B MN-contiguous, fp32 output.
+hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  const int kp = router_dx_k(a.E);
+  const int64_t n = (int64_t)a.T * (kp / 8) + (int64_t)kp * (a.d / 8);
+  hipLaunchKernelGGL(router_dx_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dlogits,
+                     a.w_router, a.T, a.E, a.d, kp, a.gx, a.wsplit, a.offs2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmArgs g{};
+  g.kind = 0;
+  g.epi = EPI_STORE_F32;
+  g.b_kcontig = 0;
+  g.M = a.T;
+  g.N = a.d;
+  g.K = kp;
+  g.offsets = a.offs2;
+  g.E = 1;
+  g.shared_rows = 0;
+  g.has_shared = 0;
+  g.max_rows = a.T;
+  g.order = nullptr;
+  g.A = a.gx;
+  g.lda = kp;
+  g.B = a.wsplit;
+  g.ldb = a.d;
+  g.strideB = 0;
+  g.C = a.dx_router;
+  g.ldc = a.d;
+  return launch_gemm_bf16(g, st);
+}
 
 hipError_t launch_router_dw_mfma(const float* g, const uint16_t* x, int T, int E, int d, int chunk, int nsplit,
                                  float* part, hipStream_t st) {

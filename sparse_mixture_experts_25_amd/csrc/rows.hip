@@ -378,7 +378,7 @@ hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns,
                        n, a.dw_router);
-    return launch_router_dx_mfma(a.dlogits, a.w_router, a.T, a.E, a.d, a.dx_router, st);
+    return launch_router_dx_gemm(a, st);
   }
   if (ns > 0)
     hipLaunchKernelGGL(gemm_tn_split_kernel<float>, dim3(tiles, ns), dim3(256), 0, st, a.dlogits, (int64_t)a.E,
