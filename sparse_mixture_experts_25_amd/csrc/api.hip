@@ -49,7 +49,7 @@ int64_t max_rows_of(const moe_config* c, int C) {
 
 // Backward workspace layout.
 struct BwdWs {
-  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, gx, wsp, offs2, total;
+  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, gx, gw, wsp, offs, total;
 };
 BwdWs bwd_layout(const moe_config* c, int64_t R) {
   const int64_t T = c->num_tokens, d = c->d_model, E = c->num_experts, k = c->top_k;
@@ -64,14 +64,17 @@ BwdWs bwd_layout(const moe_config* c, int64_t R) {
   w.dg = o; o += align_up(T * k * 4);
   w.dl = o; o += align_up(T * E * 4);
   w.dxr = o; o += align_up(T * d * 4);
-  w.part = o; o += align_up(ns * E * d * 4);
+  const int64_t kp = moe::router_dx_k((int)E);
+  const int64_t nsw = moe::router_dw_splits((int)T, (int)E, (int)d);
+  const int64_t part_f = ns * E * d, part_w = c->dtype == MOE_DT_BF16 ? nsw * kp * d : 0;
+  w.part = o; o += align_up((part_f > part_w ? part_f : part_w) * 4);
   w.dA_sh = o; o += c->num_shared_experts ? align_up(T * f1 * eb) : 0;
   w.dX_sh = o; o += c->num_shared_experts ? align_up(T * d * eb) : 0;
   w.order = o; o += align_up((E + 1) * 4);
-  const int64_t kp = moe::router_dx_k((int)E);
   w.gx = o; o += c->dtype == MOE_DT_BF16 ? align_up(T * kp * 2) : 0;
+  w.gw = o; o += c->dtype == MOE_DT_BF16 ? align_up(T * kp * 2) : 0;
   w.wsp = o; o += c->dtype == MOE_DT_BF16 ? align_up(kp * d * 2) : 0;
-  w.offs2 = o; o += align_up(2 * 4);
+  w.offs = o; o += align_up((3 + nsw) * 4);
   w.total = o;
   return w;
 }
@@ -372,7 +375,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;
   }
   moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, (uint16_t*)(base + L.gx),
-                         (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs2), T, d, E, c->dtype};
+                         (uint16_t*)(base + L.gw), (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs), T, d, E,
+                         c->dtype};
   {
     StageTimer pt("bwd_router_grads", s);
     if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;

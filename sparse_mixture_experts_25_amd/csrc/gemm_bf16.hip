@@ -477,6 +477,12 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         if (KIND == 1) {
           const int mm = mb * BM + m, nn = nb * BN + n;
           if (mm >= a.M || nn >= a.N) continue;
+          if (EPI == EPI_STORE_F32) {
+            float* Cf = reinterpret_cast<float*>(a.C) + (int64_t)g * a.strideC + (int64_t)mm * a.ldc + nn;
+            reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
+            reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
+            continue;
+          }
           uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
           st128(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
           continue;
@@ -546,7 +552,9 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   const int64_t b_rows = a.kind == 0 && a.b_kcontig ? (a.epi == EPI_SWIGLU_FWD ? 2 * (int64_t)a.f : a.N) : BK;
   const int64_t a_rows = a.kind == 0 ? BM : BK;
   if (a_rows * a.lda * 2 >= lim || b_rows * a.ldb * 2 >= lim) return hipErrorInvalidValue;
-  if (a.kind == 1) return launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN>(a, st);
+  if (a.kind == 1)
+    return a.epi == EPI_STORE_F32 ? launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE_F32, WGN>(a, st)
+                                  : launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN>(a, st);
   if (a.b_kcontig) {
     switch (a.epi) {
       case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE, WGN>(a, st);
@@ -606,7 +614,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
   if (big) return launch_tiles<256, 256, 32, 3, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
-  if (a.kind == 1) return launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
+  if (a.kind == 1)
+    return a.epi == EPI_STORE_F32 ? launch_t<128, 128, 32, 2, 1, 0, EPI_STORE_F32>(a, st)
+                                  : launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
   return launch_tiles<128, 128, 32, 3>(a, st);
 }
 

@@ -128,19 +128,21 @@ struct RouterGradArgs {
   float* dw_router;      // [E, d]
   float* dx_router;      // [T, d]
   float* ws_partial;     // [nsplit, E, d]
-  uint16_t* gx;          // bf16 [T, router_dx_k(E)] split dlogits (bf16 layers)
+  uint16_t* gx;          // bf16 [T, router_dx_k(E)] split dlogits for dx_router (bf16 layers)
+  uint16_t* gw;          // bf16 [T, router_dx_k(E)] split dlogits for dW_router (bf16 layers)
   uint16_t* wsplit;      // bf16 [router_dx_k(E), d] split router weights (bf16 layers)
-  int32_t* offs2;        // [2] row range of the single dx group
+  int32_t* offs;         // [2 + router_dw_splits + 1] row ranges of the dx group and the dW chunks
   int T, d, E, dtype;
 };
-// contraction length of the split dx_router product: 3E rounded up to 8
+// width of the split operands: 3E rounded up to 8
 inline int router_dx_k(int E) { return (3 * E + 7) / 8 * 8; }
+// token chunks of the matrix-core dW_router (each an fp32 partial of router_dx_k(E) x d)
+int router_dw_splits(int T, int E, int d);
 int router_grad_splits(int T, int E, int d);
 hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st);
-// matrix-core router gradients for bf16 activations (split-fp32 operands)
-hipError_t launch_router_dw_mfma(const float* g, const uint16_t* x, int T, int E, int d, int chunk, int nsplit,
-                                 float* part, hipStream_t st);
-hipError_t launch_router_dx_mfma(const float* g, const float* w, int T, int E, int d, float* dxr, hipStream_t st);
+// matrix-core router gradients for bf16 activations (split-fp32 operands);
+// dw first (it also writes the split operands dx uses)
+hipError_t launch_router_dw_gemm(const RouterGradArgs& a, hipStream_t st);
 hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st);
 
 struct UnpermuteArgs {

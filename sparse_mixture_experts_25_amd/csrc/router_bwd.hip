@@ -9,25 +9,22 @@
 // three bf16 terms, v = hi + mid + lo (hi = bf16(v), mid = bf16(v - hi),
 // lo = bf16(v - hi - mid); each subtraction is exact, and the three terms
 // carry the full 24-bit significand). A bf16 x bf16 product is exact in fp32,
-// so summing the partial products with fp32 accumulation on
-// v_mfma_f32_32x32x16_bf16 gives an fp32-accurate result:
-//   dW_r[e][j] = sum_t (g_hi + g_mid + g_lo)[t][e] * x[t][j]   (x is bf16: 3 products)
+// so the grouped matmul kernel (fp32 accumulation) gives fp32-accurate results:
+//   dW_r[e][j] = sum_t (g_hi + g_mid + g_lo)[t][e] * x[t][j]   (x is bf16: 3 bands)
 //   dx_r[t][j] = sum_e g[t][e] * W[e][j] with the cross terms hi.hi, hi.mid
 //                and mid.hi; the dropped ones (hi.lo, mid.mid, lo.hi and
 //                smaller) are at most about 2^-16 of each product. dx_r only
 //                enters the input gradient, which is rounded to bf16 (2^-9).
-// Tiles are staged through LDS (fp32 loaded, split, written as bf16); the
-// fragment reads are those of the expert matmuls. No atomics: dW_r is summed
-// over fixed token chunks into partial buffers and then in a fixed order.
+// Each product is one contraction over split operands of width 3E (rounded up
+// to 8): dW_r runs on the weight-gradient (ragged-K) path over fixed token
+// chunks with fp32 partials summed in a fixed order; dx_r runs on the
+// ragged-M path as a single group. No atomics.
 #include "internal.h"
 #include "mfma_tile.h"
 
 namespace moe {
 
 namespace {
-
-constexpr int kT = 64;  // workgroup tile (rows and columns)
-constexpr int kK = 32;  // contraction step
 
 struct Split3 {
   uint16_t h, m, l;
@@ -42,196 +39,139 @@ __device__ __forceinline__ Split3 split3(float v) {
   return s;
 }
 
-// Split 8 fp32 values and store the three 16-byte bf16 vectors at offset o of
-// the three part tiles.
-__device__ __forceinline__ void split_store(const float* v, uint16_t* t0, uint16_t* t1, uint16_t* t2, int o) {
-  u128 a, b, c;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const Split3 s0 = split3(v[2 * i]), s1 = split3(v[2 * i + 1]);
-    a.w[i] = (uint32_t)s0.h | ((uint32_t)s1.h << 16);
-    b.w[i] = (uint32_t)s0.m | ((uint32_t)s1.m << 16);
-    c.w[i] = (uint32_t)s0.l | ((uint32_t)s1.l << 16);
-  }
-  st128(t0 + o, a);
-  st128(t1 + o, b);
-  st128(t2 + o, c);
-}
-
-// part[c][e][j] = sum over the tokens of chunk c of g[t][e] * x[t][j].
-// Workgroup: 64 experts x 64 columns; four waves of 32 x 32.
-__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ g, const uint16_t* __restrict__ x,
-                                                        int T, int E, int d, int chunk, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[3][kK * kT];  // [k = t][m = e], per split term
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kK * kT];     // [k = t][n = j]
-  const int nN = (d + kT - 1) / kT;
-  const int mb = blockIdx.x / nN, nb = blockIdx.x % nN;
-  const int t0 = blockIdx.y * chunk, t1 = min(T, t0 + chunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int kr = tid >> 3, c = tid & 7;  // this thread's row and 8-wide chunk of both tiles
-  floatx16 acc = {};
-  // the next step's operands are loaded into registers during this step's
-  // matrix work
-  float v[8];
-  u128 xv;
-  auto load = [&](int k0) {
-    const int t = k0 + kr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = mb * kT + 8 * c + i;
-      v[i] = (t < t1 && e < E) ? g[(int64_t)t * E + e] : 0.0f;
-    }
-    const int j = nb * kT + 8 * c;
-    xv = (t < t1 && j < d) ? ld128(x + (int64_t)t * d + j) : zero128();
-  };
-  if (t0 < t1) load(t0);
-  for (int k0 = t0; k0 < t1; k0 += kK) {
-    __syncthreads();  // the previous step's fragments are read
-    split_store(v, As[0], As[1], As[2], mn_off<kT>(kr, c));
-    st128(Bs + mn_off<kT>(kr, c), xv);
-    __syncthreads();
-    if (k0 + kK < t1) load(k0 + kK);
-#pragma unroll
-    for (int s = 0; s < kK / 16; ++s) {
-      const bf16x8 b = frag_mn<kT>(Bs, wn * 32, s, lane);
-#pragma unroll
-      for (int p = 0; p < 3; ++p)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_mn<kT>(As[p], wm * 32, s, lane), b, acc, 0, 0, 0);
-    }
-  }
-  float* out = part + (int64_t)blockIdx.y * E * d;
-  const int n = nb * kT + wn * 32 + (lane & 31);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int m = mb * kT + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    if (m < E && n < d) out[(int64_t)m * d + n] = acc[e];
-  }
-}
-
-// dxr[t][j] = sum_e g[t][e] * W[e][j]. Workgroup: 64 tokens x 64 columns.
-__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ g, const float* __restrict__ w,
-                                                        int T, int E, int d, float* __restrict__ dxr) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[3][kT * kK];  // [m = t][k = e] (K-contiguous)
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][kK * kT];  // [k = e][n = j] (lo terms unused)
-  const int nN = (d + kT - 1) / kT;
-  const int mb = blockIdx.x / nN, nb = blockIdx.x % nN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ar = tid >> 2, ac = tid & 3;  // A: row (token) and 8-wide e chunk
-  const int br = tid >> 3, bc = tid & 7;  // B: row (expert) and 8-wide column chunk
-  floatx16 acc = {};
-  float va[8], vb[8];
-  auto load = [&](int k0) {
-    const int t = mb * kT + ar;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = k0 + 8 * ac + i;
-      va[i] = (t < T && e < E) ? g[(int64_t)t * E + e] : 0.0f;
-    }
-    const int e = k0 + br, j = nb * kT + 8 * bc;
-    if (e < E && j < d) {
-      const float4 p = *reinterpret_cast<const float4*>(w + (int64_t)e * d + j);
-      const float4 q = *reinterpret_cast<const float4*>(w + (int64_t)e * d + j + 4);
-      vb[0] = p.x; vb[1] = p.y; vb[2] = p.z; vb[3] = p.w;
-      vb[4] = q.x; vb[5] = q.y; vb[6] = q.z; vb[7] = q.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vb[i] = 0.0f;
-    }
-  };
-  if (E > 0) load(0);
-  for (int k0 = 0; k0 < E; k0 += kK) {
-    __syncthreads();
-    split_store(va, As[0], As[1], As[2], kc_off<kK>(ar, ac));
-    split_store(vb, Bs[0], Bs[1], Bs[2], mn_off<kT>(br, bc));
-    __syncthreads();
-    if (k0 + kK < E) load(k0 + kK);
-#pragma unroll
-    for (int s = 0; s < kK / 16; ++s) {
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        fa[p] = frag_kc<kK>(As[p], wm * 32, s, lane);
-        fb[p] = frag_mn<kT>(Bs[p], wn * 32, s, lane);
-      }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[0], acc, 0, 0, 0);
-    }
-  }
-  const int n = nb * kT + wn * 32 + (lane & 31);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int m = mb * kT + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    if (m < T && n < d) dxr[(int64_t)m * d + n] = acc[e];
-  }
-}
-
-// Operands of dx_r as one contraction of length Kp = router_dx_k(E):
-//   gx[t]  = [g_hi | g_hi | g_mid | 0 ...]      (bf16 [T][Kp])
-//   wsp    = [W_hi ; W_mid ; W_hi ; 0 ...]      (bf16 [Kp][d])
-// so gx[t] . wsp[:, j] = hi.hi + hi.mid + mid.hi of g[t] . W[:, j]. One
-// thread per 8 output elements; also writes the single group's row range.
-__global__ __launch_bounds__(256) void router_dx_split_kernel(const float* __restrict__ g, const float* __restrict__ w,
-                                                              int T, int E, int d, int kp, uint16_t* __restrict__ gx,
-                                                              uint16_t* __restrict__ wsp, int32_t* __restrict__ offs2) {
+// Split operands, all of width Kp = router_dx_k(E):
+//   gx[t]  = [g_hi | g_hi | g_mid | 0 ...]      dx_r:   gx[t] . wsp[:, j]
+//   wsp    = [W_hi ; W_mid ; W_hi ; 0 ...]              = hi.hi + hi.mid + mid.hi
+//   gw[t]  = [g_hi | g_mid | g_lo | 0 ...]      dW_r:   sum_t gw[t][p E + e] x[t][j],
+//                                                       summed over the three bands p
+// One thread per 8 elements. Also writes the row ranges: offs[0..1] = the
+// single dx group, offs[2 + c] = the start of token chunk c of dW_r.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ g, const float* __restrict__ w,
+                                                           int T, int E, int d, int kp, int nsw, int chunk,
+                                                           uint16_t* __restrict__ gx, uint16_t* __restrict__ gw,
+                                                           uint16_t* __restrict__ wsp, int32_t* __restrict__ offs) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t ng = (int64_t)T * (kp / 8);
+  if (u <= nsw) offs[2 + u] = (int)min((int64_t)u * chunk, (int64_t)T);
   if (u == 0) {
-    offs2[0] = 0;
-    offs2[1] = T;
+    offs[0] = 0;
+    offs[1] = T;
   }
   if (u < ng) {
     const int t = (int)(u / (kp / 8)), c0 = (int)(u % (kp / 8)) * 8;
-    u128 o;
+    u128 ox, ow;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t h[2];
+      uint16_t hx[2], hw[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int c = c0 + 2 * i + q;
-        const int e = c % E, part = c / E;
-        uint16_t v = 0;
-        if (part < 3) {
+        const int e = c % E, band = c / E;
+        hx[q] = hw[q] = 0;
+        if (band < 3) {
           const Split3 sp = split3(g[(int64_t)t * E + e]);
-          v = part == 2 ? sp.m : sp.h;
+          hx[q] = band == 2 ? sp.m : sp.h;
+          hw[q] = band == 0 ? sp.h : band == 1 ? sp.m : sp.l;
         }
-        h[q] = v;
       }
-      o.w[i] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      ox.w[i] = (uint32_t)hx[0] | ((uint32_t)hx[1] << 16);
+      ow.w[i] = (uint32_t)hw[0] | ((uint32_t)hw[1] << 16);
     }
-    st128(gx + (int64_t)t * kp + c0, o);
+    st128(gx + (int64_t)t * kp + c0, ox);
+    st128(gw + (int64_t)t * kp + c0, ow);
     return;
   }
   const int64_t v = u - ng;
   if (v >= (int64_t)kp * (d / 8)) return;
   const int r = (int)(v / (d / 8)), j0 = (int)(v % (d / 8)) * 8;
-  const int e = r % E, part = r / E;
+  const int e = r % E, band = r / E;
   u128 o = zero128();
-  if (part < 3) {
+  if (band < 3) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const Split3 a = split3(w[(int64_t)e * d + j0 + 2 * i]), b = split3(w[(int64_t)e * d + j0 + 2 * i + 1]);
-      const uint16_t x0 = part == 1 ? a.m : a.h, x1 = part == 1 ? b.m : b.h;
+      const Split3 p = split3(w[(int64_t)e * d + j0 + 2 * i]), q = split3(w[(int64_t)e * d + j0 + 2 * i + 1]);
+      const uint16_t x0 = band == 1 ? p.m : p.h, x1 = band == 1 ? q.m : q.h;
       o.w[i] = (uint32_t)x0 | ((uint32_t)x1 << 16);
     }
   }
   st128(wsp + (int64_t)r * d + j0, o);
 }
 
+// dW_r[e][j] = sum over chunks c and bands p of part[c][p E + e][j], in that
+// fixed order.
+__global__ __launch_bounds__(256) void router_dw_sum_kernel(const float* __restrict__ part, int nsw, int E, int d,
+                                                            int kp, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)E * d) return;
+  const int64_t e = i / d, j = i % d;
+  float s = 0.0f;
+  for (int c = 0; c < nsw; ++c)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) s += part[((int64_t)c * kp + p * E + e) * d + j];
+  out[i] = s;
+}
+
 }  // namespace
 
+// About 512 workgroups of 256x256 tiles, with the fp32 partials capped at
+// 128 MB and chunks of at least 256 tokens.
+int router_dw_splits(int T, int E, int d) {
+  const int64_t kp = router_dx_k(E);
+  const int64_t tiles = ((kp + 255) / 256) * (((int64_t)d + 255) / 256);
+  int64_t ns = (512 + tiles - 1) / tiles;
+  const int64_t mem = (int64_t(128) << 20) / (kp * (int64_t)d * 4 > 0 ? kp * (int64_t)d * 4 : 1);
+  if (ns > mem) ns = mem;
+  const int64_t by_t = ((int64_t)T + 255) / 256;
+  if (ns > by_t) ns = by_t;
+  return (int)(ns < 1 ? 1 : ns);
+}
+
+// Split operands (both layouts), dW_r on the weight-gradient matmul (one
+// group per token chunk, fp32 partials), then the fixed-order sum.
+hipError_t launch_router_dw_gemm(const RouterGradArgs& a, hipStream_t st) {
+  const int64_t ed = (int64_t)a.E * a.d;
+  if (a.T == 0) {
+    hipLaunchKernelGGL(router_dw_sum_kernel, dim3((unsigned)((ed + 255) / 256)), dim3(256), 0, st, a.ws_partial, 0,
+                       a.E, a.d, router_dx_k(a.E), a.dw_router);
+    return hipGetLastError();
+  }
+  const int kp = router_dx_k(a.E);
+  const int nsw = router_dw_splits(a.T, a.E, a.d);
+  const int chunk = (a.T + nsw - 1) / nsw;
+  const int64_t n = (int64_t)a.T * (kp / 8) + (int64_t)kp * (a.d / 8);
+  const int64_t nthreads = n > nsw + 1 ? n : nsw + 1;
+  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a.dlogits,
+                     a.w_router, a.T, a.E, a.d, kp, nsw, chunk, a.gx, a.gw, a.wsplit, a.offs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmArgs g{};
+  g.kind = 1;
+  g.epi = EPI_STORE_F32;
+  g.M = kp;
+  g.N = a.d;
+  g.offsets = a.offs + 2;
+  g.E = nsw;
+  g.max_rows = a.T;
+  g.order = nullptr;
+  g.A = a.gw;
+  g.lda = kp;
+  g.B = a.x;
+  g.ldb = a.d;
+  g.C = a.ws_partial;
+  g.ldc = a.d;
+  g.strideC = (int64_t)kp * a.d;
+  if ((e = launch_gemm_bf16(g, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(router_dw_sum_kernel, dim3((unsigned)((ed + 255) / 256)), dim3(256), 0, st, a.ws_partial, nsw,
+                     a.E, a.d, kp, a.dw_router);
+  return hipGetLastError();
+}
+
 // dx_r on the grouped matmul: one ragged-M group of T rows, K = Kp, N = d,
-// B MN-contiguous, fp32 output.
+// B MN-contiguous, fp32 output. Needs the split operands of
+// launch_router_dw_gemm (same stream, launched before).
 hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int kp = router_dx_k(a.E);
-  const int64_t n = (int64_t)a.T * (kp / 8) + (int64_t)kp * (a.d / 8);
-  hipLaunchKernelGGL(router_dx_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dlogits,
-                     a.w_router, a.T, a.E, a.d, kp, a.gx, a.wsplit, a.offs2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   GemmArgs g{};
   g.kind = 0;
   g.epi = EPI_STORE_F32;
@@ -239,35 +179,17 @@ hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st) {
   g.M = a.T;
   g.N = a.d;
   g.K = kp;
-  g.offsets = a.offs2;
+  g.offsets = a.offs;
   g.E = 1;
-  g.shared_rows = 0;
-  g.has_shared = 0;
   g.max_rows = a.T;
   g.order = nullptr;
   g.A = a.gx;
   g.lda = kp;
   g.B = a.wsplit;
   g.ldb = a.d;
-  g.strideB = 0;
   g.C = a.dx_router;
   g.ldc = a.d;
   return launch_gemm_bf16(g, st);
-}
-
-hipError_t launch_router_dw_mfma(const float* g, const uint16_t* x, int T, int E, int d, int chunk, int nsplit,
-                                 float* part, hipStream_t st) {
-  const int tiles = ((E + kT - 1) / kT) * ((d + kT - 1) / kT);
-  if (tiles == 0 || nsplit == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_dw_kernel, dim3(tiles, nsplit), dim3(256), 0, st, g, x, T, E, d, chunk, part);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_dx_mfma(const float* g, const float* w, int T, int E, int d, float* dxr, hipStream_t st) {
-  const int tiles = ((T + kT - 1) / kT) * ((d + kT - 1) / kT);
-  if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_dx_kernel, dim3(tiles), dim3(256), 0, st, g, w, T, E, d, dxr);
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -372,12 +372,9 @@ hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
   const int tiles = ((a.E + kRG - 1) / kRG) * ((a.d + kRG - 1) / kRG);
   const int64_t n = (int64_t)a.E * a.d;
   if (a.dtype == MOE_DT_BF16) {
-    // matrix cores on exactly split fp32 operands
-    hipError_t e = launch_router_dw_mfma(a.dlogits, (const uint16_t*)a.x, a.T, a.E, a.d, chunk, ns, a.ws_partial,
-                                         st);
+    // the grouped matmul on exactly split fp32 operands
+    const hipError_t e = launch_router_dw_gemm(a, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.ws_partial, ns,
-                       n, a.dw_router);
     return launch_router_dx_gemm(a, st);
   }
   if (ns > 0)
