@@ -31,7 +31,7 @@ PEAK_BF16 = 2.5e15         # flop/s, dense bf16 matrix cores
 PEAK_F32_VALU = 78.6e12
 
 # Kernel sources whose hash a measured HBM-traffic figure is tied to.
-GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "internal.h", "common.h", "api.hip")
+GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "mfma_tile.h", "internal.h", "common.h", "api.hip")
 
 
 def sources_sha(names):
