@@ -35,7 +35,9 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.cpp")
 
 MODE_EXACT, MODE_F32, MODE_BF16 = 0, 1, 2
-GATE_SOFTMAX, GATE_SIGMOID_BIAS = 0, 1
+GATE_SOFTMAX, GATE_SIGMOID_BIAS, GATE_SQRT_SOFTPLUS_BIAS = 0, 1, 2
+GATE_OF = {"softmax": GATE_SOFTMAX, "sigmoid_bias": GATE_SIGMOID_BIAS,
+           "sqrt_softplus_bias": GATE_SQRT_SOFTPLUS_BIAS}
 ACT_RELU, ACT_SWIGLU = 0, 1
 
 _lib = None
@@ -64,6 +66,10 @@ def lib():
             "orc_round_bf16": (d, [d]),
             "orc_exp_contract": (ctypes.c_float, [ctypes.c_float]),
             "orc_sigmoid_contract": (ctypes.c_float, [ctypes.c_float]),
+            "orc_log1p_contract": (ctypes.c_float, [ctypes.c_float]),
+            "orc_sqrt_softplus_contract": (ctypes.c_float, [ctypes.c_float]),
+            "orc_gate_deriv": (d, [i, d]),
+            "orc_bias_update": (None, [i, I, d, D, D]),
             "orc_capacity": (i, [i, i, d]),
             "orc_logits": (None, [i, i, i, i, D, D, D, D]),
             "orc_gate": (None, [i, i, i, i, i, i, D, D, D, I, D]),
@@ -124,6 +130,27 @@ def exp_contract(x: float) -> float:
 
 def sigmoid_contract(x: float) -> float:
     return lib().orc_sigmoid_contract(float(x))
+
+
+def log1p_contract(x: float) -> float:
+    return lib().orc_log1p_contract(float(x))
+
+
+def sqrt_softplus_contract(x: float) -> float:
+    return lib().orc_sqrt_softplus_contract(float(x))
+
+
+def gate_deriv(gate: int, s: float) -> float:
+    return lib().orc_gate_deriv(int(gate), float(s))
+
+
+def bias_update(counts, gamma: float, bias):
+    """Aux-loss-free selection-bias step (fp32 values in, fp32 values out as float64)."""
+    c = np.ascontiguousarray(counts, np.int32)
+    b = f64(bias)
+    out = np.empty_like(b)
+    lib().orc_bias_update(int(c.size), _i(c), float(gamma), _d(b), _d(out))
+    return out
 
 
 def capacity(T: int, E: int, cf: float) -> int:
@@ -274,7 +301,7 @@ class Spec:
 
     @staticmethod
     def of(cfg, mode=None):
-        gate = GATE_SIGMOID_BIAS if cfg.gate == "sigmoid_bias" else GATE_SOFTMAX
+        gate = GATE_OF[cfg.gate]
         act = ACT_SWIGLU if cfg.act == "swiglu" else ACT_RELU
         m = mode if mode is not None else (MODE_F32 if cfg.dtype == "f32" else MODE_BF16)
         return Spec(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, gate, bool(cfg.renorm), act, m,

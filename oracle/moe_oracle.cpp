@@ -35,6 +35,9 @@
 // fp32 add. The sigmoid gate is 1/(1 + exp_c(-h)) with fp32 add and division,
 // where exp_c is the fixed-operation exponential below (Cody-Waite range
 // reduction, Cody & Waite 1980, then a degree-7 Taylor polynomial in Horner form).
+// The square-root-softplus gate is sqrt(max(h, 0) + log1p_c(exp_c(-|h|))) with
+// one fp32 add and a correctly rounded fp32 square root, where log1p_c is the
+// fixed-operation log(1 + u) below (the inverse-hyperbolic-tangent series).
 
 #include <algorithm>
 #include <cmath>
@@ -48,7 +51,7 @@
 namespace {
 
 enum { MODE_EXACT = 0, MODE_F32 = 1, MODE_BF16 = 2 };
-enum { GATE_SOFTMAX = 0, GATE_SIGMOID_BIAS = 1 };
+enum { GATE_SOFTMAX = 0, GATE_SIGMOID_BIAS = 1, GATE_SQRT_SOFTPLUS_BIAS = 2 };
 enum { ACT_RELU = 0, ACT_SWIGLU = 1 };
 
 // Round a double to the nearest bf16 value (ties to even), by scaling the
@@ -113,6 +116,46 @@ float sigmoid_c(float h) {
   return 1.0f / den;
 }
 
+// log1p_c(u) for u in [0, 1]: log(1 + u) = 2 artanh(z) with z = u / (2 + u), so
+// z lies in [0, 1/3], and artanh(z) = z + z^3/3 + z^5/5 + ... The series is cut
+// after the z^15 term (the first dropped term is below 2e-9 of the sum at
+// z = 1/3) and evaluated as z * P(z^2), P in Horner form with fp32 coefficients
+// 2/(2i + 1). Every operation is one correctly rounded fp32 operation.
+float log1p_c(float u) {
+  const float z = u / (2.0f + u);
+  const float z2 = z * z;
+  float p = 0.133333333333333333f;       // 2/15
+  p = std::fma(p, z2, 0.153846153846153846f);  // 2/13
+  p = std::fma(p, z2, 0.181818181818181818f);  // 2/11
+  p = std::fma(p, z2, 0.222222222222222222f);  // 2/9
+  p = std::fma(p, z2, 0.285714285714285714f);  // 2/7
+  p = std::fma(p, z2, 0.4f);                   // 2/5
+  p = std::fma(p, z2, 0.666666666666666667f);  // 2/3
+  p = std::fma(p, z2, 2.0f);
+  return z * p;
+}
+
+// [WIKI] (cross-cutting finding on the three generations of gating functions):
+// DeepSeek-V4 replaces the sigmoid by the square root of softplus. softplus(h) =
+// log(1 + e^h) is evaluated as max(h, 0) + log(1 + e^-|h|), which never
+// overflows; the square root is the correctly rounded fp32 one.
+float sqrt_softplus_c(float h) {
+  const float u = exp_c(-std::fabs(h));
+  const float sp = (h > 0.0f ? h : 0.0f) + log1p_c(u);
+  return std::sqrt(sp);
+}
+
+// The gate's derivative written with the gate value s = g(h) (the backward
+// only has the saved gate values):
+//   sigmoid:            s (1 - s)
+//   sqrt(softplus):     sigmoid(h) / (2 s) = (1 - exp(-s^2)) / (2 s), since
+//                       exp(-softplus(h)) = 1 - sigmoid(h); 0 at s = 0 (its limit).
+double gate_deriv(int gate, double s) {
+  if (gate == GATE_SIGMOID_BIAS) return s * (1.0 - s);
+  if (s <= 0.0) return 0.0;
+  return -std::expm1(-s * s) / (2.0 * s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +169,9 @@ void orc_round_array(int mode, int64_t n, const double* in, double* out) {
 }
 float orc_exp_contract(float x) { return exp_c(x); }
 float orc_sigmoid_contract(float x) { return sigmoid_c(x); }
+float orc_log1p_contract(float x) { return log1p_c(x); }
+float orc_sqrt_softplus_contract(float x) { return sqrt_softplus_c(x); }
+double orc_gate_deriv(int gate, double s) { return gate_deriv(gate, s); }
 
 // [SW] eq. (3): capacity = tokens per batch / number of experts * capacity
 // factor, rounded up, evaluated in double in exactly this order.
@@ -166,6 +212,9 @@ void orc_logits(int mode, int T, int d, int E, const double* x, const double* Wr
 //    bias and on DeepSeek-V3's bias used only for the routing decision):
 //    probs = s = sigmoid_c(h); key = s + b (one fp32 add); the bias takes no
 //    part in the weights.
+//  square root of softplus + bias ([WIKI], DeepSeek-V4's gate in place of the
+//    sigmoid, the selection bias kept as for the sigmoid):
+//    probs = s = sqrt_softplus_c(h); key = s + b as above.
 // Selection: experts ordered by key descending, equal keys by index ascending;
 // the first k are chosen and idx[t, 0..k-1] lists them in that order.
 // Weights: without renormalisation w_r = p[e_r] ([SW] numpy sketch: gate is
@@ -187,10 +236,13 @@ void orc_gate(int mode, int T, int E, int k, int gate, int renorm, const double*
     } else {
       for (int e = 0; e < E; ++e) {
         if (mode == MODE_EXACT) {
-          pt[e] = 1.0 / (1.0 + std::exp(-ht[e]));
+          const double hv = ht[e];
+          pt[e] = gate == GATE_SIGMOID_BIAS
+                      ? 1.0 / (1.0 + std::exp(-hv))
+                      : std::sqrt(std::max(hv, 0.0) + std::log1p(std::exp(-std::fabs(hv))));
           key[e] = pt[e] + (sel_bias ? sel_bias[e] : 0.0);
         } else {
-          float s = sigmoid_c((float)ht[e]);
+          float s = gate == GATE_SIGMOID_BIAS ? sigmoid_c((float)ht[e]) : sqrt_softplus_c((float)ht[e]);
           pt[e] = s;
           key[e] = sel_bias ? (double)(s + (float)sel_bias[e]) : (double)s;
         }
@@ -399,11 +451,12 @@ void orc_wgrad(int mode, int n, int M, int N, const double* G, const double* V, 
 // gradient through it), with dg[t,r] = dL/dw[t,r]:
 //  softmax, no renorm:  dh_j = sum_r dg_r * p_{e_r} * (delta(j, e_r) - p_j)
 //  softmax, renorm:     dh_{e_r} = w_r * (dg_r - sum_s w_s dg_s), 0 elsewhere
-//  sigmoid, no renorm:  dh_{e_r} = dg_r * s(1 - s)
-//  sigmoid, renorm:     dh_{e_r} = (dg_r - sum_s w_s dg_s) / sum_s s_{e_s} * s(1 - s)
+//  sigmoid-type gates s = g(h) (sigmoid, sqrt-softplus), with g' = gate_deriv(s):
+//   no renorm:          dh_{e_r} = dg_r * g'(s_{e_r})
+//   renorm:             dh_{e_r} = (dg_r - sum_s w_s dg_s) / sum_s s_{e_s} * g'(s_{e_r})
 // Aux path ([SW] eq. (4): f is a constant, only P carries gradient):
 //  dh_j += (alpha * E / T) * sum_i f_i * dp_i/dh_j, i.e.
-//  softmax: (alpha E / T) * p_j * (f_j - sum_i f_i p_i);  sigmoid: (alpha E / T) f_j s_j (1 - s_j).
+//  softmax: (alpha E / T) * p_j * (f_j - sum_i f_i p_i);  sigmoid-type: (alpha E / T) f_j g'(s_j).
 // The selection bias and the fixed logit offsets receive no gradient.
 // T: tokens to process (rows of probs/idx/w/dg/dlogits); T_batch: the batch size
 // that normalises f and P in the aux loss (equal to T for a whole batch).
@@ -431,20 +484,14 @@ void orc_router_dlogits(int T, int T_batch, int E, int k, int gate, int renorm, 
       }
     } else {
       if (!renorm) {
-        for (int r = 0; r < k; ++r) {
-          double s = p[it[r]];
-          o[it[r]] += gt[r] * s * (1.0 - s);
-        }
+        for (int r = 0; r < k; ++r) o[it[r]] += gt[r] * gate_deriv(gate, p[it[r]]);
       } else {
         double sdot = 0.0, ssum = 0.0;
         for (int r = 0; r < k; ++r) {
           sdot += wt[r] * gt[r];
           ssum += p[it[r]];
         }
-        for (int r = 0; r < k; ++r) {
-          double s = p[it[r]];
-          o[it[r]] += (gt[r] - sdot) / ssum * s * (1.0 - s);
-        }
+        for (int r = 0; r < k; ++r) o[it[r]] += (gt[r] - sdot) / ssum * gate_deriv(gate, p[it[r]]);
       }
     }
     if (alpha != 0.0) {
@@ -454,7 +501,7 @@ void orc_router_dlogits(int T, int T_batch, int E, int k, int gate, int renorm, 
       for (int j = 0; j < E; ++j) {
         double fj = (double)counts[j] / ((double)T_batch * k);
         if (gate == GATE_SOFTMAX) o[j] += c * p[j] * (fj - fp);
-        else o[j] += c * fj * p[j] * (1.0 - p[j]);
+        else o[j] += c * fj * gate_deriv(gate, p[j]);
       }
     }
   }
@@ -479,6 +526,24 @@ void orc_router_grads(int mode, int T, int d, int E, const double* dlogits, cons
       for (int e = 0; e < E; ++e) acc += dlogits[(size_t)t * E + e] * Wr[(size_t)e * d + j];
       dx_router[(size_t)t * d + j] = acc;
     }
+}
+
+// [WIKI] (finding on Quantile Balancing, which restates DeepSeek-V3's rule):
+// the selection bias moves by a fixed step against the load imbalance,
+// b_j <- b_j + gamma * sign(mean load - l_j), where l_j = counts[j] is the
+// number of assignments expert j received in the batch (before capacity drops)
+// and the mean load is sum_i l_i / E. Since E > 0 the sign equals
+// sign(sum_i l_i - E l_j), which is decided here exactly in integers. The step
+// is one fp32 add: b + gamma, b - gamma, or b unchanged. Bias values cross the
+// interface as double holding fp32 values.
+void orc_bias_update(int E, const int* counts, double gamma, const double* bias_in, double* bias_out) {
+  int64_t total = 0;
+  for (int i = 0; i < E; ++i) total += counts[i];
+  for (int j = 0; j < E; ++j) {
+    const int64_t diff = total - (int64_t)E * counts[j];
+    const float b = (float)bias_in[j], g = (float)gamma;
+    bias_out[j] = diff > 0 ? (double)(b + g) : diff < 0 ? (double)(b - g) : (double)b;
+  }
 }
 
 // dx[t] = dy[t] (residual) + sum over kept r of dX_perm[slot[t,r]]

@@ -33,7 +33,7 @@ class LayerConfig:
     f: int                 # expert hidden width (per half for SwiGLU)
     E: int                 # routed experts
     k: int                 # experts per token
-    gate: str = "softmax"  # "softmax" | "sigmoid_bias"
+    gate: str = "softmax"  # "softmax" | "sigmoid_bias" | "sqrt_softplus_bias"
     renorm: bool = False   # renormalise the k selected weights
     act: str = "relu"      # "relu" | "swiglu"
     dtype: str = "bf16"    # activations / expert weights: "bf16" | "f32"

@@ -71,6 +71,44 @@ def test_sigmoid_contract_close_to_logistic():
     assert O.sigmoid_contract(0.0) == 0.5
 
 
+def test_log1p_contract_within_3ulp_of_log1p():
+    # rounding of 2 + u, the division and the final product add up to about 2.6 ulp
+    us = np.concatenate([np.linspace(0, 1, 20001), np.geomspace(1e-30, 1e-3, 2001), [1.0, 0.5]])
+    for u in us.astype(np.float32):
+        got = O.log1p_contract(float(u))
+        true = math.log1p(float(u))
+        assert abs(got - true) <= 3 * float(np.spacing(np.float32(true))) + 1e-45, (u, got, true)
+    assert O.log1p_contract(0.0) == 0.0
+
+
+def _sqrt_softplus64(h):
+    return math.sqrt(max(h, 0.0) + math.log1p(math.exp(-abs(h))))
+
+
+def test_sqrt_softplus_contract_close_to_definition():
+    for x in np.concatenate([np.linspace(-40, 40, 16001), np.linspace(-1, 1, 4001)]).astype(np.float32):
+        s = O.sqrt_softplus_contract(float(x))
+        true = _sqrt_softplus64(float(x))
+        assert abs(s - true) <= 4 * float(np.spacing(np.float32(true))) + 1e-45, (x, s, true)
+    # closed forms: sqrt(ln 2) at 0, sqrt(h) once e^-h is below fp32 resolution, 0 far left
+    assert abs(O.sqrt_softplus_contract(0.0) - math.sqrt(math.log(2.0))) <= 2 * 2.0 ** -24
+    assert O.sqrt_softplus_contract(100.0) == 10.0
+    assert O.sqrt_softplus_contract(-100.0) == 0.0
+
+
+@pytest.mark.parametrize("gate", ["sigmoid_bias", "sqrt_softplus_bias"])
+def test_gate_derivative_from_gate_value(gate):
+    # The backward sees only s = g(h); its derivative written in s must equal dg/dh,
+    # checked against central differences of the plain double gate.
+    g = (lambda h: 1.0 / (1.0 + math.exp(-h))) if gate == "sigmoid_bias" else _sqrt_softplus64
+    gid = O.GATE_OF[gate]
+    for h in np.linspace(-12, 12, 97):
+        eps = 1e-4
+        fd = (g(h + eps) - g(h - eps)) / (2 * eps)
+        assert O.gate_deriv(gid, g(h)) == pytest.approx(fd, rel=1e-6, abs=1e-12), h
+    assert O.gate_deriv(gid, 0.0) == 0.0
+
+
 # ----------------------------------------------------------------- router logits
 
 def test_logits_exact_on_integer_inputs():
@@ -141,7 +179,7 @@ def test_selection_bruteforce_all_tie_patterns(E):
     vals = [-1.0, 0.0, 0.5, 1.0]
     rows = np.array(list(itertools.product(vals, repeat=E)), np.float64)
     for k in range(1, E + 1):
-        for gate in (O.GATE_SOFTMAX, O.GATE_SIGMOID_BIAS):
+        for gate in (O.GATE_SOFTMAX, O.GATE_SIGMOID_BIAS, O.GATE_SQRT_SOFTPLUS_BIAS):
             probs, idx, w = O.gate_topk(O.MODE_F32, rows, k, gate, True,
                                         np.zeros(E) if gate else None)
             for t in range(rows.shape[0]):
@@ -154,18 +192,63 @@ def test_selection_bruteforce_all_tie_patterns(E):
                 assert abs(w[t].sum() - 1.0) < 1e-6
 
 
-def test_sigmoid_bias_only_selects():
+@pytest.mark.parametrize("gate", ["sigmoid_bias", "sqrt_softplus_bias"])
+def test_gate_bias_only_selects(gate):
     rng = np.random.default_rng(4)
     h = rng.standard_normal((64, 16)).astype(np.float32).astype(np.float64)
     b = (rng.random(16) - 0.5).astype(np.float32).astype(np.float64)
-    probs, idx, w = O.gate_topk(O.MODE_F32, h, 4, O.GATE_SIGMOID_BIAS, True, b)
+    probs, idx, w = O.gate_topk(O.MODE_F32, h, 4, O.GATE_OF[gate], True, b)
+    fn = O.sigmoid_contract if gate == "sigmoid_bias" else O.sqrt_softplus_contract
     for t in range(64):
-        s = np.array([O.sigmoid_contract(float(v)) for v in h[t]], np.float64)
+        s = np.array([fn(float(v)) for v in h[t]], np.float64)
         np.testing.assert_array_equal(probs[t], s)
         key = (s.astype(np.float32) + b.astype(np.float32)).astype(np.float64)
         assert set(idx[t].tolist()) == _brute_select(list(key), 4)
         sel = s[idx[t]]
         np.testing.assert_allclose(w[t], sel / sel.sum(), rtol=1e-7)
+
+
+# ----------------------------------------------------------------- selection-bias update
+
+def test_bias_update_hand_example():
+    # loads 3,1,2,2 -> mean 2: the busy expert's bias falls, the idle one's rises,
+    # the two at the mean keep theirs bit for bit
+    b = np.array([0.25, -0.125, 0.1, -0.3], np.float32).astype(np.float64)
+    out = O.bias_update(np.array([3, 1, 2, 2]), 0.001, b)
+    f = np.float32
+    np.testing.assert_array_equal(out, [f(f(0.25) - f(0.001)), f(f(-0.125) + f(0.001)), f(0.1), f(-0.3)])
+
+
+def test_bias_update_balanced_and_fractional_mean():
+    b = np.linspace(-1, 1, 7).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(O.bias_update(np.full(7, 5), 0.5, b), b)
+    # mean 7/3: a load of 2 is below it, 3 above (an integer mean test would call both equal)
+    out = O.bias_update(np.array([2, 2, 3]), 0.5, np.zeros(3))
+    np.testing.assert_array_equal(out, [0.5, 0.5, -0.5])
+
+
+def test_bias_update_balances_a_skewed_router():
+    # Closed loop on a fixed batch: a sigmoid router with a strong per-expert skew
+    # routes most tokens to a few experts; repeated sign steps on the selection bias
+    # must even the loads out (a flipped sign or index makes them worse).
+    rng = np.random.default_rng(11)
+    T, E, k = 2048, 16, 2
+    h = (rng.standard_normal((T, E)) + 2.0 * np.linspace(1, -1, E)).astype(np.float32).astype(np.float64)
+    bias = np.zeros(E)
+
+    def loads(bias):
+        _, idx, _ = O.gate_topk(O.MODE_F32, h, k, O.GATE_SIGMOID_BIAS, True, bias)
+        return np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+
+    c0 = loads(bias)
+    mean = T * k / E
+    assert c0.max() > 2.5 * mean
+    for _ in range(400):
+        bias = O.bias_update(loads(bias), 0.002, bias)
+    c = loads(bias)
+    assert c.max() < 1.2 * mean and c.min() > 0.8 * mean, c
+    # the bias ends ordered against the skew: favoured experts are pushed down
+    assert bias[0] < bias[-1]
 
 
 # ----------------------------------------------------------------- capacity + positions
@@ -324,7 +407,7 @@ def test_single_expert_is_dense_ffn(act):
     np.testing.assert_allclose(fw["y"], ref, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("gate", ["softmax", "sigmoid_bias"])
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid_bias", "sqrt_softplus_bias"])
 def test_identical_experts_renorm_is_dense_ffn(gate):
     cfg = _tiny(6, 3, act="swiglu", gate=gate, sel_bias="uniform" if gate != "softmax" else "none")
     spec = spec_of(cfg, O.MODE_EXACT)
@@ -393,6 +476,9 @@ FD_CASES = [
     dict(E=4, k=2, gate="sigmoid_bias", renorm=True, act="swiglu", cf=0.0, alpha=0.0, shared=1,
          sel_bias="uniform"),
     dict(E=4, k=1, gate="sigmoid_bias", renorm=False, act="relu", cf=0.5, alpha=0.3, sel_bias="uniform"),
+    dict(E=4, k=2, gate="sqrt_softplus_bias", renorm=True, act="swiglu", cf=0.0, alpha=0.3, shared=1,
+         sel_bias="uniform"),
+    dict(E=4, k=1, gate="sqrt_softplus_bias", renorm=False, act="relu", cf=0.5, alpha=0.3, sel_bias="uniform"),
 ]
 
 
