@@ -2,7 +2,8 @@
 
 One step = the whole layer on one batch: moe_route, moe_dispatch,
 moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward (all through the C ABI,
-inputs already resident in HBM). Default workload: the Switch-Base-shaped layer
+inputs already resident in HBM), plus moe_bias_update for the gates that carry
+a selection bias (the aux-loss-free balancing step, gamma = 1e-3). Default workload: the Switch-Base-shaped layer
 (T=8192 tokens as 16x512, d_model=768, 128 ReLU experts 768->3072->768, top-1,
 capacity factor 1.25, bf16 activations and weights, fp32 router, aux alpha 0.01).
 
@@ -29,6 +30,9 @@ PEAK_BF16 = 2.5e15         # flop/s, dense bf16 matrix cores
 # flop/s, fp32 vector FMA without packed-fp32 instructions: 256 CUs x 64 FMA lanes
 # per clock x 2 flop x 2.4 GHz (packed fp32 would double it; it is not generated)
 PEAK_F32_VALU = 78.6e12
+
+# step of the aux-loss-free selection-bias update (the pages give no value)
+BIAS_GAMMA = 1e-3
 
 # Kernel sources whose hash a measured HBM-traffic figure is tied to.
 GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "mfma_tile.h", "internal.h", "common.h", "api.hip")
@@ -113,6 +117,7 @@ def stage_work(c, rows, ne_experts):
         "bwd_dlogits": (0, T * E * 8 + T * k * 12),
         "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 + T * d * 4),
         "bwd_unpermute": (0, T * d * eb * 2 + rows * d * eb + T * d * 4),
+        "bias_update": (0, E * 4 * 3),
     }
 
 
@@ -140,6 +145,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="switch_base")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias"],
+                    help="override the workload's gate (a bias-carrying gate draws the selection bias)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
@@ -159,6 +166,8 @@ def main():
     c = CONFIGS[args.config]
     if c.fwd_only:
         c = c.replace(fwd_only=False)
+    if args.gate and args.gate != c.gate:
+        c = c.replace(gate=args.gate, sel_bias="none" if args.gate == "softmax" else "uniform")
     torch.cuda.set_device(0)
     inp = make_inputs(c, seed=args.seed, device="cuda")
     cfg = M.make_config(c.T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate, act=c.act,
@@ -166,8 +175,12 @@ def main():
     buf = M.LayerBuffers.allocate(cfg)
     stream = torch.cuda.current_stream()
 
+    biased = c.gate != "softmax"
+
     def step():
         M.forward(buf, inp, stream=stream)
+        if biased:
+            M.moe_bias_update(cfg, buf.t["expert_counts"], BIAS_GAMMA, inp["sel_bias"], stream=stream)
         M.backward(buf, inp, inp["dy"], stream=stream)
 
     for _ in range(args.warmup):

@@ -52,6 +52,7 @@ extern "C" {
 /* gates */
 #define MOE_GATE_SOFTMAX 0        /* [SW] eq. (1); selection on the logits */
 #define MOE_GATE_SIGMOID_BIAS 1   /* [WIKI] sigmoid gate + per-expert bias used only to select */
+#define MOE_GATE_SQRT_SOFTPLUS_BIAS 2 /* [WIKI] sqrt(softplus) gate (DeepSeek-V4) + the same selection bias */
 /* expert activations */
 #define MOE_ACT_RELU 0
 #define MOE_ACT_SWIGLU 1          /* silu(x Wg^T) * (x Wu^T); W1 stacks [Wg; Wu] */
@@ -134,6 +135,11 @@ int moe_plan(const moe_config* cfg, moe_plan_info* out);
  *   softmax gate: probs = softmax(h) over the E experts; selection key = h.
  *   sigmoid gate: probs = s = 1/(1 + exp_c(-h)) with exp_c the library's fixed
  *            fp32 exponential (Cody-Waite reduction + degree-7 Taylor); key = s + sel_bias[e].
+ *   sqrt-softplus gate ([WIKI], finding on the gating functions: DeepSeek-V4
+ *            replaces the sigmoid by sqrt(softplus)): probs = s =
+ *            sqrt(max(h,0) + log1p_c(exp_c(-|h|))), one fp32 add and the correctly
+ *            rounded fp32 square root; log1p_c is the library's fixed fp32 log(1+u)
+ *            (artanh series of z = u/(2+u) through z^15); key = s + sel_bias[e].
  *   topk_idx[t,:] = the k experts of largest key, equal keys broken by the lower
  *            index, listed in that order. topk_w[t,r] = probs[t,e_r], divided by the
  *            sum over the k selected when cfg->renormalize.
@@ -194,6 +200,19 @@ int moe_combine(const moe_config* cfg, const void* x, const void* y_perm, const 
  * when aux_alpha == 0. Needs the workspace. */
 int moe_aux_loss(const moe_config* cfg, const float* probs, const int32_t* expert_counts,
                  float* aux_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Aux-loss-free balancing step on the selection bias ([WIKI], finding on
+ * Quantile Balancing, which restates DeepSeek-V3's fixed-step rule):
+ *   sel_bias[j] <- sel_bias[j] + gamma * sign(mean load - expert_counts[j]),
+ *   mean load = sum_i expert_counts[i] / E.
+ * The sign is decided exactly (in 64-bit integers, as sign(sum - E * count));
+ * the step is one fp32 add (b + gamma, b - gamma, or b unchanged). Call it after
+ * moe_dispatch on the counts of the same batch; the updated bias steers the
+ * next moe_route. Only cfg->num_experts is used (the config must still be
+ * valid). expert_counts: [E] int32, non-negative (device). sel_bias: [E] fp32
+ * (device), updated in place. gamma: finite and >= 0 (else MOE_ERR_INVALID_ARG). */
+int moe_bias_update(const moe_config* cfg, const int32_t* expert_counts, float gamma,
+                    float* sel_bias, void* stream);
 
 /* Backward of the layer for the loss L = sum_t <dy[t], y[t]> + aux (aux term
  * only when aux_alpha != 0): [SW] eq. (2) (the gate multiplies the expert

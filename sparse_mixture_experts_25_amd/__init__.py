@@ -6,7 +6,8 @@ fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
 Entry points mirror the C ABI: moe_plan, moe_route, moe_dispatch,
-moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward, moe_status_string.
+moe_expert_ffn, moe_combine, moe_aux_loss, moe_bias_update, moe_backward,
+moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
 ``forward`` / ``backward`` issue the ABI calls in order on those buffers.
 """
@@ -23,12 +24,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = 0, 1
+MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SQRT_SOFTPLUS_BIAS = 0, 1, 2
+GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid_bias": MOE_GATE_SIGMOID_BIAS,
+         "sqrt_softplus_bias": MOE_GATE_SQRT_SOFTPLUS_BIAS}
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
 EXPORTS = ["moe_plan", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-           "moe_backward", "moe_status_string"]
+           "moe_bias_update", "moe_backward", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +86,7 @@ def lib():
         L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_aux_loss.argtypes = [cfg, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_bias_update.argtypes = [cfg, _vp, ctypes.c_float, _vp, _vp]
         L.moe_backward.argtypes = [cfg, _vp, P(moe_saved), P(moe_weights), P(moe_grads), _vp,
                                    ctypes.c_size_t, _vp]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -115,7 +119,7 @@ def _stream(stream=None):
 def make_config(T, d, f, E, k, *, cf=0.0, renorm=False, gate="softmax", act="relu", dtype="bf16",
                 alpha=0.0, shared=0) -> moe_config:
     return moe_config(int(T), int(d), int(f), int(E), int(k), float(cf), int(bool(renorm)),
-                      MOE_GATE_SIGMOID_BIAS if gate == "sigmoid_bias" else MOE_GATE_SOFTMAX,
+                      GATES[gate],
                       MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_RELU,
                       MOE_DT_BF16 if dtype == "bf16" else MOE_DT_F32, float(alpha), int(shared))
 
@@ -153,6 +157,11 @@ def moe_combine(cfg, x, y_perm, slot, topk_w, y_shared, y, stream=None):
 def moe_aux_loss(cfg, probs, expert_counts, aux_out, ws, stream=None):
     _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(probs), _p(expert_counts), _p(aux_out), _p(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_aux_loss")
+
+
+def moe_bias_update(cfg, expert_counts, gamma, sel_bias, stream=None):
+    _check(lib().moe_bias_update(ctypes.byref(cfg), _p(expert_counts), float(gamma), _p(sel_bias),
+                                 _stream(stream)), "moe_bias_update")
 
 
 def moe_backward(cfg, dy, saved: dict, weights: dict, grads: dict, ws, stream=None):

@@ -25,7 +25,8 @@ int check_config(const moe_config* c) {
   if (c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
   if (c->num_experts > 512 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)c->num_tokens * c->top_k > (int64_t)0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS && c->gate != MOE_GATE_SQRT_SOFTPLUS_BIAS)
+    return MOE_ERR_UNSUPPORTED;
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (c->dtype != MOE_DT_F32 && c->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->num_shared_experts != 0 && c->num_shared_experts != 1) return MOE_ERR_UNSUPPORTED;
@@ -263,6 +264,16 @@ int moe_aux_loss(const moe_config* c, const float* probs, const int32_t* expert_
                  c->aux_alpha};
   StageTimer pt("aux", (hipStream_t)stream);
   return launch_status(moe::launch_aux(a, (hipStream_t)stream));
+}
+
+int moe_bias_update(const moe_config* c, const int32_t* expert_counts, float gamma, float* sel_bias,
+                    void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (!expert_counts || !sel_bias || !aligned16(expert_counts) || !aligned16(sel_bias)) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(gamma) || gamma < 0.0f) return MOE_ERR_INVALID_ARG;
+  StageTimer pt("bias_update", (hipStream_t)stream);
+  return launch_status(moe::launch_bias_update(expert_counts, c->num_experts, gamma, sel_bias, (hipStream_t)stream));
 }
 
 int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const moe_weights* w,

@@ -17,6 +17,7 @@ struct RouterArgs {
   int T, d, E, k, gate, renorm, dtype;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st);
 
 struct DispatchArgs {
   const void* x;

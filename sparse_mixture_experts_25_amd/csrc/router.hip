@@ -3,7 +3,8 @@
 // [SW] = "Mixture of Experts (MoE) を1から解説 — Switch Transformerのルーティングと負荷分散"
 // (ta-paperlens.web.app), eq. (1) and the section on routing; [WIKI] =
 // "Mixture-of-Experts" (notes.yuuk.io), bullets on sigmoid gating with a
-// per-expert bias that only steers the selection.
+// per-expert bias that only steers the selection, and the finding on the
+// sigmoid giving way to the square root of softplus.
 //
 // The logit h[t,e] is the fp32 sum over j = 0..d-1 in ascending order of one
 // fused multiply-add per term, starting from +0, so each lane owns whole dot
@@ -56,6 +57,33 @@ __device__ __forceinline__ float sigmoid_c(float h) {
   float den = 1.0f + e;
   return 1.0f / den;
 }
+
+// Fixed-operation log(1 + u) for u in [0, 1]: log(1 + u) = 2 artanh(z) with
+// z = u / (2 + u) in [0, 1/3]; the artanh series through z^15 (first dropped
+// term below 2e-9 relative) as z * P(z^2), P in Horner form with coefficients
+// 2/(2i + 1).
+__device__ __forceinline__ float log1p_c(float u) {
+  const float z = u / (2.0f + u);
+  const float z2 = z * z;
+  float p = 0.133333333333333333f;
+  p = __builtin_fmaf(p, z2, 0.153846153846153846f);
+  p = __builtin_fmaf(p, z2, 0.181818181818181818f);
+  p = __builtin_fmaf(p, z2, 0.222222222222222222f);
+  p = __builtin_fmaf(p, z2, 0.285714285714285714f);
+  p = __builtin_fmaf(p, z2, 0.4f);
+  p = __builtin_fmaf(p, z2, 0.666666666666666667f);
+  p = __builtin_fmaf(p, z2, 2.0f);
+  return z * p;
+}
+
+// Square root of softplus ([WIKI], DeepSeek-V4's replacement of the sigmoid
+// gate): softplus(h) = max(h, 0) + log(1 + e^-|h|), which cannot overflow, then
+// the correctly rounded fp32 square root.
+__device__ __forceinline__ float sqrt_softplus_c(float h) {
+  const float u = exp_c(-__builtin_fabsf(h));
+  const float sp = (h > 0.0f ? h : 0.0f) + log1p_c(u);
+  return __builtin_sqrtf(sp);
+}
 #pragma clang fp contract(on)
 
 // Gate and top-k of one token whose logits h[q] (expert lane + 64 q) sit in
@@ -90,7 +118,7 @@ __device__ __forceinline__ void gate_topk(const float* h, const float* __restric
     for (int q = 0; q < QE; ++q) {
       const int e = lane + 64 * q;
       if (e < E) {
-        p[q] = sigmoid_c(h[q]);
+        p[q] = gate == MOE_GATE_SIGMOID_BIAS ? sigmoid_c(h[q]) : sqrt_softplus_c(h[q]);
         key[q] = sel_bias ? p[q] + sel_bias[e] : p[q];
       } else {
         p[q] = 0.0f;
@@ -505,6 +533,39 @@ hipError_t launch_router_wide(const RouterArgs& a, hipStream_t st) {
   if (a.E <= 128) return big ? launch_router_tile<TX, 8, 1>(a, st) : launch_router_tile<TX, 4, 1>(a, st);
   if (a.E <= 256) return big ? launch_router_tile<TX, 8, 2>(a, st) : launch_router_tile<TX, 4, 2>(a, st);
   return launch_router_tile<TX, 4, 4>(a, st);
+}
+
+namespace {
+
+// Selection-bias step ([WIKI], Quantile Balancing finding, restating
+// DeepSeek-V3's rule): b_j += gamma * sign(mean load - l_j) with l_j =
+// counts[j]. sign(sum_i l_i / E - l_j) = sign(sum_i l_i - E l_j) is decided in
+// 64-bit integers, so the step is exact; the add is one fp32 add. One
+// workgroup: the count total is a fixed tree over LDS.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, int E, float gamma,
+                                                          float* __restrict__ bias) {
+  __shared__ int64_t red[256];
+  int64_t s = 0;
+  for (int i = threadIdx.x; i < E; i += 256) s += counts[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  const int64_t total = red[0];
+  for (int j = threadIdx.x; j < E; j += 256) {
+    const int64_t diff = total - (int64_t)E * counts[j];
+    const float b = bias[j];
+    bias[j] = diff > 0 ? b + gamma : diff < 0 ? b - gamma : b;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(256), 0, st, counts, E, gamma, bias);
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {

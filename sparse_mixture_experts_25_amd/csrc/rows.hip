@@ -167,11 +167,16 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
       }
       if (alpha != 0.0f) v += c * pj * ((float)counts[j] * invTk - fp);
     } else {
+      // derivative of the gate written with its value s: sigmoid s (1 - s);
+      // sqrt(softplus) sigmoid(h) / (2 s) = (1 - e^(-s^2)) / (2 s), 0 at s = 0
+      const float gd = gate == MOE_GATE_SIGMOID_BIAS ? pj * (1.0f - pj)
+                       : pj > 0.0f                   ? -expm1f(-pj * pj) / (2.0f * pj)
+                                                     : 0.0f;
       if (rsel >= 0) {
         const float ds = renorm ? (gt[rsel] - wdg) / ssum : gt[rsel];
-        v = ds * pj * (1.0f - pj);
+        v = ds * gd;
       }
-      if (alpha != 0.0f) v += c * (float)counts[j] * invTk * pj * (1.0f - pj);
+      if (alpha != 0.0f) v += c * (float)counts[j] * invTk * gd;
     }
     dlogits[(int64_t)t * E + j] = v;
   }

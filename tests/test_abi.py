@@ -119,5 +119,12 @@ def test_entry_points_validate_before_launch():
     w = M.moe_weights()
     g = M.moe_grads()
     assert L.moe_backward(c, A, ctypes.byref(s), ctypes.byref(w), ctypes.byref(g), A, ws_need, N) == E
+    L.moe_bias_update.argtypes = [ctypes.POINTER(M.moe_config), ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    assert L.moe_bias_update(c, A, float("nan"), A, N) == E
+    assert L.moe_bias_update(c, A, -1e-3, A, N) == E
+    assert L.moe_bias_update(c, A, float("inf"), A, N) == E
+    assert L.moe_bias_update(c, N, 1e-3, A, N) == E
+    assert L.moe_bias_update(c, A, 1e-3, MIS, N) == E
     bad = M.make_config(64, 60, 64, 4, 2)
     assert L.moe_route(ctypes.byref(bad), A, A, N, N, A, A, A, N) == E

@@ -28,6 +28,12 @@ CASES["big_tiles_swiglu"] = LayerConfig("big_tiles_swiglu", T=2048, d=264, f=392
                                         logit_offset="normal")
 CASES["big_tiles_relu_drops"] = LayerConfig("big_tiles_relu_drops", T=2048, d=296, f=520, E=4, k=1,
                                             act="relu", cf=1.1, alpha=0.01, logit_offset="normal")
+# the square-root-softplus gate with the selection bias, with and without renormalisation
+CASES["sqrt_softplus_bf16"] = SMALL["deepseek_v3"].replace(name="sqrt_softplus_bf16", gate="sqrt_softplus_bias",
+                                                           alpha=0.01)
+CASES["sqrt_softplus_f32_drops"] = LayerConfig("sqrt_softplus_f32_drops", T=200, d=72, f=48, E=8, k=2,
+                                               gate="sqrt_softplus_bias", renorm=False, act="relu", dtype="f32",
+                                               cf=0.75, alpha=0.01, sel_bias="uniform")
 
 
 def _forward_both(c, seed=0):
@@ -159,15 +165,17 @@ def test_determinism_bitwise():
             assert torch.equal(outs[0][k], outs[1][k]), k
 
 
-def test_sigmoid_contract_bitwise():
+@pytest.mark.parametrize("gate", ["sigmoid_bias", "sqrt_softplus_bias"])
+def test_gate_contract_bitwise(gate):
     # one-hot router rows make each logit equal an input value exactly
-    # (x*1 then + x'*0 terms are exact), so probs = sigmoid_contract(x) bit for bit
+    # (x*1 then + x'*0 terms are exact), so probs = the gate contract of x bit for bit
     vals = np.linspace(-30, 30, 8 * 4096, dtype=np.float32)
-    vals = np.concatenate([vals, np.array([0, -0.0, 1e-30, -1e-30, 86, -86, 87, -87, 20, -20], np.float32)])
+    vals = np.concatenate([vals, np.linspace(-1, 1, 8 * 512, dtype=np.float32),
+                           np.array([0, -0.0, 1e-30, -1e-30, 86, -86, 87, -87, 20, -20, 1e30, -1e30], np.float32)])
     E, d = 8, 8
     T = len(vals) // E
     vals = vals[:T * E]
-    c = LayerConfig("sig", T=T, d=d, f=8, E=E, k=2, gate="sigmoid_bias", renorm=True, dtype="f32", cf=0.0)
+    c = LayerConfig("sig", T=T, d=d, f=8, E=E, k=2, gate=gate, renorm=True, dtype="f32", cf=0.0)
     x = torch.from_numpy(vals.reshape(T, E).copy())
     wr = torch.eye(E, d)
     cfg = cfg_of(c)
@@ -177,14 +185,15 @@ def test_sigmoid_contract_bitwise():
     M.moe_route(cfg, x.cuda(), wr.cuda(), None, None, probs, idx, w)
     torch.cuda.synchronize()
     got = probs.cpu().numpy().reshape(-1)
-    ref = np.array([O.sigmoid_contract(float(v)) for v in vals], np.float32)
+    fn = O.sigmoid_contract if gate == "sigmoid_bias" else O.sqrt_softplus_contract
+    ref = np.array([fn(float(v)) for v in vals], np.float32)
     np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 # Router shapes that reach every launch path of moe_route: narrow d_model
 # (scalar-operand kernel; expert counts not a multiple of 4, partial 64-token
 # tiles) and wide d_model (register-tiled kernel with 128, 256 and 512-expert
-# tiles, a ragged last d chunk, bf16 and fp32 activations, sigmoid and softmax).
+# tiles, a ragged last d chunk, bf16 and fp32 activations, all three gates).
 ROUTER_SHAPES = [
     dict(T=130, d=136, E=6, k=2, gate="sigmoid_bias", renorm=True, dtype="f32", sel_bias="uniform"),
     dict(T=333, d=1024, E=64, k=2, gate="softmax", renorm=True, dtype="bf16", logit_offset="normal"),
@@ -192,6 +201,8 @@ ROUTER_SHAPES = [
     dict(T=200, d=2056, E=130, k=1, gate="softmax", renorm=False, dtype="f32"),
     dict(T=97, d=1104, E=100, k=8, gate="sigmoid_bias", renorm=True, dtype="bf16", sel_bias="uniform"),
     dict(T=100, d=1096, E=400, k=2, gate="sigmoid_bias", renorm=False, dtype="bf16", sel_bias="uniform"),
+    dict(T=150, d=1040, E=256, k=8, gate="sqrt_softplus_bias", renorm=True, dtype="bf16", sel_bias="uniform"),
+    dict(T=140, d=200, E=72, k=6, gate="sqrt_softplus_bias", renorm=False, dtype="f32", sel_bias="uniform"),
 ]
 
 
