@@ -74,6 +74,8 @@ def lib():
             "orc_logits": (None, [i, i, i, i, D, D, D, D]),
             "orc_gate": (None, [i, i, i, i, i, i, D, D, D, I, D]),
             "orc_positions": (None, [i, i, i, i, I, I, I, I, I]),
+            "orc_softmax_ec": (None, [i, i, i, D, D]),
+            "orc_expert_choice": (None, [i, i, i, D, I, D, I, I, I]),
             "orc_aux": (d, [i, i, i, i, d, D, I]),
             "orc_ffn_fwd": (None, [i, i, i, i, i, D, D, D, D, D, D]),
             "orc_combine": (None, [i, i, i, i, D, D, I, D, D, D]),
@@ -183,6 +185,29 @@ def positions(idx, E, C):
     lib().orc_positions(T, k, E, C, _i(np.ascontiguousarray(idx, np.int32)), _i(counts),
                         _i(offsets), _i(slot), _i(row_token))
     return counts, offsets, slot, row_token
+
+
+def softmax_ec(mode, h):
+    """Softmax with the expert-choice fp32 contract (plain double softmax in mode 0)."""
+    T, E = h.shape
+    probs = np.empty((T, E))
+    lib().orc_softmax_ec(mode, T, E, _d(np.ascontiguousarray(h, np.float64)), _d(probs))
+    return probs
+
+
+def expert_choice(probs, C):
+    """Each expert takes its C most probable tokens -> slot [T,E], w [T,E], row_token,
+    counts [E], offsets [E+1]."""
+    T, E = probs.shape
+    Cp = min(C, T)
+    slot = np.empty((T, E), np.int32)
+    w = np.empty((T, E))
+    row_token = np.full(max(E * Cp, 1), -1, np.int32)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    lib().orc_expert_choice(T, E, C, _d(np.ascontiguousarray(probs, np.float64)), _i(slot), _d(w),
+                            _i(row_token), _i(counts), _i(offsets))
+    return slot, w, row_token, counts, offsets
 
 
 def aux_loss(mode, probs, counts, k, alpha):
@@ -298,6 +323,7 @@ class Spec:
     cf: float
     alpha: float
     shared: int
+    expert_choice: bool = False
 
     @staticmethod
     def of(cfg, mode=None):
@@ -305,11 +331,21 @@ class Spec:
         act = ACT_SWIGLU if cfg.act == "swiglu" else ACT_RELU
         m = mode if mode is not None else (MODE_F32 if cfg.dtype == "f32" else MODE_BF16)
         return Spec(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, gate, bool(cfg.renorm), act, m,
-                    float(cfg.cf), float(cfg.alpha), int(cfg.shared))
+                    float(cfg.cf), float(cfg.alpha), int(cfg.shared),
+                    getattr(cfg, "routing", "token_choice") == "expert_choice")
 
 
 def route(spec: Spec, x, w_router, logit_offset=None, sel_bias=None):
     h = logits(spec.mode, x, w_router, logit_offset)
+    if spec.expert_choice:
+        # the token tables have one column per expert (k = E); idx is the identity
+        assert spec.k == spec.E and spec.gate == GATE_SOFTMAX and not spec.renorm and spec.cf > 0
+        probs = softmax_ec(spec.mode, h)
+        C = capacity(spec.T, spec.E, spec.cf)
+        slot, w, row_token, counts, offsets = expert_choice(probs, C)
+        idx = np.ascontiguousarray(np.broadcast_to(np.arange(spec.E, dtype=np.int32), (spec.T, spec.E)))
+        return dict(h=h, probs=probs, idx=idx, w=w, C=C, counts=counts, offsets=offsets, slot=slot,
+                    row_token=row_token, aux=0.0)
     probs, idx, w = gate_topk(spec.mode, h, spec.k, spec.gate, spec.renorm, sel_bias)
     C = capacity(spec.T, spec.E, spec.cf)
     counts, offsets, slot, row_token = positions(idx, spec.E, C)

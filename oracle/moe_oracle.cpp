@@ -265,6 +265,72 @@ void orc_gate(int mode, int T, int E, int k, int gate, int renorm, const double*
   }
 }
 
+// Softmax for expert-choice routing. Experts compare probabilities of different
+// tokens, so the probabilities themselves decide the routing and need a fixed
+// fp32 contract: m = max_j h_j; e_j = exp_c(h_j - m) (one fp32 subtraction);
+// z = sum of e_j in ascending j with fp32 adds from +0; p_j = e_j / z (one
+// correctly rounded fp32 division). Mode 0 uses the plain double softmax.
+void orc_softmax_ec(int mode, int T, int E, const double* h, double* probs) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const double* ht = h + (size_t)t * E;
+    double* pt = probs + (size_t)t * E;
+    if (mode == MODE_EXACT) {
+      double m = ht[0];
+      for (int e = 1; e < E; ++e) m = std::max(m, ht[e]);
+      double z = 0.0;
+      for (int e = 0; e < E; ++e) z += std::exp(ht[e] - m);
+      for (int e = 0; e < E; ++e) pt[e] = std::exp(ht[e] - m) / z;
+      continue;
+    }
+    float m = (float)ht[0];
+    for (int e = 1; e < E; ++e) m = std::max(m, (float)ht[e]);
+    std::vector<float> ev(E);
+    float z = 0.0f;
+    for (int e = 0; e < E; ++e) {
+      ev[e] = exp_c((float)ht[e] - m);
+      z = z + ev[e];
+    }
+    for (int e = 0; e < E; ++e) pt[e] = ev[e] / z;
+  }
+}
+
+// Expert-choice routing ([WIKI], survey finding on MoE-based LLMs: the experts,
+// not the tokens, take the top-k). Each expert e takes the C tokens of largest
+// probs[t, e], equal values broken by the lower token index (C >= T: every
+// token). Its seats are listed in ascending token order: row = e * C' + rank,
+// C' = min(C, T). Token tables have one column per expert:
+//   slot[t, e] = row, or -1 if e did not take t;  w[t, e] = probs[t, e] or 0.
+// counts[e] = C' (rows of expert e), offsets[e] = e * C', row_token[row] = t.
+void orc_expert_choice(int T, int E, int C, const double* probs, int* slot, double* w, int* row_token,
+                       int* counts, int* offsets) {
+  const int Cp = std::min(C, T);
+  for (int e = 0; e < E; ++e) {
+    std::vector<int> order(T);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      const double pa = probs[(size_t)a * E + e], pb = probs[(size_t)b * E + e];
+      if (pa != pb) return pa > pb;
+      return a < b;
+    });
+    std::vector<int> chosen(order.begin(), order.begin() + Cp);
+    std::sort(chosen.begin(), chosen.end());
+    for (int t = 0; t < T; ++t) {
+      slot[(size_t)t * E + e] = -1;
+      w[(size_t)t * E + e] = 0.0;
+    }
+    for (int r = 0; r < Cp; ++r) {
+      const int t = chosen[r], row = e * Cp + r;
+      slot[(size_t)t * E + e] = row;
+      w[(size_t)t * E + e] = probs[(size_t)t * E + e];
+      row_token[row] = t;
+    }
+    counts[e] = Cp;
+    offsets[e] = e * Cp;
+  }
+  offsets[E] = E * Cp;
+}
+
 // [SW] section on expert capacity: a fixed number of seats per expert, filled
 // in token order; tokens beyond it skip the expert and ride the residual.
 // pos(t, r) = number of assignments (t', r') with t' < t (a token's k experts

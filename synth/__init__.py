@@ -44,6 +44,7 @@ class LayerConfig:
     sel_bias: str = "none"       # "none" | "uniform"
     router_init: str = "normal_fanin"  # "normal_fanin" | "truncnormal_small"
     fwd_only: bool = False
+    routing: str = "token_choice"  # "token_choice" | "expert_choice" (then k = E)
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)

@@ -251,6 +251,82 @@ def test_bias_update_balances_a_skewed_router():
     assert bias[0] < bias[-1]
 
 
+# ----------------------------------------------------------------- expert-choice routing
+
+def test_softmax_ec_contract():
+    rng = np.random.default_rng(21)
+    for E in (1, 3, 64, 257):
+        h = (rng.standard_normal((40, E)) * 4).astype(np.float32).astype(np.float64)
+        p = O.softmax_ec(O.MODE_F32, h)
+        assert np.all(p == p.astype(np.float32))
+        ref = torch.softmax(torch.from_numpy(h), 1).numpy()
+        # error bound: the rounded difference h - m moves exp by up to |h - m| * 2^-24
+        # relative, exp_c adds a few ulp, the sequential sum of E positive terms (E-1) ulp
+        m = h.max(1, keepdims=True)
+        bound = ref * (np.abs(h - m) + E + 4) * 2.0 ** -24 + 1e-45
+        assert np.all(np.abs(p - ref) <= bound)
+        assert np.all(np.abs(p.sum(1) - 1.0) <= 2 * E * 2.0 ** -24)
+        # equal logits: every e_j = exp_c(0) = 1 and z = E exactly, so p = fl(1/E)
+        np.testing.assert_array_equal(O.softmax_ec(O.MODE_F32, np.full((2, E), 0.75)),
+                                      np.full((2, E), float(np.float32(1.0) / np.float32(E))))
+    # one dominant logit: the others underflow to exactly 0
+    h = np.array([[0.0, 100.0, -3.0]])
+    np.testing.assert_array_equal(O.softmax_ec(O.MODE_F32, h), [[0.0, 1.0, 0.0]])
+
+
+def _ec_brute_column(col, C):
+    # the unique set S of size C with every member beating every non-member on
+    # (probability desc, token index asc)
+    return _brute_select(list(col), min(C, len(col)))
+
+
+@pytest.mark.parametrize("T,E", [(3, 2), (4, 3), (5, 2)])
+def test_expert_choice_bruteforce_tie_patterns(T, E):
+    vals = [0.1, 0.25, 0.5]
+    rng = np.random.default_rng(T * 10 + E)
+    for C in (1, 2, T, T + 3):
+        for _ in range(60):
+            probs = rng.choice(vals, (T, E))
+            slot, w, row_token, counts, offsets = O.expert_choice(probs, C)
+            Cp = min(C, T)
+            np.testing.assert_array_equal(counts, np.full(E, Cp))
+            np.testing.assert_array_equal(offsets, np.arange(E + 1) * Cp)
+            for e in range(E):
+                chosen = set(np.nonzero(slot[:, e] >= 0)[0].tolist())
+                assert chosen == _ec_brute_column(probs[:, e], C)
+                rows = row_token[e * Cp:(e + 1) * Cp]
+                assert rows.tolist() == sorted(chosen)          # seats in token order
+                for r, t in enumerate(rows):
+                    assert slot[t, e] == e * Cp + r and w[t, e] == probs[t, e]
+            assert np.all(w[slot < 0] == 0)
+
+
+def test_expert_choice_every_token_taken_is_dense_mixture():
+    # C >= T: every expert takes every token, so y = x + sum_e p_e FFN_e(x)
+    cfg = _tiny(5, 5, act="swiglu", renorm=False, cf=5.0, routing="expert_choice")  # C = T
+    spec = spec_of(cfg, O.MODE_EXACT)
+    inp = inputs64(cfg)
+    fw = O.forward(spec, inp)
+    assert fw["n_rows"] == 5 * cfg.T
+    p = torch.softmax(torch.from_numpy(inp["x"] @ inp["w_router"].T), 1).numpy()
+    ref = inp["x"].copy()
+    for e in range(5):
+        ref += p[:, e:e + 1] * _dense_ffn(inp["x"], inp["w1"][e], inp["w2"][e], spec.act)
+    np.testing.assert_allclose(fw["y"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_expert_choice_load_is_exactly_balanced():
+    cfg = SMALL["gshard_top2"].replace(routing="expert_choice", k=8, renorm=False, alpha=0.0, cf=2.0)
+    spec = spec_of(cfg)
+    fw = O.forward(spec, inputs64(cfg))
+    C = O.capacity(cfg.T, cfg.E, cfg.cf)
+    np.testing.assert_array_equal(np.diff(fw["offsets"]), np.full(cfg.E, C))
+    assert int((fw["slot"] >= 0).sum()) == cfg.E * C
+    # tokens no expert took pass through unchanged
+    none = np.all(fw["slot"] < 0, axis=1)
+    np.testing.assert_array_equal(fw["y"][none], inputs64(cfg)["x"][none])
+
+
 # ----------------------------------------------------------------- capacity + positions
 
 def test_capacity_golden():
@@ -392,9 +468,9 @@ def _dense_ffn(x, w1, w2, act):
 
 
 def _tiny(E, k, act="relu", gate="softmax", renorm=True, cf=0.0, shared=0, T=24, d=8, f=12, alpha=0.0,
-          sel_bias="none"):
+          sel_bias="none", routing="token_choice"):
     return LayerConfig("t", T=T, d=d, f=f, E=E, k=k, gate=gate, renorm=renorm, act=act, dtype="f32",
-                       cf=cf, alpha=alpha, shared=shared, sel_bias=sel_bias)
+                       cf=cf, alpha=alpha, shared=shared, sel_bias=sel_bias, routing=routing)
 
 
 @pytest.mark.parametrize("act", ["relu", "swiglu"])
@@ -479,6 +555,8 @@ FD_CASES = [
     dict(E=4, k=2, gate="sqrt_softplus_bias", renorm=True, act="swiglu", cf=0.0, alpha=0.3, shared=1,
          sel_bias="uniform"),
     dict(E=4, k=1, gate="sqrt_softplus_bias", renorm=False, act="relu", cf=0.5, alpha=0.3, sel_bias="uniform"),
+    dict(E=4, k=4, gate="softmax", renorm=False, act="swiglu", cf=1.0, routing="expert_choice"),
+    dict(E=4, k=4, gate="softmax", renorm=False, act="relu", cf=0.5, shared=1, routing="expert_choice"),
 ]
 
 
