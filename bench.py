@@ -104,6 +104,8 @@ def stage_work(c, rows, ne_experts):
     W2all = (E + (1 if c.shared else 0)) * d * f * eb
     return {
         "route": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 + T * k * 8),
+        # logits, softmax (probs + transposed copy), selection, token tables, gather
+        "route_ec": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 * 6 + rows * (d * eb * 2 + 4)),
         "dispatch": (0, T * k * 4 * 3 + T * d * eb + rows * d * eb + rows * 4),
         "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * (f1 + f) * eb),
         "ffn_gemm2": (2 * R * f * d, W2 + R * f * eb + R * d * eb),
@@ -145,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="switch_base")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--routing", default="token_choice", choices=["token_choice", "expert_choice"],
+                    help="expert_choice: every expert takes its top tokens (k = E, capacity from cf)")
     ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias"],
                     help="override the workload's gate (a bias-carrying gate draws the selection bias)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size for cpu_baseline")
@@ -168,10 +172,14 @@ def main():
         c = c.replace(fwd_only=False)
     if args.gate and args.gate != c.gate:
         c = c.replace(gate=args.gate, sel_bias="none" if args.gate == "softmax" else "uniform")
+    if args.routing == "expert_choice":
+        # each expert takes C = ceil(T/E * cf) tokens: the same rows as top-k at cf = k
+        c = c.replace(name=c.name + "_ec", routing="expert_choice", k=c.E, gate="softmax", renorm=False,
+                      alpha=0.0, sel_bias="none", cf=c.cf if c.cf > 0 else float(c.k))
     torch.cuda.set_device(0)
     inp = make_inputs(c, seed=args.seed, device="cuda")
     cfg = M.make_config(c.T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate, act=c.act,
-                        dtype=c.dtype, alpha=c.alpha, shared=c.shared)
+                        dtype=c.dtype, alpha=c.alpha, shared=c.shared, routing=c.routing)
     buf = M.LayerBuffers.allocate(cfg)
     stream = torch.cuda.current_stream()
 
@@ -225,7 +233,7 @@ def main():
     ne = int(((offs[1:] - offs[:-1]) > 0).sum())
     work = stage_work(c, rows, ne)
     fl, by = work[dom]
-    if dom in ("route", "bwd_router_grads"):
+    if dom in ("route", "route_ec", "bwd_router_grads"):
         # exact fp32 router: sequential fp32 FMA on the vector units
         roof = {"bound": "alu", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12,
                 "unit": "TFLOP/s"}

@@ -53,6 +53,10 @@ extern "C" {
 #define MOE_GATE_SOFTMAX 0        /* [SW] eq. (1); selection on the logits */
 #define MOE_GATE_SIGMOID_BIAS 1   /* [WIKI] sigmoid gate + per-expert bias used only to select */
 #define MOE_GATE_SQRT_SOFTPLUS_BIAS 2 /* [WIKI] sqrt(softplus) gate (DeepSeek-V4) + the same selection bias */
+/* routing ([WIKI] survey finding on MoE-based LLMs names expert-choice routing) */
+#define MOE_ROUTING_TOKEN_CHOICE 0  /* each token takes its top_k experts (moe_route + moe_dispatch) */
+#define MOE_ROUTING_EXPERT_CHOICE 1 /* each expert takes its C tokens (moe_route_ec); top_k must equal
+                                       num_experts and every [T,k] table has one column per expert */
 /* expert activations */
 #define MOE_ACT_RELU 0
 #define MOE_ACT_SWIGLU 1          /* silu(x Wg^T) * (x Wu^T); W1 stacks [Wg; Wu] */
@@ -76,6 +80,8 @@ typedef struct moe_config {
   int32_t dtype;            /* MOE_DT_*: activations and expert weights */
   float aux_alpha;          /* alpha of [SW] eq. (4); 0 disables the aux loss */
   int32_t num_shared_experts; /* 0 or 1: an always-on expert added with weight 1 ([WIKI]) */
+  int32_t routing;          /* MOE_ROUTING_*; expert choice needs the softmax gate, renormalize = 0,
+                               aux_alpha = 0, capacity_factor > 0 and top_k = num_experts */
 } moe_config;
 
 /* Sizes derived from a config (host memory), filled by moe_plan. */
@@ -149,6 +155,30 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router,
               const float* logit_offset, const float* sel_bias, float* probs,
               int32_t* topk_idx, float* topk_w, void* stream);
 
+/* Expert-choice routing and permutation in one call ([WIKI], survey finding on
+ * MoE-based LLMs: the experts, not the tokens, take the top-k).
+ *   h as in moe_route (+ logit_offset[e]); probs[t,:] = softmax(h[t,:]) with a
+ *     fixed fp32 contract, since experts compare probabilities across tokens:
+ *     m = max_e h; z = sum over ascending e of exp_c(h_e - m) (fp32 adds from +0);
+ *     p_e = exp_c(h_e - m) / z (one correctly rounded division).
+ *   Each expert e takes the C' = min(C, T) tokens of largest probs[t,e]
+ *     (C = ceil(T / E * capacity_factor) in double, as in moe_plan), equal
+ *     values broken by the lower token index; its rows are e*C' .. e*C'+C'-1,
+ *     filled in ascending token order.
+ *   slot[t,e] = row, or -1 if expert e did not take token t; topk_w[t,e] =
+ *     probs[t,e] where taken, else 0; expert_counts[e] = C'; expert_offsets[e]
+ *     = e*C'; row_token[row] = t; x_perm[row] = x[t] (bitwise copy).
+ * The outputs feed moe_expert_ffn, moe_combine and moe_backward unchanged
+ * (k = E; moe_backward needs no topk_idx in this mode). A token no expert took
+ * gets y = x. Requires cfg->routing == MOE_ROUTING_EXPERT_CHOICE.
+ * x [T,d] act, w_router [E,d]; outputs probs [T,E], topk_w [T,E], slot [T,E],
+ * expert_counts [E], expert_offsets [E+1], row_token [E*C'], x_perm [E*C',d].
+ * Needs the workspace. */
+int moe_route_ec(const moe_config* cfg, const void* x, const float* w_router,
+                 const float* logit_offset, float* probs, float* topk_w, int32_t* slot,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                 void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* Capacity, positions and permutation: [SW] eq. (3) and the section on expert
  * capacity (seats fixed before the data is seen, overflow rides the residual),
  * with the compacted expert-contiguous layout of [LRMOE].
@@ -159,6 +189,7 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router,
  *   offsets[e] + pos if kept else -1; row_token[slot] = t;
  *   x_perm[slot] = x[t] (bitwise copy).
  * topk_idx may come from moe_route or from the caller (values must lie in [0,E)).
+ * Token-choice routing only (MOE_ERR_UNSUPPORTED otherwise), as is moe_route.
  * Outputs: expert_counts [E], expert_offsets [E+1], slot [T,k], row_token [R],
  * x_perm [R,d] act. Needs the workspace. */
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,

@@ -5,7 +5,7 @@ kernels. torch supplies device memory and the current stream. There is no
 fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
-Entry points mirror the C ABI: moe_plan, moe_route, moe_dispatch,
+Entry points mirror the C ABI: moe_plan, moe_route, moe_route_ec, moe_dispatch,
 moe_expert_ffn, moe_combine, moe_aux_loss, moe_bias_update, moe_backward,
 moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
@@ -27,10 +27,11 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SQRT_SOFTPLUS_BIAS = 0, 1, 2
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid_bias": MOE_GATE_SIGMOID_BIAS,
          "sqrt_softplus_bias": MOE_GATE_SQRT_SOFTPLUS_BIAS}
+MOE_ROUTING_TOKEN_CHOICE, MOE_ROUTING_EXPERT_CHOICE = 0, 1
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
-EXPORTS = ["moe_plan", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
+EXPORTS = ["moe_plan", "moe_route", "moe_route_ec", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
            "moe_bias_update", "moe_backward", "moe_status_string"]
 
 
@@ -43,7 +44,8 @@ class moe_config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("aux_alpha", ctypes.c_float), ("num_shared_experts", ctypes.c_int32)]
+                ("aux_alpha", ctypes.c_float), ("num_shared_experts", ctypes.c_int32),
+                ("routing", ctypes.c_int32)]
 
 
 class moe_plan_info(ctypes.Structure):
@@ -82,6 +84,7 @@ def lib():
         cfg = P(moe_config)
         L.moe_plan.argtypes = [cfg, P(moe_plan_info)]
         L.moe_route.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_route_ec.argtypes = [cfg] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         L.moe_dispatch.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -117,11 +120,12 @@ def _stream(stream=None):
 
 
 def make_config(T, d, f, E, k, *, cf=0.0, renorm=False, gate="softmax", act="relu", dtype="bf16",
-                alpha=0.0, shared=0) -> moe_config:
+                alpha=0.0, shared=0, routing="token_choice") -> moe_config:
     return moe_config(int(T), int(d), int(f), int(E), int(k), float(cf), int(bool(renorm)),
                       GATES[gate],
                       MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_RELU,
-                      MOE_DT_BF16 if dtype == "bf16" else MOE_DT_F32, float(alpha), int(shared))
+                      MOE_DT_BF16 if dtype == "bf16" else MOE_DT_F32, float(alpha), int(shared),
+                      MOE_ROUTING_EXPERT_CHOICE if routing == "expert_choice" else MOE_ROUTING_TOKEN_CHOICE)
 
 
 def moe_plan(cfg: moe_config) -> moe_plan_info:
@@ -133,6 +137,13 @@ def moe_plan(cfg: moe_config) -> moe_plan_info:
 def moe_route(cfg, x, w_router, logit_offset, sel_bias, probs, topk_idx, topk_w, stream=None):
     _check(lib().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(sel_bias), _p(probs),
                            _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_route_ec(cfg, x, w_router, logit_offset, probs, topk_w, slot, expert_counts, expert_offsets, row_token,
+                 x_perm, ws, stream=None):
+    _check(lib().moe_route_ec(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(probs), _p(topk_w),
+                              _p(slot), _p(expert_counts), _p(expert_offsets), _p(row_token), _p(x_perm), _p(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_route_ec")
 
 
 def moe_dispatch(cfg, x, topk_idx, expert_counts, expert_offsets, slot, row_token, x_perm, ws, stream=None):
@@ -204,12 +215,16 @@ class LayerBuffers:
 
 
 def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
-    """moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (-> moe_aux_loss)."""
+    """moe_route -> moe_dispatch (or moe_route_ec) -> moe_expert_ffn -> moe_combine (-> moe_aux_loss)."""
     c, t = buf.cfg, buf.t
-    moe_route(c, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"), t["probs"],
-              t["topk_idx"], t["topk_w"], stream)
-    moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"], t["row_token"],
-                 t["x_perm"], t["ws"], stream)
+    if c.routing == MOE_ROUTING_EXPERT_CHOICE:
+        moe_route_ec(c, inp["x"], inp["w_router"], inp.get("logit_offset"), t["probs"], t["topk_w"], t["slot"],
+                     t["expert_counts"], t["expert_offsets"], t["row_token"], t["x_perm"], t["ws"], stream)
+    else:
+        moe_route(c, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"), t["probs"],
+                  t["topk_idx"], t["topk_w"], stream)
+        moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
+                     t["row_token"], t["x_perm"], t["ws"], stream)
     moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
                    inp.get("ws2"), t["act_saved"], t["h_saved"], t["y_perm"], t.get("act_shared"),
                    t.get("h_shared"), t.get("y_shared"), t["ws"], stream)

@@ -23,7 +23,14 @@ int check_config(const moe_config* c) {
   if (c->num_tokens < 0 || c->d_model < 8 || c->d_ff < 8) return MOE_ERR_INVALID_ARG;
   if (c->d_model % 8 || c->d_ff % 8) return MOE_ERR_INVALID_ARG;
   if (c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
-  if (c->num_experts > 512 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE && c->routing != MOE_ROUTING_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
+  const bool ec = c->routing == MOE_ROUTING_EXPERT_CHOICE;
+  if (c->num_experts > 512 || (!ec && c->top_k > 64)) return MOE_ERR_UNSUPPORTED;
+  if (ec) {
+    // token tables carry one column per expert; capacity sets the seats
+    if (c->top_k != c->num_experts || !(c->capacity_factor > 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (c->gate != MOE_GATE_SOFTMAX || c->renormalize || c->aux_alpha != 0.0f) return MOE_ERR_UNSUPPORTED;
+  }
   if ((int64_t)c->num_tokens * c->top_k > (int64_t)0x7fffffff) return MOE_ERR_UNSUPPORTED;
   if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS && c->gate != MOE_GATE_SQRT_SOFTPLUS_BIAS)
     return MOE_ERR_UNSUPPORTED;
@@ -86,6 +93,10 @@ size_t workspace_of(const moe_config* c, int64_t R) {
   if (aux > ws) ws = aux;
   const size_t bw = bwd_layout(c, R).total;
   if (bw > ws) ws = bw;
+  if (c->routing == MOE_ROUTING_EXPERT_CHOICE) {
+    const size_t ec = align_up(moe::ec_workspace_bytes(c->num_tokens, c->num_experts));
+    if (ec > ws) ws = ec;
+  }
   return ws;
 }
 
@@ -157,6 +168,7 @@ int moe_route(const moe_config* c, const void* x, const float* w_router, const f
               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
   int st = check_config(c);
   if (st) return st;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;  // token-indexed pointers may then be NULL
   if (!w_router || (!empty && (!x || !probs || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
@@ -167,11 +179,31 @@ int moe_route(const moe_config* c, const void* x, const float* w_router, const f
   return launch_status(moe::launch_router(a, (hipStream_t)stream));
 }
 
+int moe_route_ec(const moe_config* c, const void* x, const float* w_router, const float* logit_offset, float* probs,
+                 float* topk_w, int32_t* slot, int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                 void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->routing != MOE_ROUTING_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
+  const bool empty = c->num_tokens == 0;
+  if (!w_router || !expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (!empty && (!x || !probs || !topk_w || !slot || !row_token || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(c);
+  if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, C))) return MOE_ERR_WORKSPACE;
+  const int Cp = C < c->num_tokens ? C : c->num_tokens;
+  moe::RouteEcArgs a{x, w_router, logit_offset, probs, topk_w, slot, expert_counts, expert_offsets, row_token,
+                     x_perm, ws, c->num_tokens, c->d_model, c->num_experts, Cp, c->dtype, elem_bytes(c)};
+  StageTimer pt("route_ec", (hipStream_t)stream);
+  return launch_status(moe::launch_route_ec(a, (hipStream_t)stream));
+}
+
 int moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, int32_t* expert_counts,
                  int32_t* expert_offsets, int32_t* slot, int32_t* row_token, void* x_perm, void* ws,
                  size_t ws_bytes, void* stream) {
   int st = check_config(c);
   if (st) return st;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;
   if (!expert_counts || !expert_offsets || (!empty && (!x || !topk_idx || !slot || !row_token || !x_perm)))
     return MOE_ERR_INVALID_ARG;
@@ -284,7 +316,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   const bool sh = c->num_shared_experts > 0;
   const bool empty = c->num_tokens == 0;  // token- and row-indexed pointers may then be NULL
   if (!sv->expert_counts || !sv->expert_offsets) return MOE_ERR_INVALID_ARG;
-  if (!empty && (!dy || !sv->x || !sv->probs || !sv->topk_idx || !sv->topk_w || !sv->slot || !sv->x_perm ||
+  const bool ec = c->routing == MOE_ROUTING_EXPERT_CHOICE;  // topk_idx is implied (column = expert)
+  if (!empty && (!dy || !sv->x || !sv->probs || (!ec && !sv->topk_idx) || !sv->topk_w || !sv->slot || !sv->x_perm ||
                  !sv->act_saved || !sv->h_saved || !sv->y_perm || !g->dx))
     return MOE_ERR_INVALID_ARG;
   if (!w->w_router || !w->w1 || !w->w2 || !g->dw_router || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
@@ -380,7 +413,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   if ((st = gemm(c, w1g, s, "bwd_wgrad1"))) return st;
   // router: dlogits, dW_r, dx_router
   if (T > 0) {
-    moe::DlogitsArgs dla{sv->probs, sv->topk_idx, sv->topk_w, dg, sv->expert_counts, dl, T, E, k, c->gate,
+    moe::DlogitsArgs dla{sv->probs, ec ? nullptr : sv->topk_idx, sv->topk_w, dg, sv->expert_counts, dl, T, E, k, c->gate,
                          c->renormalize ? 1 : 0, c->aux_alpha};
     StageTimer pt("bwd_dlogits", s);
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;

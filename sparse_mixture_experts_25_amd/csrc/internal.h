@@ -17,6 +17,28 @@ struct RouterArgs {
   int T, d, E, k, gate, renorm, dtype;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+// gate value of RouterArgs asking for the logits only (probs <- h)
+constexpr int kGateLogitsOnly = -1;
+// Logits only into a.probs; *offset_applied says whether a.logit_offset was
+// already added (the wide-d kernel adds it, the narrow one does not).
+hipError_t launch_router_logits(const RouterArgs& a, hipStream_t st, bool* offset_applied);
+
+struct RouteEcArgs {
+  const void* x;
+  const float* w_router;
+  const float* logit_offset;
+  float* probs;
+  float* topk_w;
+  int32_t* slot;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  void* x_perm;
+  void* ws;  // ec_workspace_bytes(T, E)
+  int T, d, E, Cp, dtype, elem_bytes;
+};
+size_t ec_workspace_bytes(int T, int E);
+hipError_t launch_route_ec(const RouteEcArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st);
 
 struct DispatchArgs {

@@ -17,74 +17,12 @@
 // vector loads. The logits go to the probabilities buffer. Gate and top-k
 // then run one wave per token on that row.
 #include "common.h"
+#include "gate_math.h"
 #include "internal.h"
 
 namespace moe {
 
 namespace {
-
-#pragma clang fp contract(off)
-// Fixed-operation fp32 exponential: Cody-Waite range reduction (Cody & Waite,
-// "Software Manual for the Elementary Functions", 1980) with ln2 split in a
-// 15-bit head and an fp32 tail, then the degree-7 Taylor polynomial of e^r in
-// Horner form with fused multiply-adds, then scaling by 2^n built from the
-// exponent bits. Inputs above 86 give +inf and below -86 give 0, so no result
-// is subnormal. Every operation is a correctly rounded IEEE fp32 operation.
-__device__ __forceinline__ float exp_c(float x) {
-  if (x > 86.0f) return __builtin_inff();
-  if (x < -86.0f) return 0.0f;
-  const float log2e = 1.44269504088896341f;
-  const float ln2_hi = 0.693145751953125f;
-  const float ln2_lo = 1.42860682030941723e-6f;
-  float n = __builtin_rintf(x * log2e);
-  float r = __builtin_fmaf(-n, ln2_hi, x);
-  r = __builtin_fmaf(-n, ln2_lo, r);
-  float p = 1.98412698412698413e-4f;             // 1/7!
-  p = __builtin_fmaf(p, r, 1.38888888888888889e-3f);  // 1/6!
-  p = __builtin_fmaf(p, r, 8.33333333333333333e-3f);  // 1/5!
-  p = __builtin_fmaf(p, r, 4.16666666666666667e-2f);  // 1/4!
-  p = __builtin_fmaf(p, r, 1.66666666666666667e-1f);  // 1/3!
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  int ni = (int)n;
-  float scale = __uint_as_float((uint32_t)(ni + 127) << 23);
-  return p * scale;
-}
-
-__device__ __forceinline__ float sigmoid_c(float h) {
-  float e = exp_c(-h);
-  float den = 1.0f + e;
-  return 1.0f / den;
-}
-
-// Fixed-operation log(1 + u) for u in [0, 1]: log(1 + u) = 2 artanh(z) with
-// z = u / (2 + u) in [0, 1/3]; the artanh series through z^15 (first dropped
-// term below 2e-9 relative) as z * P(z^2), P in Horner form with coefficients
-// 2/(2i + 1).
-__device__ __forceinline__ float log1p_c(float u) {
-  const float z = u / (2.0f + u);
-  const float z2 = z * z;
-  float p = 0.133333333333333333f;
-  p = __builtin_fmaf(p, z2, 0.153846153846153846f);
-  p = __builtin_fmaf(p, z2, 0.181818181818181818f);
-  p = __builtin_fmaf(p, z2, 0.222222222222222222f);
-  p = __builtin_fmaf(p, z2, 0.285714285714285714f);
-  p = __builtin_fmaf(p, z2, 0.4f);
-  p = __builtin_fmaf(p, z2, 0.666666666666666667f);
-  p = __builtin_fmaf(p, z2, 2.0f);
-  return z * p;
-}
-
-// Square root of softplus ([WIKI], DeepSeek-V4's replacement of the sigmoid
-// gate): softplus(h) = max(h, 0) + log(1 + e^-|h|), which cannot overflow, then
-// the correctly rounded fp32 square root.
-__device__ __forceinline__ float sqrt_softplus_c(float h) {
-  const float u = exp_c(-__builtin_fabsf(h));
-  const float sp = (h > 0.0f ? h : 0.0f) + log1p_c(u);
-  return __builtin_sqrtf(sp);
-}
-#pragma clang fp contract(on)
 
 // Gate and top-k of one token whose logits h[q] (expert lane + 64 q) sit in
 // the registers of the wave.
@@ -482,6 +420,12 @@ __global__ __launch_bounds__(256) void router_tile_kernel(
       const int e = lane + 64 * q;
       h[q] = (e < E) ? Ls[t * LP + e] : 0.0f;
     }
+    if (gate == kGateLogitsOnly) {
+#pragma unroll
+      for (int q = 0; q < QE; ++q)
+        if (lane + 64 * q < E) probs[(int64_t)tt * E + lane + 64 * q] = h[q];
+      continue;
+    }
     gate_topk<QE>(h, sel_bias, lane, E, k, gate, renorm, tt, probs, topk_idx, topk_w);
   }
 }
@@ -566,6 +510,26 @@ __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restr
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st) {
   hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(256), 0, st, counts, E, gamma, bias);
   return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const RouterArgs& a, hipStream_t st, bool* offset_applied) {
+  if (a.d <= 1024) {
+    *offset_applied = false;
+    const int64_t total = (int64_t)((a.T + 63) / 64) * ((a.E + kEW * kWaves - 1) / (kEW * kWaves));
+    const dim3 g1((unsigned)((total + 7) / 8 * 8));
+    if (a.dtype == MOE_DT_BF16)
+      hipLaunchKernelGGL(router_logits_kernel<uint16_t>, g1, dim3(256), 0, st, (const uint16_t*)a.x, a.w_router,
+                         a.probs, a.T, a.d, a.E);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<float>, g1, dim3(256), 0, st, (const float*)a.x, a.w_router,
+                         a.probs, a.T, a.d, a.E);
+    return hipGetLastError();
+  }
+  *offset_applied = true;
+  RouterArgs b = a;
+  b.gate = kGateLogitsOnly;
+  if (a.dtype == MOE_DT_BF16) return launch_router_wide<uint16_t>(b, st);
+  return launch_router_wide<float>(b, st);
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {

@@ -135,16 +135,28 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const float* p = probs + (int64_t)t * E;
-  const int32_t* it = topk_idx + (int64_t)t * k;
+  // without topk_idx (expert-choice tables) column r is expert r and k = E
+  const int32_t* it = topk_idx ? topk_idx + (int64_t)t * k : nullptr;
   const float* wt = topk_w + (int64_t)t * k;
   const float* gt = dg + (int64_t)t * k;
   // token-level sums over the k selected
   float S = 0.0f, wdg = 0.0f, ssum = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    const float pe = p[it[r]];
-    S += gt[r] * pe;
-    wdg += wt[r] * gt[r];
-    ssum += pe;
+  if (it) {
+    for (int r = 0; r < k; ++r) {
+      const float pe = p[it[r]];
+      S += gt[r] * pe;
+      wdg += wt[r] * gt[r];
+      ssum += pe;
+    }
+  } else {
+    for (int j = lane; j < E; j += 64) {
+      S += gt[j] * p[j];
+      wdg += wt[j] * gt[j];
+      ssum += p[j];
+    }
+    S = wave_sum(S);
+    wdg = wave_sum(wdg);
+    ssum = wave_sum(ssum);
   }
   const float c = alpha * (float)E / (float)T;
   const float invTk = 1.0f / ((float)T * (float)k);
@@ -155,9 +167,10 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
   }
   for (int j = lane; j < E; j += 64) {
     const float pj = p[j];
-    int rsel = -1;
-    for (int r = 0; r < k; ++r)
-      if (it[r] == j) rsel = r;
+    int rsel = it ? -1 : j;
+    if (it)
+      for (int r = 0; r < k; ++r)
+        if (it[r] == j) rsel = r;
     float v = 0.0f;
     if (gate == MOE_GATE_SOFTMAX) {
       if (!renorm) {

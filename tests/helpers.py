@@ -14,7 +14,7 @@ TOL_F32 = 1e-5    # fp32 router outputs and the fp32 layer
 
 def cfg_of(c, T=None):
     return M.make_config(c.T if T is None else T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate,
-                         act=c.act, dtype=c.dtype, alpha=c.alpha, shared=c.shared)
+                         act=c.act, dtype=c.dtype, alpha=c.alpha, shared=c.shared, routing=c.routing)
 
 
 def relerr(a, r, mask=None) -> float:

@@ -35,6 +35,18 @@ CASES["sqrt_softplus_f32_drops"] = LayerConfig("sqrt_softplus_f32_drops", T=200,
                                                gate="sqrt_softplus_bias", renorm=False, act="relu", dtype="f32",
                                                cf=0.75, alpha=0.01, sel_bias="uniform")
 
+# expert-choice routing (k = E columns): narrow-d logits kernel with a per-expert
+# logit offset, wide-d tile kernel (logits-only mode), fp32 with a shared expert,
+# and C >= T (every expert takes every token)
+_EC = dict(routing="expert_choice", gate="softmax", renorm=False, alpha=0.0)
+CASES["ec_relu_bf16"] = LayerConfig("ec_relu_bf16", T=777, d=192, f=320, E=8, k=8, act="relu", cf=2.0,
+                                    logit_offset="normal", **_EC)
+CASES["ec_swiglu_wide_d"] = LayerConfig("ec_swiglu_wide_d", T=300, d=1032, f=136, E=64, k=64, act="swiglu",
+                                        cf=4.0, logit_offset="logzipf", **_EC)
+CASES["ec_f32_shared"] = LayerConfig("ec_f32_shared", T=130, d=72, f=48, E=6, k=6, act="swiglu", dtype="f32",
+                                     cf=1.5, shared=1, **_EC)
+CASES["ec_all_tokens"] = LayerConfig("ec_all_tokens", T=96, d=64, f=64, E=4, k=4, act="relu", cf=6.0, **_EC)
+
 
 def _forward_both(c, seed=0):
     inp = make_inputs(c, seed=seed)
@@ -48,7 +60,13 @@ def _forward_both(c, seed=0):
 
 def _check_routing(buf, fw, n):
     t = buf.t
-    np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), fw["idx"])
+    if buf.cfg.routing == M.MOE_ROUTING_EXPERT_CHOICE:
+        # the experts compared these probabilities: they must match bit for bit
+        np.testing.assert_array_equal(t["probs"].cpu().numpy().view(np.uint32),
+                                      fw["probs"].astype(np.float32).view(np.uint32))
+        np.testing.assert_array_equal(t["topk_w"].cpu().numpy(), fw["w"].astype(np.float32))
+    else:
+        np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), fw["idx"])
     np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), fw["counts"])
     np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), fw["offsets"])
     np.testing.assert_array_equal(t["slot"].cpu().numpy(), fw["slot"])
@@ -289,3 +307,26 @@ def test_caller_supplied_routing():
     np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), offsets)
     n = int(offsets[-1])
     np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), row_token[:n])
+
+
+def test_expert_choice_ties_and_empty():
+    # a zero router gives every token the same probabilities: each expert takes
+    # the first C tokens; an empty batch writes zero counts and offsets
+    c = CASES["ec_relu_bf16"].replace(name="ec_ties", logit_offset="none")
+    inp = make_inputs(c, seed=2)
+    inp["w_router"] = torch.zeros_like(inp["w_router"])
+    dev = to_dev(inp)
+    buf = run_forward(c, dev, backward=False)
+    torch.cuda.synchronize()
+    C = O.capacity(c.T, c.E, c.cf)
+    slot = buf.t["slot"].cpu().numpy()
+    for e in range(c.E):
+        np.testing.assert_array_equal(np.nonzero(slot[:, e] >= 0)[0], np.arange(C))
+    np.testing.assert_array_equal(buf.t["row_token"][:c.E * C].cpu().numpy(), np.tile(np.arange(C), c.E))
+    e0 = c.replace(T=0)
+    inp0 = to_dev(make_inputs(e0))
+    buf0 = run_forward(e0, inp0)
+    run_backward(buf0, inp0)
+    torch.cuda.synchronize()
+    assert int(buf0.t["expert_offsets"][-1]) == 0 and torch.all(buf0.t["expert_counts"] == 0)
+    assert torch.all(buf0.t["dw1"] == 0)
