@@ -32,10 +32,11 @@ namespace moe {
 namespace {
 
 // p[t, :] = softmax of h[t, :] (+ offset) with the fixed-operation contract.
-// One token per lane; three passes over the row (max, sum, write).
-__global__ __launch_bounds__(256) void ec_softmax_kernel(float* __restrict__ probs, const float* __restrict__ offset,
-                                                         int T, int E, float* __restrict__ pT) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+// One token per lane, one wave per workgroup (spreads small batches over the
+// CUs); three passes over the row (max, sum, write).
+__global__ __launch_bounds__(64) void ec_softmax_kernel(float* __restrict__ probs, const float* __restrict__ offset,
+                                                        int T, int E, float* __restrict__ pT) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= T) return;
   float* row = probs + (int64_t)t * E;
   float m = -__builtin_inff();
@@ -208,7 +209,7 @@ hipError_t launch_route_ec(const RouteEcArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   float* pT = reinterpret_cast<float*>(a.ws);
   int32_t* selpos = reinterpret_cast<int32_t*>(pT + (int64_t)a.T * a.E);
-  hipLaunchKernelGGL(ec_softmax_kernel, dim3((a.T + 255) / 256), dim3(256), 0, st, a.probs,
+  hipLaunchKernelGGL(ec_softmax_kernel, dim3((a.T + 63) / 64), dim3(64), 0, st, a.probs,
                      offset_applied ? nullptr : a.logit_offset, a.T, a.E, pT);
   hipLaunchKernelGGL(ec_select_kernel, dim3(a.E), dim3(kSel), 0, st, pT, a.T, a.E, a.Cp, selpos, a.row_token,
                      a.counts, a.offsets);

@@ -20,8 +20,42 @@ namespace moe {
 
 namespace {
 
-// y[t] = x[t] + sum_kept w[t,r] * y_perm[slot[t,r]] (+ y_shared[t])
-template <typename TX>
+// Wide token tables (expert-choice routing has one column per expert, k = E,
+// with only a few kept) are first compacted per token: the kept columns, in
+// column order, go to a per-wave LDS list, so the row loop touches only them.
+constexpr int kWideK = 8;       // tables wider than this take the compacted path
+constexpr int kListMax = 512;   // most table columns a token can have
+
+// Hand LDS written by some lanes of a wave to the other lanes of that wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Kept columns (slot >= 0) of one token's k columns, in column order: slot to
+// ls[], column to lr[]. Returns their number (wave-uniform).
+__device__ __forceinline__ int kept_columns(const int32_t* __restrict__ srow, int k, int lane, int32_t* ls,
+                                            int32_t* lr) {
+  int n = 0;
+  for (int r0 = 0; r0 < k; r0 += 64) {
+    const int r = r0 + lane;
+    const int s = r < k ? srow[r] : -1;
+    const uint64_t m = __ballot(s >= 0);
+    if (s >= 0) {
+      const int pos = n + (int)__popcll(m & ((1ull << lane) - 1ull));
+      ls[pos] = s;
+      lr[pos] = r;
+    }
+    n += (int)__popcll(m);
+  }
+  wave_lds_sync();
+  return n;
+}
+
+// y[t] = x[t] + sum_kept w[t,r] * y_perm[slot[t,r]] (+ y_shared[t]), kept
+// columns in ascending r
+template <typename TX, bool WIDE>
 __global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, const TX* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot,
                                                       const float* __restrict__ topk_w,
@@ -32,11 +66,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
+  int n = k;
+  const int32_t* ls = nullptr;
+  const int32_t* lr = nullptr;
+  if constexpr (WIDE) {
+    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+    ls = lsb[wave];
+    lr = lrb[wave];
+  }
   for (int v = lane; v < nvec; v += 64) {
     float acc[V], tmp[V];
     Elem<TX>::unpack(ld128(x + (int64_t)t * d + v * V), acc);
-    for (int r = 0; r < k; ++r) {
-      const int s = slot[(int64_t)t * k + r];
+    for (int i = 0; i < n; ++i) {
+      const int r = WIDE ? lr[i] : i;
+      const int s = WIDE ? ls[i] : slot[(int64_t)t * k + r];
       if (s < 0) continue;
       const float w = topk_w[(int64_t)t * k + r];
       Elem<TX>::unpack(ld128(y_perm + (int64_t)s * d + v * V), tmp);
@@ -89,7 +133,7 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict_
 }
 
 // dO[slot] = w * dy[t]; dg[t,r] = <dy[t], y_perm[slot]> (0 when dropped)
-template <typename TX>
+template <typename TX, bool WIDE>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const TX* __restrict__ dy, const TX* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot,
                                                           const float* __restrict__ topk_w, TX* __restrict__ dO,
@@ -99,8 +143,20 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TX* __restrict__
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
-  for (int r = 0; r < k; ++r) {
-    const int s = slot[(int64_t)t * k + r];
+  int n = k;
+  const int32_t* ls = nullptr;
+  const int32_t* lr = nullptr;
+  if constexpr (WIDE) {
+    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+    ls = lsb[wave];
+    lr = lrb[wave];
+    for (int r = lane; r < k; r += 64)
+      if (slot[(int64_t)t * k + r] < 0) dg[(int64_t)t * k + r] = 0.0f;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int r = WIDE ? lr[i] : i;
+    const int s = WIDE ? ls[i] : slot[(int64_t)t * k + r];
     if (s < 0) {
       if (lane == 0) dg[(int64_t)t * k + r] = 0.0f;
       continue;
@@ -285,7 +341,7 @@ __global__ __launch_bounds__(256) void gemm_nn_f32_kernel(const float* __restric
 }
 
 // dx[t] = dy[t] + sum_kept dX_perm[slot] + dx_router[t] (+ dx_shared[t])
-template <typename TX>
+template <typename TX, bool WIDE>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict__ dy,
                                                             const TX* __restrict__ dX_perm,
                                                             const int32_t* __restrict__ slot,
@@ -297,11 +353,18 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
+  int n = k;
+  const int32_t* ls = nullptr;
+  if constexpr (WIDE) {
+    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+    ls = lsb[wave];
+  }
   for (int v = lane; v < nvec; v += 64) {
     float acc[V], tmp[V];
     Elem<TX>::unpack(ld128(dy + (int64_t)t * d + v * V), acc);
-    for (int r = 0; r < k; ++r) {
-      const int s = slot[(int64_t)t * k + r];
+    for (int i = 0; i < n; ++i) {
+      const int s = WIDE ? ls[i] : slot[(int64_t)t * k + i];
       if (s < 0) continue;
       Elem<TX>::unpack(ld128(dX_perm + (int64_t)s * d + v * V), tmp);
 #pragma unroll
@@ -326,15 +389,21 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict
 
 }  // namespace
 
+template <typename TX, bool WIDE>
+void launch_combine_t(const CombineArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((combine_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.x,
+                     (const TX*)a.y_perm, a.slot, a.topk_w, (const TX*)a.y_shared, (TX*)a.y, a.T, a.d, a.k);
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  const dim3 grid((a.T + 3) / 4);
-  if (a.dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.x,
-                       (const uint16_t*)a.y_perm, a.slot, a.topk_w, (const uint16_t*)a.y_shared,
-                       (uint16_t*)a.y, a.T, a.d, a.k);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, (const float*)a.x, (const float*)a.y_perm,
-                       a.slot, a.topk_w, (const float*)a.y_shared, (float*)a.y, a.T, a.d, a.k);
+  const bool wide = a.k > kWideK;
+  if (a.dtype == MOE_DT_BF16) {
+    if (wide) launch_combine_t<uint16_t, true>(a, st);
+    else launch_combine_t<uint16_t, false>(a, st);
+  } else {
+    if (wide) launch_combine_t<float, true>(a, st);
+    else launch_combine_t<float, false>(a, st);
+  }
   return hipGetLastError();
 }
 
@@ -349,14 +418,21 @@ hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename TX, bool WIDE>
+void launch_combine_bwd_t(const CombineBwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((combine_bwd_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.dy,
+                     (const TX*)a.y_perm, a.slot, a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k);
+}
+
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
-  const dim3 grid((a.T + 3) / 4);
-  if (a.dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.dy,
-                       (const uint16_t*)a.y_perm, a.slot, a.topk_w, (uint16_t*)a.dO, a.dg, a.T, a.d, a.k);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, st, (const float*)a.dy,
-                       (const float*)a.y_perm, a.slot, a.topk_w, (float*)a.dO, a.dg, a.T, a.d, a.k);
+  const bool wide = a.k > kWideK;
+  if (a.dtype == MOE_DT_BF16) {
+    if (wide) launch_combine_bwd_t<uint16_t, true>(a, st);
+    else launch_combine_bwd_t<uint16_t, false>(a, st);
+  } else {
+    if (wide) launch_combine_bwd_t<float, true>(a, st);
+    else launch_combine_bwd_t<float, false>(a, st);
+  }
   return hipGetLastError();
 }
 
@@ -407,16 +483,21 @@ hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename TX, bool WIDE>
+void launch_unpermute_bwd_t(const UnpermuteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((unpermute_bwd_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.dy,
+                     (const TX*)a.dX_perm, a.slot, a.dx_router, (const TX*)a.dx_shared, (TX*)a.dx, a.T, a.d, a.k);
+}
+
 hipError_t launch_unpermute_bwd(const UnpermuteArgs& a, hipStream_t st) {
-  const dim3 grid((a.T + 3) / 4);
-  if (a.dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(unpermute_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)a.dy,
-                       (const uint16_t*)a.dX_perm, a.slot, a.dx_router, (const uint16_t*)a.dx_shared,
-                       (uint16_t*)a.dx, a.T, a.d, a.k);
-  else
-    hipLaunchKernelGGL(unpermute_bwd_kernel<float>, grid, dim3(256), 0, st, (const float*)a.dy,
-                       (const float*)a.dX_perm, a.slot, a.dx_router, (const float*)a.dx_shared, (float*)a.dx,
-                       a.T, a.d, a.k);
+  const bool wide = a.k > kWideK;
+  if (a.dtype == MOE_DT_BF16) {
+    if (wide) launch_unpermute_bwd_t<uint16_t, true>(a, st);
+    else launch_unpermute_bwd_t<uint16_t, false>(a, st);
+  } else {
+    if (wide) launch_unpermute_bwd_t<float, true>(a, st);
+    else launch_unpermute_bwd_t<float, false>(a, st);
+  }
   return hipGetLastError();
 }
 
