@@ -70,6 +70,8 @@ def lib():
             "orc_sqrt_softplus_contract": (ctypes.c_float, [ctypes.c_float]),
             "orc_gate_deriv": (d, [i, d]),
             "orc_bias_update": (None, [i, I, d, D, D]),
+            "orc_bias_quantile": (None, [i, i, i, D, D, D]),
+            "qb_target": (i, [i, i, i]),
             "orc_capacity": (i, [i, i, d]),
             "orc_logits": (None, [i, i, i, i, D, D, D, D]),
             "orc_gate": (None, [i, i, i, i, i, i, D, D, D, I, D]),
@@ -153,6 +155,20 @@ def bias_update(counts, gamma: float, bias):
     out = np.empty_like(b)
     lib().orc_bias_update(int(c.size), _i(c), float(gamma), _d(b), _d(out))
     return out
+
+
+def bias_quantile(probs, k: int, bias):
+    """Quantile-Balancing bias from one batch's gate values (fp32 values as float64)."""
+    p = f64(probs)
+    T, E = p.shape
+    b = f64(bias)
+    out = np.empty_like(b)
+    lib().orc_bias_quantile(T, E, int(k), _d(p), _d(b), _d(out))
+    return out
+
+
+def qb_target(T: int, E: int, k: int) -> int:
+    return lib().qb_target(int(T), int(E), int(k))
 
 
 def capacity(T: int, E: int, cf: float) -> int:

@@ -612,6 +612,59 @@ void orc_bias_update(int E, const int* counts, double gamma, const double* bias_
   }
 }
 
+// [WIKI] (finding on Quantile Balancing, Kimi K3): each expert's selection
+// bias is set from a quantile of routing margins at the target load
+// q = T k / E (tokens times experts per token over experts), the margins taken
+// against the top-(k+1) cutoff, and the result used from the next step on.
+// Reading written out here (fp32 like the routing itself):
+//   key[t, j] = s[t, j] + b[j] (s = the gate values in probs);
+//   per token, with keys ordered descending (ties: lower index first), c_k and
+//   c_k1 are the k-th and (k+1)-th keys; margin m[t, j] = key[t, j] - c_k1 if
+//   j is among the first k, else key[t, j] - c_k. Moving b[j] alone by delta
+//   keeps or wins token t for j exactly when m[t, j] + delta > 0 (up to ties).
+//   Per expert, mu_1 >= mu_2 >= ... are its margins over the batch; with
+//   q = ceil(T k / E) clamped to [1, T - 1], delta[j] = -(mu_q + mu_(q+1)) / 2,
+//   so that exactly q margins clear it, and b[j] <- b[j] + delta[j]: one fp32
+//   add of the two margins, a multiply by 0.5 (exact) and one fp32 subtraction.
+// The page's histogram of margins is the distributed approximation of this
+// quantile; one device computes it exactly. T < 2 leaves the bias unchanged.
+int qb_target(int T, int E, int k) {
+  int64_t q = ((int64_t)T * k + E - 1) / E;
+  if (q > T - 1) q = T - 1;
+  if (q < 1) q = 1;
+  return (int)q;
+}
+
+void orc_bias_quantile(int T, int E, int k, const double* probs, const double* bias_in, double* bias_out) {
+  for (int j = 0; j < E; ++j) bias_out[j] = bias_in[j];
+  if (T < 2) return;
+  std::vector<float> m((size_t)T * E);
+  for (int t = 0; t < T; ++t) {
+    std::vector<float> key(E);
+    for (int j = 0; j < E; ++j) key[j] = (float)probs[(size_t)t * E + j] + (float)bias_in[j];
+    std::vector<int> order(E);
+    std::iota(order.begin(), order.end(), 0);
+    std::sort(order.begin(), order.end(), [&](int a, int b) {
+      if (key[a] != key[b]) return key[a] > key[b];
+      return a < b;
+    });
+    std::vector<char> sel(E, 0);
+    for (int r = 0; r < k; ++r) sel[order[r]] = 1;
+    const float ck = key[order[k - 1]];
+    const float ck1 = k < E ? key[order[k]] : -INFINITY;
+    for (int j = 0; j < E; ++j) m[(size_t)t * E + j] = key[j] - (sel[j] ? ck1 : ck);
+  }
+  const int q = qb_target(T, E, k);
+  for (int j = 0; j < E; ++j) {
+    std::vector<float> col(T);
+    for (int t = 0; t < T; ++t) col[t] = m[(size_t)t * E + j];
+    std::sort(col.begin(), col.end(), [](float a, float b) { return a > b; });
+    const float sum = col[q - 1] + col[q];
+    const float half = sum * 0.5f;
+    bias_out[j] = (double)((float)bias_in[j] - half);
+  }
+}
+
 // dx[t] = dy[t] (residual) + sum over kept r of dX_perm[slot[t,r]]
 //         + dx_router[t] (+ dx_shared[t]).
 void orc_unpermute_bwd(int mode, int T, int d, int k, const double* dy, const double* dX_perm,

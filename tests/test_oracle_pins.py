@@ -251,6 +251,59 @@ def test_bias_update_balances_a_skewed_router():
     assert bias[0] < bias[-1]
 
 
+def test_bias_quantile_hand_example():
+    # T=3, E=2, k=1, zero bias: q = ceil(3/2) = 2. Expert 0 margins 0.8, 0.5, 0.1 (each
+    # token's key minus its best rival), expert 1 the negatives; the bias moves to minus
+    # the midpoint of the 2nd and 3rd largest margins
+    f = np.float32
+    s = np.array([[0.9, 0.1], [0.8, 0.3], [0.7, 0.6]], np.float32)
+    out = O.bias_quantile(s.astype(np.float64), 1, np.zeros(2))
+    m0 = [f(s[t, 0] - s[t, 1]) for t in range(3)]
+    m1 = [f(s[t, 1] - s[t, 0]) for t in range(3)]
+    a0, b0 = sorted(m0, reverse=True)[1:3]
+    a1, b1 = sorted(m1, reverse=True)[1:3]
+    np.testing.assert_array_equal(out, [f(0) - f(f(a0 + b0) * f(0.5)), f(0) - f(f(a1 + b1) * f(0.5))])
+    assert O.qb_target(3, 2, 1) == 2 and O.qb_target(10, 4, 8) == 9 and O.qb_target(100, 64, 1) == 2
+
+
+def _skewed_sigmoid_router(T=1200, E=12, k=2, seed=5):
+    rng = np.random.default_rng(seed)
+    h = (rng.standard_normal((T, E)) + 1.5 * np.linspace(1, -1, E)).astype(np.float32).astype(np.float64)
+
+    def route(b):
+        p, idx, _ = O.gate_topk(O.MODE_F32, h, k, O.GATE_SIGMOID_BIAS, True, b)
+        return p, np.bincount(idx.ravel(), minlength=E)
+    return route
+
+
+def test_bias_quantile_single_expert_reaches_target_exactly():
+    # moving one expert's bias by its step, the others fixed, gives it exactly q tokens:
+    # this fixes the margins (which cutoff, which sign) and the rank of the quantile
+    T, E, k = 1200, 12, 2
+    route = _skewed_sigmoid_router(T, E, k)
+    b0 = np.zeros(E)
+    p, c0 = route(b0)
+    q = O.qb_target(T, E, k)
+    bq = O.bias_quantile(p, k, b0)
+    for j in range(E):
+        b = b0.copy()
+        b[j] = bq[j]
+        assert route(b)[1][j] == q, j
+    assert c0.max() > 3 * q
+
+
+def test_bias_quantile_closed_loop_balances():
+    T, E, k = 1200, 12, 2
+    route = _skewed_sigmoid_router(T, E, k)
+    q = O.qb_target(T, E, k)
+    b = np.zeros(E)
+    p, c = route(b)
+    for _ in range(3):
+        b = O.bias_quantile(p, k, b)
+        p, c = route(b)
+    assert np.all(np.abs(c - q) <= 0.05 * q), c
+
+
 # ----------------------------------------------------------------- expert-choice routing
 
 def test_softmax_ec_contract():
