@@ -627,7 +627,8 @@ void orc_bias_update(int E, const int* counts, double gamma, const double* bias_
 //   so that exactly q margins clear it, and b[j] <- b[j] + delta[j]: one fp32
 //   add of the two margins, a multiply by 0.5 (exact) and one fp32 subtraction.
 // The page's histogram of margins is the distributed approximation of this
-// quantile; one device computes it exactly. T < 2 leaves the bias unchanged.
+// quantile; one device computes it exactly. T < 2, or k >= E (every expert
+// takes every token, nothing to balance), leaves the bias unchanged.
 int qb_target(int T, int E, int k) {
   int64_t q = ((int64_t)T * k + E - 1) / E;
   if (q > T - 1) q = T - 1;
@@ -637,7 +638,7 @@ int qb_target(int T, int E, int k) {
 
 void orc_bias_quantile(int T, int E, int k, const double* probs, const double* bias_in, double* bias_out) {
   for (int j = 0; j < E; ++j) bias_out[j] = bias_in[j];
-  if (T < 2) return;
+  if (T < 2 || k >= E) return;
   std::vector<float> m((size_t)T * E);
   for (int t = 0; t < T; ++t) {
     std::vector<float> key(E);
@@ -651,7 +652,7 @@ void orc_bias_quantile(int T, int E, int k, const double* probs, const double* b
     std::vector<char> sel(E, 0);
     for (int r = 0; r < k; ++r) sel[order[r]] = 1;
     const float ck = key[order[k - 1]];
-    const float ck1 = k < E ? key[order[k]] : -INFINITY;
+    const float ck1 = key[order[k]];
     for (int j = 0; j < E; ++j) m[(size_t)t * E + j] = key[j] - (sel[j] ? ck1 : ck);
   }
   const int q = qb_target(T, E, k);

@@ -264,6 +264,10 @@ def test_bias_quantile_hand_example():
     a1, b1 = sorted(m1, reverse=True)[1:3]
     np.testing.assert_array_equal(out, [f(0) - f(f(a0 + b0) * f(0.5)), f(0) - f(f(a1 + b1) * f(0.5))])
     assert O.qb_target(3, 2, 1) == 2 and O.qb_target(10, 4, 8) == 9 and O.qb_target(100, 64, 1) == 2
+    # k = E: every expert takes every token, the bias stays; one token: no quantile
+    np.testing.assert_array_equal(O.bias_quantile(s.astype(np.float64), 2, np.array([0.5, -0.25])), [0.5, -0.25])
+    np.testing.assert_array_equal(O.bias_quantile(s[:1].astype(np.float64), 1, np.array([0.5, -0.25])),
+                                  [0.5, -0.25])
 
 
 def _skewed_sigmoid_router(T=1200, E=12, k=2, seed=5):
