@@ -3,7 +3,8 @@
 One step = the whole layer on one batch: moe_route, moe_dispatch,
 moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward (all through the C ABI,
 inputs already resident in HBM), plus moe_bias_update for the gates that carry
-a selection bias (the aux-loss-free balancing step, gamma = 1e-3). Default workload: the Switch-Base-shaped layer
+a selection bias (the aux-loss-free balancing step, gamma = 1e-3, or with
+--balance quantile the Quantile-Balancing step). Default workload: the Switch-Base-shaped layer
 (T=8192 tokens as 16x512, d_model=768, 128 ReLU experts 768->3072->768, top-1,
 capacity factor 1.25, bf16 activations and weights, fp32 router, aux alpha 0.01).
 
@@ -120,6 +121,8 @@ def stage_work(c, rows, ne_experts):
         "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 + T * d * 4),
         "bwd_unpermute": (0, T * d * eb * 2 + rows * d * eb + T * d * 4),
         "bias_update": (0, E * 4 * 3),
+        # gate values read twice (cuts, margins), margins written and read twice (two selects)
+        "bias_quantile": (0, T * E * 4 * 5 + T * 16 * 2),
     }
 
 
@@ -147,6 +150,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="switch_base")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--balance", default="sign", choices=["sign", "quantile"],
+                    help="selection-bias step of the bias-carrying gates: sign (fixed step) or quantile")
     ap.add_argument("--routing", default="token_choice", choices=["token_choice", "expert_choice"],
                     help="expert_choice: every expert takes its top tokens (k = E, capacity from cf)")
     ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias"],
@@ -187,7 +192,9 @@ def main():
 
     def step():
         M.forward(buf, inp, stream=stream)
-        if biased:
+        if biased and args.balance == "quantile":
+            M.moe_bias_quantile(cfg, buf.t["probs"], inp["sel_bias"], buf.t["ws"], stream=stream)
+        elif biased:
             M.moe_bias_update(cfg, buf.t["expert_counts"], BIAS_GAMMA, inp["sel_bias"], stream=stream)
         M.backward(buf, inp, inp["dy"], stream=stream)
 

@@ -245,6 +245,28 @@ int moe_aux_loss(const moe_config* cfg, const float* probs, const int32_t* exper
 int moe_bias_update(const moe_config* cfg, const int32_t* expert_counts, float gamma,
                     float* sel_bias, void* stream);
 
+/* Quantile Balancing of the selection bias ([WIKI], finding on Quantile
+ * Balancing: the bias of each expert is set from the quantile of routing
+ * margins at the target load, margins taken against the top-(k+1) cutoff, and
+ * used from the next step on). With key[t,j] = probs[t,j] + sel_bias[j] (fp32)
+ * and, per token, c_k and c_k1 its k-th and (k+1)-th keys (descending, lower
+ * index first on ties):
+ *   margin[t,j] = key - c_k1 if j is among the token's k selected experts,
+ *                 key - c_k otherwise
+ *   (moving sel_bias[j] alone by delta keeps or wins token t for j exactly when
+ *   margin + delta > 0);
+ *   q = ceil(T*k/E) clamped to [1, T-1]; mu_q >= mu_(q+1) the q-th and (q+1)-th
+ *   largest margins of expert j;
+ *   sel_bias[j] <- sel_bias[j] - (mu_q + mu_(q+1)) * 0.5   (fp32 add, exact halving,
+ *   fp32 subtraction).
+ * The page estimates the quantile from margin histograms reduced across
+ * devices; here it is exact. T < 2 or top_k >= E leaves the bias unchanged.
+ * probs: [T,E] the gate values moe_route wrote for this batch (sigmoid-type
+ * gates only; softmax -> MOE_ERR_UNSUPPORTED). sel_bias: [E] fp32, updated in
+ * place, to be used by the next moe_route. Needs the workspace. */
+int moe_bias_quantile(const moe_config* cfg, const float* probs, float* sel_bias, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Backward of the layer for the loss L = sum_t <dy[t], y[t]> + aux (aux term
  * only when aux_alpha != 0): [SW] eq. (2) (the gate multiplies the expert
  * output, so the router is trained through it) and eq. (4) (only P carries

@@ -6,7 +6,7 @@ fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
 Entry points mirror the C ABI: moe_plan, moe_route, moe_route_ec, moe_dispatch,
-moe_expert_ffn, moe_combine, moe_aux_loss, moe_bias_update, moe_backward,
+moe_expert_ffn, moe_combine, moe_aux_loss, moe_bias_update, moe_bias_quantile, moe_backward,
 moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
 ``forward`` / ``backward`` issue the ABI calls in order on those buffers.
@@ -32,7 +32,7 @@ MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
 EXPORTS = ["moe_plan", "moe_route", "moe_route_ec", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-           "moe_bias_update", "moe_backward", "moe_status_string"]
+           "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -90,6 +90,7 @@ def lib():
         L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_aux_loss.argtypes = [cfg, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_bias_update.argtypes = [cfg, _vp, ctypes.c_float, _vp, _vp]
+        L.moe_bias_quantile.argtypes = [cfg, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_backward.argtypes = [cfg, _vp, P(moe_saved), P(moe_weights), P(moe_grads), _vp,
                                    ctypes.c_size_t, _vp]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -173,6 +174,11 @@ def moe_aux_loss(cfg, probs, expert_counts, aux_out, ws, stream=None):
 def moe_bias_update(cfg, expert_counts, gamma, sel_bias, stream=None):
     _check(lib().moe_bias_update(ctypes.byref(cfg), _p(expert_counts), float(gamma), _p(sel_bias),
                                  _stream(stream)), "moe_bias_update")
+
+
+def moe_bias_quantile(cfg, probs, sel_bias, ws, stream=None):
+    _check(lib().moe_bias_quantile(ctypes.byref(cfg), _p(probs), _p(sel_bias), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "moe_bias_quantile")
 
 
 def moe_backward(cfg, dy, saved: dict, weights: dict, grads: dict, ws, stream=None):

@@ -97,6 +97,10 @@ size_t workspace_of(const moe_config* c, int64_t R) {
     const size_t ec = align_up(moe::ec_workspace_bytes(c->num_tokens, c->num_experts));
     if (ec > ws) ws = ec;
   }
+  if (c->gate != MOE_GATE_SOFTMAX) {
+    const size_t qb = align_up(moe::qb_workspace_bytes(c->num_tokens, c->num_experts));
+    if (qb > ws) ws = qb;
+  }
   return ws;
 }
 
@@ -306,6 +310,19 @@ int moe_bias_update(const moe_config* c, const int32_t* expert_counts, float gam
   if (!isfinite(gamma) || gamma < 0.0f) return MOE_ERR_INVALID_ARG;
   StageTimer pt("bias_update", (hipStream_t)stream);
   return launch_status(moe::launch_bias_update(expert_counts, c->num_experts, gamma, sel_bias, (hipStream_t)stream));
+}
+
+int moe_bias_quantile(const moe_config* c, const float* probs, float* sel_bias, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->gate == MOE_GATE_SOFTMAX || c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+  if (!sel_bias || (c->num_tokens > 0 && !probs) || !aligned16(probs) || !aligned16(sel_bias))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, capacity_of(c)))) return MOE_ERR_WORKSPACE;
+  StageTimer pt("bias_quantile", (hipStream_t)stream);
+  return launch_status(moe::launch_bias_quantile(probs, sel_bias, c->num_tokens, c->num_experts, c->top_k, ws,
+                                                 (hipStream_t)stream));
 }
 
 int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const moe_weights* w,

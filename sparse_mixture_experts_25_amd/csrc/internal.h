@@ -40,6 +40,8 @@ struct RouteEcArgs {
 size_t ec_workspace_bytes(int T, int E);
 hipError_t launch_route_ec(const RouteEcArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st);
+size_t qb_workspace_bytes(int T, int E);
+hipError_t launch_bias_quantile(const float* probs, float* bias, int T, int E, int k, void* ws, hipStream_t st);
 
 struct DispatchArgs {
   const void* x;

@@ -126,5 +126,13 @@ def test_entry_points_validate_before_launch():
     assert L.moe_bias_update(c, A, float("inf"), A, N) == E
     assert L.moe_bias_update(c, N, 1e-3, A, N) == E
     assert L.moe_bias_update(c, A, 1e-3, MIS, N) == E
+    L.moe_bias_quantile.argtypes = [ctypes.POINTER(M.moe_config), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert L.moe_bias_quantile(c, A, A, A, ws_need, N) == M.MOE_ERR_UNSUPPORTED  # softmax gate
+    sg = M.make_config(64, 64, 64, 4, 2, gate="sigmoid_bias")
+    ws_sg = M.moe_plan(sg).workspace_bytes
+    assert L.moe_bias_quantile(ctypes.byref(sg), A, N, A, ws_sg, N) == E
+    assert L.moe_bias_quantile(ctypes.byref(sg), MIS, A, A, ws_sg, N) == E
+    assert L.moe_bias_quantile(ctypes.byref(sg), A, A, A, ws_sg - 1, N) == M.MOE_ERR_WORKSPACE
     bad = M.make_config(64, 60, 64, 4, 2)
     assert L.moe_route(ctypes.byref(bad), A, A, N, N, A, A, A, N) == E

@@ -69,3 +69,59 @@ def test_bias_update_closed_loop(gate):
         bias_ref = O.bias_update(r["counts"], gamma, bias_ref)
         np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32),
                                       bias_ref.astype(np.float32).view(np.uint32))
+
+
+# Quantile Balancing: the GPU's margins, exact quantiles and bias step against the
+# oracle's on the same gate values, bit for bit; shapes cover one to eight experts
+# per lane, k = E (no change) and a two-token batch
+QB_SHAPES = [(1000, 16, 2, "sigmoid_bias"), (777, 64, 6, "sqrt_softplus_bias"), (300, 256, 8, "sigmoid_bias"),
+             (513, 400, 3, "sqrt_softplus_bias"), (64, 8, 8, "sigmoid_bias"), (2, 4, 1, "sigmoid_bias")]
+
+
+@pytest.mark.parametrize("shape", range(len(QB_SHAPES)))
+def test_bias_quantile_bitwise(shape):
+    T, E, k, gate = QB_SHAPES[shape]
+    print(f"\n[bias quantile] T={T} E={E} k={k} {gate}", flush=True)
+    c = LayerConfig("qb", T=T, d=64, f=8, E=E, k=k, gate=gate, renorm=True, dtype="bf16", cf=0.0,
+                    logit_offset="logzipf", sel_bias="uniform")
+    cfg = cfg_of(c)
+    buf = M.LayerBuffers.allocate(cfg, backward=False)
+    t = buf.t
+    inp = to_dev(make_inputs(c, seed=shape, with_dy=False))
+    bias = inp["sel_bias"].clone()
+    b0 = host64(bias)
+    M.moe_route(cfg, inp["x"], inp["w_router"], inp["logit_offset"], bias, t["probs"], t["topk_idx"], t["topk_w"])
+    M.moe_bias_quantile(cfg, t["probs"], bias, t["ws"])
+    torch.cuda.synchronize()
+    ref = O.bias_quantile(host64(t["probs"]), k, b0).astype(np.float32)
+    np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_bias_quantile_closed_loop():
+    # the same skewed batch routed again after each step: GPU and oracle agree on
+    # every decision and bias bit, and the loads approach q = ceil(T k / E)
+    c = LayerConfig("qb_loop", T=2048, d=128, f=8, E=32, k=4, gate="sigmoid_bias", renorm=True, dtype="bf16",
+                    cf=0.0, logit_offset="logzipf", sel_bias="uniform")
+    cfg = cfg_of(c)
+    buf = M.LayerBuffers.allocate(cfg, backward=False)
+    t = buf.t
+    inp = to_dev(make_inputs(c, seed=3, with_dy=False))
+    bias = inp["sel_bias"].clone()
+    bias_ref = host64(bias)
+    spec = O.Spec.of(c)
+    q = O.qb_target(c.T, c.E, c.k)
+    r = O.route(spec, host64(inp["x"]), host64(inp["w_router"]), host64(inp["logit_offset"]), bias_ref)
+    assert np.bincount(r["idx"].ravel(), minlength=c.E).max() > 2 * q  # skewed before balancing
+    for step in range(4):
+        print(f"[qb loop] step {step}", flush=True)
+        M.moe_route(cfg, inp["x"], inp["w_router"], inp["logit_offset"], bias, t["probs"], t["topk_idx"],
+                    t["topk_w"])
+        M.moe_bias_quantile(cfg, t["probs"], bias, t["ws"])
+        torch.cuda.synchronize()
+        r = O.route(spec, host64(inp["x"]), host64(inp["w_router"]), host64(inp["logit_offset"]), bias_ref)
+        np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), r["idx"])
+        bias_ref = O.bias_quantile(r["probs"], c.k, bias_ref)
+        np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32), bias_ref.astype(np.float32).view(np.uint32))
+    r = O.route(spec, host64(inp["x"]), host64(inp["w_router"]), host64(inp["logit_offset"]), bias_ref)
+    counts = np.bincount(r["idx"].ravel(), minlength=c.E)
+    assert np.all(np.abs(counts - q) <= 0.1 * q), counts
