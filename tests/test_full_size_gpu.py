@@ -29,6 +29,16 @@ from helpers import TOL_BF16, TOL_F32, cfg_of, host64, relerr, tol_for
 
 pytestmark = pytest.mark.gpu
 
+# the five workloads, plus the widened rows at full size: the GShard-shaped layer
+# under expert-choice routing (cf 2 -> every expert takes 512 of the 16384
+# tokens) and the DeepSeek-V3-shaped layer with the square-root-softplus gate
+# (whose bias steps, sign and quantile, are checked on the realised routing)
+FULL = {n: CONFIGS[n] for n in ORDER}
+FULL["gshard_top2_ec"] = CONFIGS["gshard_top2"].replace(name="gshard_top2_ec", routing="expert_choice", k=64,
+                                                        renorm=False, alpha=0.0)
+FULL["deepseek_v3_sqrt_softplus"] = CONFIGS["deepseek_v3"].replace(name="deepseek_v3_sqrt_softplus",
+                                                                   gate="sqrt_softplus_bias")
+
 
 def _expert_w(inp, e, shared=False):
     if shared:
@@ -36,9 +46,9 @@ def _expert_w(inp, e, shared=False):
     return host64(inp["w1"][e]), host64(inp["w2"][e])
 
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", list(FULL))
 def test_full_size(name):
-    c = CONFIGS[name]
+    c = FULL[name]
     print(f"\n[full size] {name}: T={c.T} d={c.d} f={c.f} E={c.E} k={c.k}", flush=True)
     torch.manual_seed(0)
     inp = make_inputs(c, seed=0, device="cuda")
@@ -54,7 +64,12 @@ def test_full_size(name):
     # ---- routing, every token
     x64 = host64(inp["x"])
     r = O.route(spec, x64, host64(inp["w_router"]), host64(inp.get("logit_offset")), host64(inp.get("sel_bias")))
-    np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), r["idx"])
+    if c.routing == "expert_choice":
+        # the experts compared these probabilities across tokens: bit for bit
+        np.testing.assert_array_equal(t["probs"].cpu().numpy().view(np.uint32),
+                                      r["probs"].astype(np.float32).view(np.uint32))
+    else:
+        np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), r["idx"])
     assert relerr(host64(t["probs"]), r["probs"]) <= TOL_F32
     assert relerr(host64(t["topk_w"]), r["w"]) <= TOL_F32
     np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), r["counts"])
@@ -65,6 +80,19 @@ def test_full_size(name):
     np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), r["row_token"][:n])
     if c.alpha:
         assert abs(float(t["aux"][0]) - r["aux"]) <= TOL_F32 * abs(r["aux"])
+    if spec.gate != O.GATE_SOFTMAX:
+        # both selection-bias steps on this batch: sign step from the counts, and
+        # Quantile Balancing from the gate values, bit for bit
+        b0 = inp["sel_bias"].clone()
+        bs = b0.clone()
+        M.moe_bias_update(cfg_of(c), t["expert_counts"], 1e-3, bs)
+        bq = b0.clone()
+        M.moe_bias_quantile(cfg_of(c), t["probs"], bq, t["ws"])
+        torch.cuda.synchronize()
+        ref_s = O.bias_update(r["counts"], 1e-3, host64(b0)).astype(np.float32)
+        ref_q = O.bias_quantile(r["probs"], c.k, host64(b0)).astype(np.float32)
+        np.testing.assert_array_equal(bs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+        np.testing.assert_array_equal(bq.cpu().numpy().view(np.uint32), ref_q.view(np.uint32))
     rows_per = np.diff(offs)
     print(f"  kept rows {n} / {c.T * c.k}; max/mean load {rows_per.max() / max(rows_per.mean(), 1e-9):.2f}; "
           f"empty experts {int((rows_per == 0).sum())}", flush=True)
