@@ -118,7 +118,9 @@ def stage_work(c, rows, ne_experts):
         "bwd_dgrad1": (2 * R * f1 * d, W1 + R * f1 * eb + R * d * eb),
         "bwd_wgrad1": (2 * R * f1 * d, W1all + R * f1 * eb + R * d * eb),
         "bwd_dlogits": (0, T * E * 8 + T * k * 12),
-        "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 + T * d * 4),
+        # bf16 with k <= 2: the dx_router product's epilogue also does the unpermute pass
+        "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 +
+                             (T * d * eb * 2 + rows * d * eb if (eb == 2 and k <= 2) else T * d * 4)),
         "bwd_unpermute": (0, T * d * eb * 2 + rows * d * eb + T * d * 4),
         "bias_update": (0, E * 4 * 3),
         # gate values read twice (cuts, margins), margins written and read twice (two selects)

@@ -435,14 +435,18 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
     StageTimer pt("bwd_dlogits", s);
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;
   }
+  // bf16 layers with one or two experts per token finish dx in the router
+  // product's epilogue (with more, the epilogue's gather of k rows per token has
+  // too few loads in flight and the separate pass is faster)
+  const bool fuse_dx = c->dtype == MOE_DT_BF16 && k <= 2;
   moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, (uint16_t*)(base + L.gx),
                          (uint16_t*)(base + L.gw), (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs), T, d, E,
-                         c->dtype};
+                         c->dtype, dy, sv->slot, k, dXp, dX_sh, fuse_dx ? g->dx : nullptr};
   {
     StageTimer pt("bwd_router_grads", s);
     if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;
   }
-  if (T > 0) {
+  if (T > 0 && !fuse_dx) {
     moe::UnpermuteArgs ua{dy, dXp, sv->slot, dxr, dX_sh, g->dx, T, d, k, c->dtype};
     StageTimer pt("bwd_unpermute", s);
     if ((st = launch_status(moe::launch_unpermute_bwd(ua, s)))) return st;

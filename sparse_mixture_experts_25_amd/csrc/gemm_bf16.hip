@@ -508,6 +508,27 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = xs[e] > 0.0f ? v[e] : 0.0f;
           st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+        } else if (EPI == EPI_UNPERMUTE) {
+          // same order as the separate pass: dy, kept expert rows in r order,
+          // router term, shared expert
+          const uint16_t* Yp = reinterpret_cast<const uint16_t*>(a.Y);
+          float o[8], tmp[8];
+          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), o);
+          for (int r = 0; r < a.slot_k; ++r) {
+            const int sl = a.slot[row * a.slot_k + r];
+            if (sl < 0) continue;
+            Elem<uint16_t>::unpack(ld128(Yp + (int64_t)sl * a.N + col), tmp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += v[e];
+          if (a.Y_sh) {
+            Elem<uint16_t>::unpack(ld128(reinterpret_cast<const uint16_t*>(a.Y_sh) + row * a.N + col), tmp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+          }
+          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(o));
         } else if (EPI == EPI_SWIGLU_BWD) {
           float gs[8], us[8], dg[8], du[8];
           Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), gs);
@@ -568,6 +589,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
     case EPI_RELU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_RELU_BWD, WGN>(a, st);
     case EPI_SWIGLU_BWD: return launch_t<BM, BN, BK, NS, 0, 0, EPI_SWIGLU_BWD, WGN>(a, st);
     case EPI_STORE_F32: return launch_t<BM, BN, BK, NS, 0, 0, EPI_STORE_F32, WGN>(a, st);
+    case EPI_UNPERMUTE: return launch_t<BM, BN, BK, NS, 0, 0, EPI_UNPERMUTE, WGN>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -611,7 +633,10 @@ hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, in
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
-  const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256));
+  // 256x256 tiles also need enough of them to give every CU a workgroup
+  const int64_t big_tiles = a.kind == 0 ? ((a.max_rows + 255) / 256) * ((a.N + 255) / 256)
+                                        : (groups + (a.has_shared ? 1 : 0)) * ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) && big_tiles >= 256;
   if (big) return launch_tiles<256, 256, 32, 3, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
   if (a.kind == 1)

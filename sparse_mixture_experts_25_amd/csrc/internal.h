@@ -72,6 +72,10 @@ enum GemmEpi {
   EPI_RELU_BWD = 3,    // C = acc * (X > 0)
   EPI_SWIGLU_BWD = 4,  // acc = dh; X = saved [gate | up]; C = [d gate | d up]
   EPI_STORE_F32 = 5,   // C (fp32) = acc (ragged-M, B MN-contiguous)
+  // C = X + sum over r < slot_k with slot[row, r] >= 0 of Y[slot] + acc (+ Y_sh):
+  // the input gradient of the layer (dy + expert input gradients + router
+  // term + shared expert), rows = tokens (ragged-M, one group, B MN-contiguous)
+  EPI_UNPERMUTE = 6,
 };
 
 struct GemmArgs {
@@ -92,6 +96,7 @@ struct GemmArgs {
   void* C2; int64_t ldc2; void* C2_sh;
   const void* X; int64_t ldx; const void* X_sh;
   int f;  // SwiGLU half width
+  const int32_t* slot; int slot_k; const void* Y; const void* Y_sh;  // EPI_UNPERMUTE
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // order[0..E(+1)): groups sorted by row count, largest first (ties: lower index;
@@ -158,6 +163,10 @@ struct RouterGradArgs {
   uint16_t* wsplit;      // bf16 [router_dx_k(E), d] split router weights (bf16 layers)
   int32_t* offs;         // [2 + router_dw_splits + 1] row ranges of the dx group and the dW chunks
   int T, d, E, dtype;
+  // bf16 layers with k <= 2: the dx_router product also finishes the input
+  // gradient, dx = dy + sum_kept dX_perm[slot] + dx_router (+ dx_shared), and
+  // dx_router is not stored (dx non-null selects this)
+  const void* dy; const int32_t* slot; int k; const void* dX_perm; const void* dX_sh; void* dx;
 };
 // width of the split operands: 3E rounded up to 8
 inline int router_dx_k(int E) { return (3 * E + 7) / 8 * 8; }

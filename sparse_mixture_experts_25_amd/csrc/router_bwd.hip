@@ -113,16 +113,30 @@ __global__ __launch_bounds__(256) void router_dw_sum_kernel(const float* __restr
 
 }  // namespace
 
-// About 512 workgroups of 256x256 tiles, with the fp32 partials capped at
-// 128 MB and chunks of at least 256 tokens.
+// Token chunks of dW_r. Every chunk writes a kp x d fp32 partial that the
+// sum kernel reads back, so chunks are as few as keep the CUs busy:
+//  - large products (at least 512 workgroups' worth of 256x256 tiles over
+//    256-token chunks): about 512 workgroups of 256x256 tiles, partials capped
+//    at 128 MB, chunks of at least 2048 tokens (fine-grained top-8 shape: 16
+//    chunks; DeepSeek-V3 shape: 5);
+//  - small products: 128x128 tiles (the matmul picks them when 256x256 tiles
+//    would leave CUs idle), about 256 workgroups, chunks of at least 1024 tokens.
 int router_dw_splits(int T, int E, int d) {
   const int64_t kp = router_dx_k(E);
-  const int64_t tiles = ((kp + 255) / 256) * (((int64_t)d + 255) / 256);
-  int64_t ns = (512 + tiles - 1) / tiles;
-  const int64_t mem = (int64_t(128) << 20) / (kp * (int64_t)d * 4 > 0 ? kp * (int64_t)d * 4 : 1);
-  if (ns > mem) ns = mem;
-  const int64_t by_t = ((int64_t)T + 255) / 256;
-  if (ns > by_t) ns = by_t;
+  const int64_t big_tiles = ((kp + 255) / 256) * (((int64_t)d + 255) / 256);
+  int64_t ns;
+  if (big_tiles * (((int64_t)T + 255) / 256) >= 512) {
+    ns = (512 + big_tiles - 1) / big_tiles;
+    const int64_t mem = (int64_t(128) << 20) / (kp * (int64_t)d * 4 > 0 ? kp * (int64_t)d * 4 : 1);
+    if (ns > mem) ns = mem;
+    const int64_t by_t = (int64_t)T / 2048;
+    if (ns > by_t) ns = by_t;
+  } else {
+    const int64_t tiles = ((kp + 127) / 128) * (((int64_t)d + 127) / 128);
+    ns = (256 + tiles - 1) / tiles;
+    const int64_t by_t = (int64_t)T / 1024;
+    if (ns > by_t) ns = by_t;
+  }
   return (int)(ns < 1 ? 1 : ns);
 }
 
@@ -167,14 +181,17 @@ hipError_t launch_router_dw_gemm(const RouterGradArgs& a, hipStream_t st) {
 }
 
 // dx_r on the grouped matmul: one ragged-M group of T rows, K = Kp, N = d,
-// B MN-contiguous, fp32 output. Needs the split operands of
-// launch_router_dw_gemm (same stream, launched before).
+// B MN-contiguous. Either an fp32 dx_router, or (a.dx set) the layer's input
+// gradient dx = dy + sum_kept dX_perm[slot] + dx_r (+ dx_shared) in the
+// epilogue, in the order of the separate unpermute pass, so dx_r never goes to
+// memory. Needs the split operands of launch_router_dw_gemm (same stream,
+// launched before).
 hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int kp = router_dx_k(a.E);
   GemmArgs g{};
   g.kind = 0;
-  g.epi = EPI_STORE_F32;
+  g.epi = a.dx ? EPI_UNPERMUTE : EPI_STORE_F32;
   g.b_kcontig = 0;
   g.M = a.T;
   g.N = a.d;
@@ -187,8 +204,16 @@ hipError_t launch_router_dx_gemm(const RouterGradArgs& a, hipStream_t st) {
   g.lda = kp;
   g.B = a.wsplit;
   g.ldb = a.d;
-  g.C = a.dx_router;
+  g.C = a.dx ? a.dx : a.dx_router;
   g.ldc = a.d;
+  if (a.dx) {
+    g.X = a.dy;
+    g.ldx = a.d;
+    g.slot = a.slot;
+    g.slot_k = a.k;
+    g.Y = a.dX_perm;
+    g.Y_sh = a.dX_sh;
+  }
   return launch_gemm_bf16(g, st);
 }
 

@@ -110,24 +110,38 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   }
 }
 
-__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ partial, int nblk,
-                                                        const int32_t* __restrict__ counts, int T, int E,
-                                                        int k, float alpha, float* __restrict__ out) {
-  __shared__ float red[4];
+// aux = alpha * E * sum_e f_e P_e. Each expert's column of block partials is
+// summed by `parts` threads (strided over the blocks), then the parts in order,
+// then the experts by a fixed tree: many short sums instead of E long ones.
+constexpr int kAuxFin = 1024;
+__global__ __launch_bounds__(kAuxFin) void aux_final_kernel(const float* __restrict__ partial, int nblk,
+                                                            const int32_t* __restrict__ counts, int T, int E,
+                                                            int k, float alpha, float* __restrict__ out) {
+  __shared__ float part_sum[kAuxFin];
+  __shared__ float red[kAuxFin / 64];
+  const int tid = threadIdx.x;
+  const int parts = kAuxFin / E;  // >= 2 (E <= 512)
+  if (tid < parts * E) {
+    const int e = tid % E, p = tid / E;
+    float s = 0.0f;
+    for (int b = p; b < nblk; b += parts) s += partial[(int64_t)b * E + e];
+    part_sum[tid] = s;
+  }
+  __syncthreads();
   float acc = 0.0f;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  if (tid < E) {
     float P = 0.0f;
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) P += partial[(int64_t)b * E + e];
+    for (int p = 0; p < parts; ++p) P += part_sum[p * E + tid];
     P /= (float)T;
-    const float f = (float)counts[e] / ((float)T * (float)k);
-    acc += f * P;
+    const float f = (float)counts[tid] / ((float)T * (float)k);
+    acc = f * P;
   }
   acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) {
+    float s = 0.0f;
+    for (int w = 0; w < kAuxFin / 64; ++w) s += red[w];
     out[0] = (T == 0 || alpha == 0.0f) ? 0.0f : alpha * (float)E * s;
   }
 }
@@ -413,7 +427,7 @@ hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
   const int nblk = (a.alpha == 0.0f) ? 0 : aux_num_blocks(a.T);
   if (nblk > 0)
     hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, st, a.probs, a.T, a.E, a.ws_partial);
-  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, st, a.ws_partial, nblk, a.counts, a.T, a.E, a.k,
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kAuxFin), 0, st, a.ws_partial, nblk, a.counts, a.T, a.E, a.k,
                      a.alpha, a.aux_out);
   return hipGetLastError();
 }
