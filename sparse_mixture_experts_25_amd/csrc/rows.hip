@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kAuxFin) void aux_final_kernel(const float* __restr
   if (tid < parts * E) {
     const int e = tid % E, p = tid / E;
     float s = 0.0f;
+#pragma unroll 8
     for (int b = p; b < nblk; b += parts) s += partial[(int64_t)b * E + e];
     part_sum[tid] = s;
   }
