@@ -35,9 +35,9 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.cpp")
 
 MODE_EXACT, MODE_F32, MODE_BF16 = 0, 1, 2
-GATE_SOFTMAX, GATE_SIGMOID_BIAS, GATE_SQRT_SOFTPLUS_BIAS = 0, 1, 2
+GATE_SOFTMAX, GATE_SIGMOID_BIAS, GATE_SQRT_SOFTPLUS_BIAS, GATE_NOISY_TOPK = 0, 1, 2, 3
 GATE_OF = {"softmax": GATE_SOFTMAX, "sigmoid_bias": GATE_SIGMOID_BIAS,
-           "sqrt_softplus_bias": GATE_SQRT_SOFTPLUS_BIAS}
+           "sqrt_softplus_bias": GATE_SQRT_SOFTPLUS_BIAS, "noisy_topk": GATE_NOISY_TOPK}
 ACT_RELU, ACT_SWIGLU = 0, 1
 
 _lib = None
@@ -71,6 +71,10 @@ def lib():
             "orc_gate_deriv": (d, [i, d]),
             "orc_bias_update": (None, [i, I, d, D, D]),
             "orc_bias_quantile": (None, [i, i, i, D, D, D]),
+            "orc_softplus_contract": (ctypes.c_float, [ctypes.c_float]),
+            "orc_noisy_logits": (None, [i, i, i, D, D, D]),
+            "orc_noisy_aux": (d, [i, i, i, i, D, D, I, D, d, D, D]),
+            "orc_noisy_dlogits": (None, [i, i, i, i, D, D, I, D, D, d, D]),
             "qb_target": (i, [i, i, i]),
             "orc_capacity": (i, [i, i, d]),
             "orc_logits": (None, [i, i, i, i, D, D, D, D]),
@@ -164,6 +168,36 @@ def bias_quantile(probs, k: int, bias):
     b = f64(bias)
     out = np.empty_like(b)
     lib().orc_bias_quantile(T, E, int(k), _d(p), _d(b), _d(out))
+    return out
+
+
+def softplus_contract(x: float) -> float:
+    return lib().orc_softplus_contract(float(x))
+
+
+def noisy_logits(mode, logits2, eps):
+    """H = h + eps * softplus(n) from the stacked [T, 2E] clean|noise logits."""
+    T, E2 = logits2.shape
+    H = np.empty((T, E2 // 2))
+    lib().orc_noisy_logits(mode, T, E2 // 2, _d(f64(logits2)), _d(f64(eps)), _d(H))
+    return H
+
+
+def noisy_aux(mode, logits2, eps, idx, w, alpha):
+    """(alpha (CV^2(importance) + CV^2(load)), importance [E], load [E])."""
+    T, E2 = logits2.shape
+    E, k = E2 // 2, idx.shape[1]
+    imp, load = np.empty(E), np.empty(E)
+    aux = lib().orc_noisy_aux(mode, T, E, k, _d(f64(logits2)), _d(f64(eps)), _i(np.ascontiguousarray(idx, np.int32)),
+                              _d(f64(w)), float(alpha), _d(imp), _d(load))
+    return aux, imp, load
+
+
+def noisy_dlogits(mode, logits2, eps, idx, w, dg, alpha):
+    T, E2 = logits2.shape
+    out = np.empty((T, E2))
+    lib().orc_noisy_dlogits(mode, T, E2 // 2, idx.shape[1], _d(f64(logits2)), _d(f64(eps)),
+                            _i(np.ascontiguousarray(idx, np.int32)), _d(f64(w)), _d(f64(dg)), float(alpha), _d(out))
     return out
 
 
@@ -351,7 +385,20 @@ class Spec:
                     getattr(cfg, "routing", "token_choice") == "expert_choice")
 
 
-def route(spec: Spec, x, w_router, logit_offset=None, sel_bias=None):
+def route(spec: Spec, x, w_router, logit_offset=None, sel_bias=None, noise=None):
+    if spec.gate == GATE_NOISY_TOPK:
+        # stacked router [W_g; W_noise] -> clean|noise logits; softmax over the top-k of H
+        assert w_router.shape[0] == 2 * spec.E and logit_offset is None and spec.renorm
+        h2 = logits(spec.mode, x, w_router)
+        H = noisy_logits(spec.mode, h2, noise)
+        probs, idx, w = gate_topk(spec.mode, H, spec.k, GATE_SOFTMAX, True)
+        C = capacity(spec.T, spec.E, spec.cf)
+        counts, offsets, slot, row_token = positions(idx, spec.E, C)
+        aux = noisy_aux(spec.mode, h2, noise, idx, w, spec.alpha)[0] if spec.alpha else 0.0
+        if spec.mode != MODE_EXACT:
+            aux = float(np.float32(aux))
+        return dict(h=H, logits2=h2, probs=probs, idx=idx, w=w, C=C, counts=counts, offsets=offsets,
+                    slot=slot, row_token=row_token, aux=aux)
     h = logits(spec.mode, x, w_router, logit_offset)
     if spec.expert_choice:
         # the token tables have one column per expert (k = E); idx is the identity
@@ -373,7 +420,7 @@ def route(spec: Spec, x, w_router, logit_offset=None, sel_bias=None):
 def forward(spec: Spec, inp: dict) -> dict:
     """Full forward. ``inp`` holds float64 arrays: x, w_router, w1, w2 and the optional
     logit_offset, sel_bias, ws1, ws2."""
-    r = route(spec, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"))
+    r = route(spec, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"), inp.get("noise"))
     n = int(r["offsets"][-1])
     f1 = 2 * spec.f if spec.act == ACT_SWIGLU else spec.f
     x_perm = inp["x"][r["row_token"][:n]] if n else np.zeros((0, spec.d))
@@ -422,8 +469,11 @@ def backward(spec: Spec, inp: dict, saved: dict, dy: np.ndarray) -> dict:
         out["dws1"] = wgrad(spec.mode, dA_s, inp["x"])
         out["dA_shared"], out["dx_shared"] = dA_s, dX_s
         dx_shared = dX_s
-    dl = router_dlogits(saved["probs"], saved["idx"], saved["w"], dg, saved["counts"],
-                        spec.gate, spec.renorm, spec.alpha)
+    if spec.gate == GATE_NOISY_TOPK:
+        dl = noisy_dlogits(spec.mode, saved["logits2"], inp["noise"], saved["idx"], saved["w"], dg, spec.alpha)
+    else:
+        dl = router_dlogits(saved["probs"], saved["idx"], saved["w"], dg, saved["counts"],
+                            spec.gate, spec.renorm, spec.alpha)
     dWr, dxr = router_grads(spec.mode, dl, inp["x"], inp["w_router"])
     out.update(dlogits=dl, dw_router=dWr, dx_router=dxr)
     out["dx"] = unpermute_bwd(spec.mode, dy, dX_perm, saved["slot"], dxr, dx_shared)

@@ -145,6 +145,16 @@ float sqrt_softplus_c(float h) {
   return std::sqrt(sp);
 }
 
+// softplus(v) = log(1 + e^v) in the same fixed fp32 operations as the
+// square-root-softplus gate (without the square root).
+float softplus_c(float v) {
+  const float u = exp_c(-std::fabs(v));
+  return (v > 0.0f ? v : 0.0f) + log1p_c(u);
+}
+
+double softplus_d(double v) { return std::max(v, 0.0) + std::log1p(std::exp(-std::fabs(v))); }
+double sigmoid_d(double v) { return 1.0 / (1.0 + std::exp(-v)); }
+
 // The gate's derivative written with the gate value s = g(h) (the backward
 // only has the saved gate values):
 //   sigmoid:            s (1 - s)
@@ -170,6 +180,7 @@ void orc_round_array(int mode, int64_t n, const double* in, double* out) {
 float orc_exp_contract(float x) { return exp_c(x); }
 float orc_sigmoid_contract(float x) { return sigmoid_c(x); }
 float orc_log1p_contract(float x) { return log1p_c(x); }
+float orc_softplus_contract(float x) { return softplus_c(x); }
 float orc_sqrt_softplus_contract(float x) { return sqrt_softplus_c(x); }
 double orc_gate_deriv(int gate, double s) { return gate_deriv(gate, s); }
 
@@ -663,6 +674,161 @@ void orc_bias_quantile(int T, int E, int k, const double* probs, const double* b
     const float sum = col[q - 1] + col[q];
     const float half = sum * 0.5f;
     bias_out[j] = (double)((float)bias_in[j] - half);
+  }
+}
+
+// ---------------------------------------------------------------- noisy top-k gating
+// [WIKI] (cross-cutting findings on Shazeer et al. 2017): top-k sparse gating
+// with noisy softmax, trained with an importance loss (dispersion of each
+// expert's summed softmax weight) and a load loss (dispersion of a smoothed
+// load estimate); total loss = main loss + alpha (importance + load). The page
+// names these but does not print them; they are written out here as that
+// paper defines them:
+//   clean logits h = W_g x and noise logits n = W_noise x (one router matrix of
+//   2E rows: h = rows 0..E-1, n = rows E..2E-1); eps ~ N(0, 1) is an input;
+//   H = h + eps * softplus(n);
+//   gate: softmax over the top-k of H (the softmax gate on H, renormalised);
+//   Importance_e = sum_t G[t, e];  L_imp = CV(Importance)^2;
+//   Load_e = sum_t Phi((h[t, e] - r[t, e]) / softplus(n[t, e])), where r[t, e]
+//   is the k-th largest H[t, :] with e left out (the (k+1)-th key if e is
+//   selected, the k-th otherwise); L_load = CV(Load)^2;
+//   aux = alpha (L_imp + L_load); CV(v)^2 = population variance / mean^2
+//   (0 for a zero mean).
+// H is formed in fp32 as one multiply and one add with softplus_c (the routing
+// decision depends on it); the losses and gradients are plain double math on
+// those stored values, with the selection and the rivals taken from the fp32 H.
+// Mode 0 keeps H in double.
+void orc_noisy_logits(int mode, int T, int E, const double* logits2, const double* eps, double* H) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      const double h = logits2[(size_t)t * 2 * E + e], n = logits2[(size_t)t * 2 * E + E + e];
+      const double ep = eps[(size_t)t * E + e];
+      if (mode == MODE_EXACT) {
+        H[(size_t)t * E + e] = h + ep * softplus_d(n);
+      } else {
+        const float sp = softplus_c((float)n);
+        const float prod = (float)ep * sp;
+        H[(size_t)t * E + e] = (double)((float)h + prod);
+      }
+    }
+}
+
+// per token: selected set (first k of H desc, index asc), the k-th and (k+1)-th
+// expert; rival[e] = index whose H is the k-th largest with e left out
+static void noisy_rivals(int E, int k, const double* Ht, std::vector<int>& rival, std::vector<char>& sel) {
+  std::vector<int> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int a, int b) {
+    if (Ht[a] != Ht[b]) return Ht[a] > Ht[b];
+    return a < b;
+  });
+  sel.assign(E, 0);
+  for (int r = 0; r < k; ++r) sel[order[r]] = 1;
+  rival.assign(E, -1);
+  for (int e = 0; e < E; ++e) rival[e] = sel[e] ? (k < E ? order[k] : -1) : order[k - 1];
+}
+
+static double cv2(const std::vector<double>& v) {
+  const int n = (int)v.size();
+  double mean = 0.0;
+  for (double x : v) mean += x;
+  mean /= n;
+  if (mean == 0.0) return 0.0;
+  double var = 0.0;
+  for (double x : v) var += (x - mean) * (x - mean);
+  var /= n;
+  return var / (mean * mean);
+}
+// d CV^2 / d v_e = 2 / (n mean^2) * (v_e - mean - var / mean)
+static void cv2_grad(const std::vector<double>& v, std::vector<double>& g) {
+  const int n = (int)v.size();
+  double mean = 0.0;
+  for (double x : v) mean += x;
+  mean /= n;
+  g.assign(n, 0.0);
+  if (mean == 0.0) return;
+  double var = 0.0;
+  for (double x : v) var += (x - mean) * (x - mean);
+  var /= n;
+  for (int e = 0; e < n; ++e) g[e] = 2.0 / (n * mean * mean) * (v[e] - mean - var / mean);
+}
+
+static double phi_cdf(double z) { return 0.5 * std::erfc(-z / std::sqrt(2.0)); }
+static double phi_pdf(double z) { return std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI); }
+
+// Importance and load (per expert) of a batch; returns aux = alpha (CV^2 + CV^2).
+double orc_noisy_aux(int mode, int T, int E, int k, const double* logits2, const double* eps, const int* idx,
+                     const double* w, double alpha, double* imp_out, double* load_out) {
+  std::vector<double> H((size_t)T * E);
+  orc_noisy_logits(mode, T, E, logits2, eps, H.data());
+  std::vector<double> imp(E, 0.0), load(E, 0.0);
+  std::vector<int> rival;
+  std::vector<char> sel;
+  for (int t = 0; t < T; ++t) {
+    for (int r = 0; r < k; ++r) imp[idx[(size_t)t * k + r]] += w[(size_t)t * k + r];
+    if (k >= E) continue;  // every expert always taken: no rival, load term constant
+    noisy_rivals(E, k, &H[(size_t)t * E], rival, sel);
+    for (int e = 0; e < E; ++e) {
+      const double h = logits2[(size_t)t * 2 * E + e], n = logits2[(size_t)t * 2 * E + E + e];
+      const double z = (h - H[(size_t)t * E + rival[e]]) / softplus_d(n);
+      load[e] += phi_cdf(z);
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    if (imp_out) imp_out[e] = imp[e];
+    if (load_out) load_out[e] = load[e];
+  }
+  if (alpha == 0.0 || T == 0) return 0.0;
+  return alpha * (cv2(imp) + (k >= E ? 0.0 : cv2(load)));
+}
+
+// Gradient of L = sum <dy, y> + aux with respect to the clean and noise logits,
+// dlogits2 [T, 2E] = [dL/dh | dL/dn], from the gate gradient dg[t, r] = dL/dw[t, r]:
+//   gate path: the softmax-over-top-k Jacobian on H with dg plus the importance
+//   term alpha dCV^2/dImportance_e, then dH/dh = 1, dH/dn = eps sigmoid(n);
+//   load path: for every (t, e), c = alpha dCV^2/dLoad_e phi(z) / softplus(n_e)
+//   goes to h_e (+c), n_e (-c z sigmoid(n_e)) and to the rival j
+//   (h_j: -c, n_j: -c eps_j sigmoid(n_j)).
+void orc_noisy_dlogits(int mode, int T, int E, int k, const double* logits2, const double* eps, const int* idx,
+                       const double* w, const double* dg, double alpha, double* dlogits2) {
+  std::vector<double> imp(E), load(E), gimp, gload;
+  orc_noisy_aux(mode, T, E, k, logits2, eps, idx, w, alpha, imp.data(), load.data());
+  cv2_grad(imp, gimp);
+  cv2_grad(load, gload);
+  std::vector<double> H((size_t)T * E);
+  orc_noisy_logits(mode, T, E, logits2, eps, H.data());
+  std::vector<int> rival;
+  std::vector<char> sel;
+  for (int t = 0; t < T; ++t) {
+    double* oh = dlogits2 + (size_t)t * 2 * E;
+    double* on = oh + E;
+    for (int j = 0; j < 2 * E; ++j) oh[j] = 0.0;
+    const double* lh = logits2 + (size_t)t * 2 * E;
+    const double* ln = lh + E;
+    const double* ep = eps + (size_t)t * E;
+    std::vector<double> dH(E, 0.0), gr(k);
+    double sdot = 0.0;
+    for (int r = 0; r < k; ++r) {
+      gr[r] = dg[(size_t)t * k + r] + alpha * gimp[idx[(size_t)t * k + r]];
+      sdot += w[(size_t)t * k + r] * gr[r];
+    }
+    for (int r = 0; r < k; ++r) dH[idx[(size_t)t * k + r]] += w[(size_t)t * k + r] * (gr[r] - sdot);
+    for (int e = 0; e < E; ++e) {
+      oh[e] += dH[e];
+      on[e] += dH[e] * ep[e] * sigmoid_d(ln[e]);
+    }
+    if (alpha == 0.0 || k >= E) continue;
+    noisy_rivals(E, k, &H[(size_t)t * E], rival, sel);
+    for (int e = 0; e < E; ++e) {
+      const double sp = softplus_d(ln[e]);
+      const int j = rival[e];
+      const double z = (lh[e] - H[(size_t)t * E + j]) / sp;
+      const double c = alpha * gload[e] * phi_pdf(z) / sp;
+      oh[e] += c;
+      on[e] += -c * z * sigmoid_d(ln[e]);
+      oh[j] -= c;
+      on[j] -= c * ep[j] * sigmoid_d(ln[j]);
+    }
   }
 }
 

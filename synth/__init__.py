@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 # tensor ids
-TID_X, TID_WR, TID_W1, TID_W2, TID_BIAS, TID_DY, TID_SHARED = 1, 2, 3, 4, 5, 6, 7
+TID_X, TID_WR, TID_W1, TID_W2, TID_BIAS, TID_DY, TID_SHARED, TID_NOISE = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -33,7 +33,7 @@ class LayerConfig:
     f: int                 # expert hidden width (per half for SwiGLU)
     E: int                 # routed experts
     k: int                 # experts per token
-    gate: str = "softmax"  # "softmax" | "sigmoid_bias" | "sqrt_softplus_bias"
+    gate: str = "softmax"  # "softmax" | "sigmoid_bias" | "sqrt_softplus_bias" | "noisy_topk"
     renorm: bool = False   # renormalise the k selected weights
     act: str = "relu"      # "relu" | "swiglu"
     dtype: str = "bf16"    # activations / expert weights: "bf16" | "f32"
@@ -114,7 +114,8 @@ def _truncnormal(shape, std, g, device):
 def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", with_dy: bool = True) -> dict:
     """Draw every input tensor of one layer call.
 
-    x ~ N(0,1); expert weights ~ N(0, 1/fan_in); W_r ~ N(0, 1/d) except the tiny
+    x ~ N(0,1); expert weights ~ N(0, 1/fan_in); W_r ~ N(0, 1/d) (2E rows, clean and
+    noise, for noisy top-k gating, whose noise eps ~ N(0,1) is drawn too) except the tiny
     workload's truncated N(0, (0.1/sqrt(d))^2) (the Switch 0.1x init scale);
     logit offsets ~ N(0,1) ("normal") or -1.1*ln(e+1) ("logzipf", Zipf s=1.1
     popularity with expert 0 the most popular); selection bias ~ U(-0.5, 0.5);
@@ -129,10 +130,13 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu", with_dy: bool = T
     big = dev.type != "cpu"
     out = {}
     out["x"] = _normal((T, d), 1.0, _gen(seed, TID_X, dev), dev).to(act_dt)
+    ER = 2 * E if cfg.gate == "noisy_topk" else E  # noisy gating stacks [W_g; W_noise]
     if cfg.router_init == "truncnormal_small":
-        out["w_router"] = _truncnormal((E, d), 0.1 / math.sqrt(d), _gen(seed, TID_WR, dev), dev)
+        out["w_router"] = _truncnormal((ER, d), 0.1 / math.sqrt(d), _gen(seed, TID_WR, dev), dev)
     else:
-        out["w_router"] = _normal((E, d), 1.0 / math.sqrt(d), _gen(seed, TID_WR, dev), dev)
+        out["w_router"] = _normal((ER, d), 1.0 / math.sqrt(d), _gen(seed, TID_WR, dev), dev)
+    if cfg.gate == "noisy_topk":
+        out["noise"] = _normal((T, E), 1.0, _gen(seed, TID_NOISE, dev), dev)
     g1 = _gen(seed, TID_W1, dev)
     g2 = _gen(seed, TID_W2, dev)
     w1 = torch.empty((E, f1, d), dtype=act_dt, device=dev)

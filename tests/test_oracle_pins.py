@@ -308,6 +308,82 @@ def test_bias_quantile_closed_loop_balances():
     assert np.all(np.abs(c - q) <= 0.05 * q), c
 
 
+# ----------------------------------------------------------------- noisy top-k gating
+
+def test_softplus_contract_close_to_definition():
+    for x in np.concatenate([np.linspace(-40, 40, 16001), np.linspace(-1, 1, 4001)]).astype(np.float32):
+        got = O.softplus_contract(float(x))
+        true = max(float(x), 0.0) + math.log1p(math.exp(-abs(float(x))))
+        assert abs(got - true) <= 3 * float(np.spacing(np.float32(true))) + 1e-45, (x, got, true)
+    assert O.softplus_contract(100.0) == 100.0 and O.softplus_contract(-100.0) == 0.0
+
+
+def _noisy_case(T=40, E=6, k=2, seed=0, noise_shift=0.0):
+    rng = np.random.default_rng(seed)
+    h2 = (rng.standard_normal((T, 2 * E)) * 1.5).astype(np.float32).astype(np.float64)
+    h2[:, E:] += noise_shift
+    eps = rng.standard_normal((T, E)).astype(np.float32).astype(np.float64)
+    return h2, eps
+
+
+def test_noisy_gate_without_noise_is_renormalised_softmax():
+    h2, eps = _noisy_case()
+    E = 6
+    H = O.noisy_logits(O.MODE_F32, h2, np.zeros_like(eps))
+    np.testing.assert_array_equal(H, h2[:, :E])
+    # H = h + eps * softplus_c(n) with one fp32 multiply and one fp32 add
+    H = O.noisy_logits(O.MODE_F32, h2, eps)
+    f = np.float32
+    for t in range(5):
+        for e in range(E):
+            sp = f(O.softplus_contract(float(h2[t, E + e])))
+            assert H[t, e] == f(f(h2[t, e]) + f(f(eps[t, e]) * sp))
+
+
+def _load_bruteforce(h2, eps, k, H):
+    T, E = eps.shape
+    load = np.zeros(E)
+    for t in range(T):
+        for e in range(E):
+            rest = np.delete(H[t], e)
+            rival = np.sort(rest)[::-1][k - 1]          # k-th largest with e left out
+            sp = max(h2[t, E + e], 0) + math.log1p(math.exp(-abs(h2[t, E + e])))
+            load[e] += 0.5 * math.erfc(-((h2[t, e] - rival) / sp) / math.sqrt(2))
+    return load
+
+
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_noisy_load_rival_is_kth_largest_excluding(k):
+    h2, eps = _noisy_case(T=30, E=6, seed=k)
+    H = O.noisy_logits(O.MODE_F32, h2, eps)
+    _, idx, w = O.gate_topk(O.MODE_F32, H, k, O.GATE_SOFTMAX, True)
+    aux, imp, load = O.noisy_aux(O.MODE_F32, h2, eps, idx, w, 1.0)
+    np.testing.assert_allclose(load, _load_bruteforce(h2, eps, k, H), rtol=1e-12, atol=1e-12)
+    # importance = column sums of the gates; the losses are CV^2 (variance over mean^2)
+    np.testing.assert_allclose(imp, np.bincount(idx.ravel(), weights=w.ravel(), minlength=6), rtol=1e-12)
+    cv2 = lambda v: np.var(v) / np.mean(v) ** 2
+    assert aux == pytest.approx(cv2(imp) + cv2(load), rel=1e-12)
+
+
+def test_noisy_load_without_noise_scale_counts_assignments():
+    # softplus(n) -> 0 makes each smoothed term a step: the load becomes the hard counts
+    h2, eps = _noisy_case(T=200, E=8, k=2, seed=7, noise_shift=-80.0)
+    H = O.noisy_logits(O.MODE_EXACT, h2, eps)
+    _, idx, w = O.gate_topk(O.MODE_EXACT, H, 2, O.GATE_SOFTMAX, True)
+    _, imp, load = O.noisy_aux(O.MODE_EXACT, h2, eps, idx, w, 1.0)
+    np.testing.assert_array_equal(load, np.bincount(idx.ravel(), minlength=8).astype(np.float64))
+
+
+def test_noisy_importance_loss_zero_when_balanced():
+    # every token splits its weight evenly over the experts in turn: equal importance
+    T, E, k = 8, 4, 2
+    idx = np.array([[t % E, (t + 1) % E] for t in range(T)], np.int32)
+    w = np.full((T, k), 0.5)
+    h2, eps = _noisy_case(T=T, E=E, k=k)
+    _, imp, _ = O.noisy_aux(O.MODE_EXACT, h2, eps, idx, w, 1.0)
+    np.testing.assert_allclose(imp, np.full(E, 2.0))
+
+
 # ----------------------------------------------------------------- expert-choice routing
 
 def test_softmax_ec_contract():
@@ -612,6 +688,8 @@ FD_CASES = [
     dict(E=4, k=2, gate="sqrt_softplus_bias", renorm=True, act="swiglu", cf=0.0, alpha=0.3, shared=1,
          sel_bias="uniform"),
     dict(E=4, k=1, gate="sqrt_softplus_bias", renorm=False, act="relu", cf=0.5, alpha=0.3, sel_bias="uniform"),
+    dict(E=4, k=2, gate="noisy_topk", renorm=True, act="swiglu", cf=0.0, alpha=0.5),
+    dict(E=5, k=1, gate="noisy_topk", renorm=True, act="relu", cf=0.75, alpha=0.5, shared=1),
     dict(E=4, k=4, gate="softmax", renorm=False, act="swiglu", cf=1.0, routing="expert_choice"),
     dict(E=4, k=4, gate="softmax", renorm=False, act="relu", cf=0.5, shared=1, routing="expert_choice"),
 ]
