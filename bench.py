@@ -95,6 +95,7 @@ def stage_work(c, rows, ne_experts):
     """Algorithmic (flops, bytes) of one launch of each stage, from the realised routing.
     rows: kept routed rows; ne_experts: experts with at least one row."""
     T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
+    ER = 2 * E if c.gate == "noisy_topk" else E  # router rows (clean + noise for noisy gating)
     f1 = 2 * f if c.act == "swiglu" else f
     eb = 2 if c.dtype == "bf16" else 4
     S = T if c.shared else 0
@@ -104,7 +105,7 @@ def stage_work(c, rows, ne_experts):
     W1all = (E + (1 if c.shared else 0)) * f1 * d * eb
     W2all = (E + (1 if c.shared else 0)) * d * f * eb
     return {
-        "route": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 + T * k * 8),
+        "route": (2 * T * d * ER, T * d * eb + ER * d * 4 + T * ER * 4 + T * k * 8),
         # logits, softmax (probs + transposed copy), selection, token tables, gather
         "route_ec": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 * 6 + rows * (d * eb * 2 + 4)),
         "dispatch": (0, T * k * 4 * 3 + T * d * eb + rows * d * eb + rows * 4),
@@ -119,7 +120,7 @@ def stage_work(c, rows, ne_experts):
         "bwd_wgrad1": (2 * R * f1 * d, W1all + R * f1 * eb + R * d * eb),
         "bwd_dlogits": (0, T * E * 8 + T * k * 12),
         # bf16 with k <= 2: the dx_router product's epilogue also does the unpermute pass
-        "bwd_router_grads": (4 * T * d * E, T * E * 4 + T * d * eb + E * d * 4 * 2 +
+        "bwd_router_grads": (4 * T * d * ER, T * ER * 4 + T * d * eb + ER * d * 4 * 2 +
                              (T * d * eb * 2 + rows * d * eb if (eb == 2 and k <= 2) else T * d * 4)),
         "bwd_unpermute": (0, T * d * eb * 2 + rows * d * eb + T * d * 4),
         "bias_update": (0, E * 4 * 3),
@@ -156,7 +157,7 @@ def main():
                     help="selection-bias step of the bias-carrying gates: sign (fixed step) or quantile")
     ap.add_argument("--routing", default="token_choice", choices=["token_choice", "expert_choice"],
                     help="expert_choice: every expert takes its top tokens (k = E, capacity from cf)")
-    ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias"],
+    ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias", "noisy_topk"],
                     help="override the workload's gate (a bias-carrying gate draws the selection bias)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,7 +179,10 @@ def main():
     if c.fwd_only:
         c = c.replace(fwd_only=False)
     if args.gate and args.gate != c.gate:
-        c = c.replace(gate=args.gate, sel_bias="none" if args.gate == "softmax" else "uniform")
+        c = c.replace(gate=args.gate, sel_bias="uniform" if args.gate in ("sigmoid_bias", "sqrt_softplus_bias")
+                      else "none")
+        if args.gate == "noisy_topk":  # softmax over the top-k: renormalised; no per-expert logit offset
+            c = c.replace(renorm=True, logit_offset="none")
     if args.routing == "expert_choice":
         # each expert takes C = ceil(T/E * cf) tokens: the same rows as top-k at cf = k
         c = c.replace(name=c.name + "_ec", routing="expert_choice", k=c.E, gate="softmax", renorm=False,
@@ -190,7 +194,7 @@ def main():
     buf = M.LayerBuffers.allocate(cfg)
     stream = torch.cuda.current_stream()
 
-    biased = c.gate != "softmax"
+    biased = c.gate in ("sigmoid_bias", "sqrt_softplus_bias")
 
     def step():
         M.forward(buf, inp, stream=stream)

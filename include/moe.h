@@ -53,6 +53,8 @@ extern "C" {
 #define MOE_GATE_SOFTMAX 0        /* [SW] eq. (1); selection on the logits */
 #define MOE_GATE_SIGMOID_BIAS 1   /* [WIKI] sigmoid gate + per-expert bias used only to select */
 #define MOE_GATE_SQRT_SOFTPLUS_BIAS 2 /* [WIKI] sqrt(softplus) gate (DeepSeek-V4) + the same selection bias */
+#define MOE_GATE_NOISY_TOPK 3     /* [WIKI] noisy top-k softmax gating (Shazeer et al. 2017); router has 2E rows,
+                                     routed with moe_route_noisy; renormalize must be 1; E <= 256 */
 /* routing ([WIKI] survey finding on MoE-based LLMs names expert-choice routing) */
 #define MOE_ROUTING_TOKEN_CHOICE 0  /* each token takes its top_k experts (moe_route + moe_dispatch) */
 #define MOE_ROUTING_EXPERT_CHOICE 1 /* each expert takes its C tokens (moe_route_ec); top_k must equal
@@ -108,6 +110,8 @@ typedef struct moe_saved {
   const void* y_perm;            /* [R, d]  act: expert outputs */
   const void* act_shared;        /* [T, f1] shared expert (NULL without one) */
   const void* h_shared;          /* [T, f]  shared expert (NULL without one) */
+  const float* noisy_logits;     /* [T, 2E] clean | noise logits (noisy gating only, else NULL) */
+  const float* noise;            /* [T, E]  eps (noisy gating only, else NULL) */
 } moe_saved;
 
 /* Layer parameters (device memory). */
@@ -154,6 +158,37 @@ int moe_plan(const moe_config* cfg, moe_plan_info* out);
 int moe_route(const moe_config* cfg, const void* x, const float* w_router,
               const float* logit_offset, const float* sel_bias, float* probs,
               int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Noisy top-k routing ([WIKI], findings on Shazeer et al. 2017: top-k sparse
+ * gating with noisy softmax). The page names the method only; it follows that
+ * paper:
+ *   logits2[t, :] = [h | n]: the router logits of the 2E-row router
+ *     (rows 0..E-1 = W_g, rows E..2E-1 = W_noise), each by the moe_route contract;
+ *   H[t, e] = h + noise[t, e] * softplus_c(n), softplus_c(n) = max(n, 0) +
+ *     log1p_c(exp_c(-|n|)) (the library's fixed fp32 functions), one fp32
+ *     multiply and one fp32 add;
+ *   then the softmax gate of moe_route on H with renormalisation: the k largest
+ *     H (lower index on ties), weights = softmax over those k; probs = softmax(H).
+ * w_router [2E, d]; noise [T, E] fp32, the N(0, 1) draws (an input). Outputs
+ * logits2 [T, 2E] (kept for the loss and the backward), probs [T, E],
+ * topk_idx [T, k], topk_w [T, k]. Requires cfg->gate == MOE_GATE_NOISY_TOPK. */
+int moe_route_noisy(const moe_config* cfg, const void* x, const float* w_router, const float* noise,
+                    float* logits2, float* probs, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Importance and load losses of noisy top-k gating ([WIKI], findings on Shazeer
+ * et al. 2017: total loss = main + alpha (importance loss + load loss), the
+ * first the dispersion of each expert's summed gate, the second that of a
+ * smoothed load estimate), as that paper defines them:
+ *   Importance_e = sum_t topk_w over the tokens that selected e;
+ *   Load_e = sum_t Phi((h[t,e] - r[t,e]) / softplus(n[t,e])), r[t,e] = the k-th
+ *     largest H of token t with e left out (the (k+1)-th H if e is selected,
+ *     else the k-th); no load term when k = E;
+ *   aux = aux_alpha (CV^2(Importance) + CV^2(Load)), CV^2 = population variance /
+ *     mean^2 (0 for a zero mean). Computed in fp32 in a fixed order.
+ * Inputs as written by moe_route_noisy; aux_out: one fp32 on the device. Needs
+ * the workspace. moe_aux_loss returns MOE_ERR_UNSUPPORTED for this gate. */
+int moe_aux_noisy(const moe_config* cfg, const float* logits2, const float* noise, const int32_t* topk_idx,
+                  const float* topk_w, float* aux_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Expert-choice routing and permutation in one call ([WIKI], survey finding on
  * MoE-based LLMs: the experts, not the tokens, take the top-k).
@@ -274,6 +309,10 @@ int moe_bias_quantile(const moe_config* cfg, const float* probs, float* sel_bias
  *   dx = dy + sum over kept r of dX_perm[slot] + dx_router (+ dx_shared)
  *   dw1, dw2 per expert from its rows (zeros for experts with no rows),
  *   dws1, dws2 for the shared expert, dw_router = dlogits^T x in fp32.
+ * Noisy gating: dlogits is [T, 2E] (clean and noise logits: the gate path through
+ * H = h + eps softplus(n), the importance loss through the gates and the load
+ * loss through Phi, also to each token's rival expert); w_router and dw_router
+ * are [2E, d]; s->noisy_logits and s->noise must be set.
  * dy: [T,d] act. s, w, g: host structs holding device pointers. Needs the workspace. */
 int moe_backward(const moe_config* cfg, const void* dy, const moe_saved* s,
                  const moe_weights* w, const moe_grads* g, void* ws, size_t ws_bytes,

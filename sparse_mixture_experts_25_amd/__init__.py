@@ -5,8 +5,8 @@ kernels. torch supplies device memory and the current stream. There is no
 fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
-Entry points mirror the C ABI: moe_plan, moe_route, moe_route_ec, moe_dispatch,
-moe_expert_ffn, moe_combine, moe_aux_loss, moe_bias_update, moe_bias_quantile, moe_backward,
+Entry points mirror the C ABI: moe_plan, moe_route, moe_route_noisy, moe_route_ec, moe_dispatch,
+moe_expert_ffn, moe_combine, moe_aux_loss, moe_aux_noisy, moe_bias_update, moe_bias_quantile, moe_backward,
 moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
 ``forward`` / ``backward`` issue the ABI calls in order on those buffers.
@@ -24,15 +24,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SQRT_SOFTPLUS_BIAS = 0, 1, 2
+MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SQRT_SOFTPLUS_BIAS, MOE_GATE_NOISY_TOPK = 0, 1, 2, 3
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid_bias": MOE_GATE_SIGMOID_BIAS,
-         "sqrt_softplus_bias": MOE_GATE_SQRT_SOFTPLUS_BIAS}
+         "sqrt_softplus_bias": MOE_GATE_SQRT_SOFTPLUS_BIAS, "noisy_topk": MOE_GATE_NOISY_TOPK}
 MOE_ROUTING_TOKEN_CHOICE, MOE_ROUTING_EXPERT_CHOICE = 0, 1
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
-EXPORTS = ["moe_plan", "moe_route", "moe_route_ec", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-           "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
+EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_dispatch", "moe_expert_ffn",
+           "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -59,7 +59,7 @@ _vp = ctypes.c_void_p
 class moe_saved(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "probs", "topk_idx", "topk_w", "slot", "expert_counts",
                                    "expert_offsets", "x_perm", "act_saved", "h_saved", "y_perm",
-                                   "act_shared", "h_shared")]
+                                   "act_shared", "h_shared", "noisy_logits", "noise")]
 
 
 class moe_weights(ctypes.Structure):
@@ -84,6 +84,8 @@ def lib():
         cfg = P(moe_config)
         L.moe_plan.argtypes = [cfg, P(moe_plan_info)]
         L.moe_route.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_route_noisy.argtypes = [cfg] + [_vp] * 8
+        L.moe_aux_noisy.argtypes = [cfg] + [_vp] * 6 + [ctypes.c_size_t, _vp]
         L.moe_route_ec.argtypes = [cfg] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         L.moe_dispatch.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
@@ -138,6 +140,16 @@ def moe_plan(cfg: moe_config) -> moe_plan_info:
 def moe_route(cfg, x, w_router, logit_offset, sel_bias, probs, topk_idx, topk_w, stream=None):
     _check(lib().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(sel_bias), _p(probs),
                            _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_route_noisy(cfg, x, w_router, noise, logits2, probs, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route_noisy(ctypes.byref(cfg), _p(x), _p(w_router), _p(noise), _p(logits2), _p(probs),
+                                 _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route_noisy")
+
+
+def moe_aux_noisy(cfg, logits2, noise, topk_idx, topk_w, aux_out, ws, stream=None):
+    _check(lib().moe_aux_noisy(ctypes.byref(cfg), _p(logits2), _p(noise), _p(topk_idx), _p(topk_w), _p(aux_out),
+                               _p(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_aux_noisy")
 
 
 def moe_route_ec(cfg, x, w_router, logit_offset, probs, topk_w, slot, expert_counts, expert_offsets, row_token,
@@ -213,8 +225,12 @@ class LayerBuffers:
                  aux=e((1,), f32), ws=e((max(int(info.workspace_bytes), 256),), torch.uint8))
         if cfg.num_shared_experts:
             t.update(act_shared=e((T, f1), dt), h_shared=e((T, f), dt), y_shared=e((T, d), dt))
+        noisy = cfg.gate == MOE_GATE_NOISY_TOPK
+        if noisy:
+            t.update(noisy_logits=e((T, 2 * E), f32))
         if backward:
-            t.update(dx=e((T, d), dt), dw_router=e((E, d), f32), dw1=e((E, f1, d), dt), dw2=e((E, d, f), dt))
+            t.update(dx=e((T, d), dt), dw_router=e(((2 if noisy else 1) * E, d), f32), dw1=e((E, f1, d), dt),
+                     dw2=e((E, d, f), dt))
             if cfg.num_shared_experts:
                 t.update(dws1=e((f1, d), dt), dws2=e((d, f), dt))
         return LayerBuffers(cfg, info, t)
@@ -223,7 +239,12 @@ class LayerBuffers:
 def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
     """moe_route -> moe_dispatch (or moe_route_ec) -> moe_expert_ffn -> moe_combine (-> moe_aux_loss)."""
     c, t = buf.cfg, buf.t
-    if c.routing == MOE_ROUTING_EXPERT_CHOICE:
+    if c.gate == MOE_GATE_NOISY_TOPK:
+        moe_route_noisy(c, inp["x"], inp["w_router"], inp["noise"], t["noisy_logits"], t["probs"], t["topk_idx"],
+                        t["topk_w"], stream)
+        moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
+                     t["row_token"], t["x_perm"], t["ws"], stream)
+    elif c.routing == MOE_ROUTING_EXPERT_CHOICE:
         moe_route_ec(c, inp["x"], inp["w_router"], inp.get("logit_offset"), t["probs"], t["topk_w"], t["slot"],
                      t["expert_counts"], t["expert_offsets"], t["row_token"], t["x_perm"], t["ws"], stream)
     else:
@@ -235,12 +256,14 @@ def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
                    inp.get("ws2"), t["act_saved"], t["h_saved"], t["y_perm"], t.get("act_shared"),
                    t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
     moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
-    if aux:
+    if aux and c.gate == MOE_GATE_NOISY_TOPK:
+        moe_aux_noisy(c, t["noisy_logits"], inp["noise"], t["topk_idx"], t["topk_w"], t["aux"], t["ws"], stream)
+    elif aux:
         moe_aux_loss(c, t["probs"], t["expert_counts"], t["aux"], t["ws"], stream)
 
 
 SAVED_KEYS = ["probs", "topk_idx", "topk_w", "slot", "expert_counts", "expert_offsets", "x_perm", "act_saved",
-              "h_saved", "y_perm", "act_shared", "h_shared"]
+              "h_saved", "y_perm", "act_shared", "h_shared", "noisy_logits"]
 
 
 def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream=None):
@@ -248,6 +271,7 @@ def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream
     t = buf.t
     sv = {k: t.get(k) for k in SAVED_KEYS}
     sv["x"] = inp["x"]
+    sv["noise"] = inp.get("noise")
     if saved:
         sv.update(saved)
     weights = {k: inp.get(k) for k in ("w_router", "w1", "w2", "ws1", "ws2")}

@@ -32,8 +32,11 @@ int check_config(const moe_config* c) {
     if (c->gate != MOE_GATE_SOFTMAX || c->renormalize || c->aux_alpha != 0.0f) return MOE_ERR_UNSUPPORTED;
   }
   if ((int64_t)c->num_tokens * c->top_k > (int64_t)0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS && c->gate != MOE_GATE_SQRT_SOFTPLUS_BIAS)
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS && c->gate != MOE_GATE_SQRT_SOFTPLUS_BIAS &&
+      c->gate != MOE_GATE_NOISY_TOPK)
     return MOE_ERR_UNSUPPORTED;
+  // noisy gating: softmax over the top-k (renormalised), 2E router rows (<= 512)
+  if (c->gate == MOE_GATE_NOISY_TOPK && (ec || !c->renormalize || c->num_experts > 256)) return MOE_ERR_UNSUPPORTED;
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (c->dtype != MOE_DT_F32 && c->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->num_shared_experts != 0 && c->num_shared_experts != 1) return MOE_ERR_UNSUPPORTED;
@@ -57,10 +60,14 @@ int64_t max_rows_of(const moe_config* c, int C) {
 
 // Backward workspace layout.
 struct BwdWs {
-  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, gx, gw, wsp, offs, total;
+  size_t dO, dA, dXp, dg, dl, dxr, part, dA_sh, dX_sh, order, gx, gw, wsp, offs, nz, total;
 };
+// router rows: E, or 2E (clean and noise) for noisy gating
+int64_t router_rows(const moe_config* c) {
+  return c->gate == MOE_GATE_NOISY_TOPK ? 2 * (int64_t)c->num_experts : c->num_experts;
+}
 BwdWs bwd_layout(const moe_config* c, int64_t R) {
-  const int64_t T = c->num_tokens, d = c->d_model, E = c->num_experts, k = c->top_k;
+  const int64_t T = c->num_tokens, d = c->d_model, E = router_rows(c), k = c->top_k;
   const int64_t f1 = c->act == MOE_ACT_SWIGLU ? 2 * (int64_t)c->d_ff : c->d_ff;
   const int64_t eb = elem_bytes(c);
   const int64_t ns = moe::router_grad_splits((int)T, (int)E, (int)d);
@@ -83,6 +90,8 @@ BwdWs bwd_layout(const moe_config* c, int64_t R) {
   w.gw = o; o += c->dtype == MOE_DT_BF16 ? align_up(T * kp * 2) : 0;
   w.wsp = o; o += c->dtype == MOE_DT_BF16 ? align_up(kp * d * 2) : 0;
   w.offs = o; o += align_up((3 + nsw) * 4);
+  w.nz = o;
+  o += c->gate == MOE_GATE_NOISY_TOPK ? align_up(moe::noisy_workspace_bytes((int)T, c->num_experts)) : 0;
   w.total = o;
   return w;
 }
@@ -97,9 +106,13 @@ size_t workspace_of(const moe_config* c, int64_t R) {
     const size_t ec = align_up(moe::ec_workspace_bytes(c->num_tokens, c->num_experts));
     if (ec > ws) ws = ec;
   }
-  if (c->gate != MOE_GATE_SOFTMAX) {
+  if (c->gate == MOE_GATE_SIGMOID_BIAS || c->gate == MOE_GATE_SQRT_SOFTPLUS_BIAS) {
     const size_t qb = align_up(moe::qb_workspace_bytes(c->num_tokens, c->num_experts));
     if (qb > ws) ws = qb;
+  }
+  if (c->gate == MOE_GATE_NOISY_TOPK) {
+    const size_t nz = align_up(moe::noisy_workspace_bytes(c->num_tokens, c->num_experts));
+    if (nz > ws) ws = nz;
   }
   return ws;
 }
@@ -172,7 +185,7 @@ int moe_route(const moe_config* c, const void* x, const float* w_router, const f
               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
   int st = check_config(c);
   if (st) return st;
-  if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE || c->gate == MOE_GATE_NOISY_TOPK) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;  // token-indexed pointers may then be NULL
   if (!w_router || (!empty && (!x || !probs || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
@@ -181,6 +194,35 @@ int moe_route(const moe_config* c, const void* x, const float* w_router, const f
                     c->num_experts, c->top_k, c->gate, c->renormalize ? 1 : 0, c->dtype};
   StageTimer pt("route", (hipStream_t)stream);
   return launch_status(moe::launch_router(a, (hipStream_t)stream));
+}
+
+int moe_route_noisy(const moe_config* c, const void* x, const float* w_router, const float* noise,
+                    float* logits2, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->gate != MOE_GATE_NOISY_TOPK) return MOE_ERR_UNSUPPORTED;
+  const bool empty = c->num_tokens == 0;
+  if (!w_router || (!empty && (!x || !noise || !logits2 || !probs || !topk_idx || !topk_w)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  if (empty) return MOE_OK;
+  moe::RouterArgs a{x, w_router, nullptr, nullptr, probs, topk_idx, topk_w, c->num_tokens, c->d_model,
+                    c->num_experts, c->top_k, MOE_GATE_SOFTMAX, 1, c->dtype};
+  StageTimer pt("route", (hipStream_t)stream);
+  return launch_status(moe::launch_route_noisy(a, noise, logits2, (hipStream_t)stream));
+}
+
+int moe_aux_noisy(const moe_config* c, const float* logits2, const float* noise, const int32_t* topk_idx,
+                  const float* topk_w, float* aux_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->gate != MOE_GATE_NOISY_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (!aux_out || (c->num_tokens > 0 && (!logits2 || !noise || !topk_idx || !topk_w))) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, capacity_of(c)))) return MOE_ERR_WORKSPACE;
+  moe::NoisyArgs a{logits2, noise, topk_idx, topk_w, (float*)ws, c->num_tokens, c->num_experts, c->top_k,
+                   c->aux_alpha};
+  StageTimer pt("aux", (hipStream_t)stream);
+  return launch_status(moe::launch_noisy_stats(a, aux_out, (hipStream_t)stream));
 }
 
 int moe_route_ec(const moe_config* c, const void* x, const float* w_router, const float* logit_offset, float* probs,
@@ -293,6 +335,7 @@ int moe_aux_loss(const moe_config* c, const float* probs, const int32_t* expert_
                  size_t ws_bytes, void* stream) {
   int st = check_config(c);
   if (st) return st;
+  if (c->gate == MOE_GATE_NOISY_TOPK) return MOE_ERR_UNSUPPORTED;  // moe_aux_noisy
   if (!expert_counts || !aux_out || (c->num_tokens > 0 && !probs)) return MOE_ERR_INVALID_ARG;
   const int C = capacity_of(c);
   if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, C))) return MOE_ERR_WORKSPACE;
@@ -334,6 +377,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   const bool empty = c->num_tokens == 0;  // token- and row-indexed pointers may then be NULL
   if (!sv->expert_counts || !sv->expert_offsets) return MOE_ERR_INVALID_ARG;
   const bool ec = c->routing == MOE_ROUTING_EXPERT_CHOICE;  // topk_idx is implied (column = expert)
+  const bool noisy = c->gate == MOE_GATE_NOISY_TOPK;
+  if (noisy && !empty && (!sv->noisy_logits || !sv->noise)) return MOE_ERR_INVALID_ARG;
   if (!empty && (!dy || !sv->x || !sv->probs || (!ec && !sv->topk_idx) || !sv->topk_w || !sv->slot || !sv->x_perm ||
                  !sv->act_saved || !sv->h_saved || !sv->y_perm || !g->dx))
     return MOE_ERR_INVALID_ARG;
@@ -429,7 +474,12 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w1g.C = g->dw1; w1g.ldc = d; w1g.strideC = (int64_t)f1 * d; w1g.C_sh = g->dws1;
   if ((st = gemm(c, w1g, s, "bwd_wgrad1"))) return st;
   // router: dlogits, dW_r, dx_router
-  if (T > 0) {
+  if (noisy) {
+    moe::NoisyArgs na{sv->noisy_logits, sv->noise, sv->topk_idx, sv->topk_w, (float*)(base + L.nz), T, E, k,
+                      c->aux_alpha};
+    StageTimer pt("bwd_dlogits", s);
+    if ((st = launch_status(moe::launch_noisy_dlogits(na, dg, dl, s)))) return st;
+  } else if (T > 0) {
     moe::DlogitsArgs dla{sv->probs, ec ? nullptr : sv->topk_idx, sv->topk_w, dg, sv->expert_counts, dl, T, E, k, c->gate,
                          c->renormalize ? 1 : 0, c->aux_alpha};
     StageTimer pt("bwd_dlogits", s);
@@ -440,8 +490,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   // too few loads in flight and the separate pass is faster)
   const bool fuse_dx = c->dtype == MOE_DT_BF16 && k <= 2;
   moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, (uint16_t*)(base + L.gx),
-                         (uint16_t*)(base + L.gw), (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs), T, d, E,
-                         c->dtype, dy, sv->slot, k, dXp, dX_sh, fuse_dx ? g->dx : nullptr};
+                         (uint16_t*)(base + L.gw), (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs), T, d,
+                         (int)router_rows(c), c->dtype, dy, sv->slot, k, dXp, dX_sh, fuse_dx ? g->dx : nullptr};
   {
     StageTimer pt("bwd_router_grads", s);
     if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;

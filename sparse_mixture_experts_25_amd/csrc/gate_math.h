@@ -65,11 +65,13 @@ __device__ __forceinline__ float log1p_c(float u) {
 // Square root of softplus ([WIKI], DeepSeek-V4's replacement of the sigmoid
 // gate): softplus(h) = max(h, 0) + log(1 + e^-|h|), which cannot overflow, then
 // the correctly rounded fp32 square root.
-__device__ __forceinline__ float sqrt_softplus_c(float h) {
+// softplus(h) = log(1 + e^h) as max(h, 0) + log1p_c(exp_c(-|h|)): never overflows.
+__device__ __forceinline__ float softplus_c(float h) {
   const float u = exp_c(-__builtin_fabsf(h));
-  const float sp = (h > 0.0f ? h : 0.0f) + log1p_c(u);
-  return __builtin_sqrtf(sp);
+  return (h > 0.0f ? h : 0.0f) + log1p_c(u);
 }
+
+__device__ __forceinline__ float sqrt_softplus_c(float h) { return __builtin_sqrtf(softplus_c(h)); }
 #pragma clang fp contract(on)
 
 }  // namespace moe

@@ -41,6 +41,21 @@ size_t ec_workspace_bytes(int T, int E);
 hipError_t launch_route_ec(const RouteEcArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias, hipStream_t st);
 size_t qb_workspace_bytes(int T, int E);
+// noisy top-k gating: routing over the stacked [W_g; W_noise] router
+hipError_t launch_route_noisy(const RouterArgs& a, const float* noise, float* logits2, hipStream_t st);
+struct NoisyArgs {
+  const float* logits2;   // [T, 2E] clean | noise logits
+  const float* noise;     // [T, E] eps
+  const int32_t* topk_idx;
+  const float* topk_w;
+  float* ws;              // noisy_workspace_bytes(T, E)
+  int T, E, k;
+  float alpha;
+};
+int noisy_num_blocks(int T);
+size_t noisy_workspace_bytes(int T, int E);
+hipError_t launch_noisy_stats(const NoisyArgs& a, float* aux_out, hipStream_t st);
+hipError_t launch_noisy_dlogits(const NoisyArgs& a, const float* dg, float* dl2, hipStream_t st);
 hipError_t launch_bias_quantile(const float* probs, float* bias, int T, int E, int k, void* ws, hipStream_t st);
 
 struct DispatchArgs {

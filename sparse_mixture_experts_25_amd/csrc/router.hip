@@ -253,6 +253,33 @@ __global__ __launch_bounds__(256) void router_gate_kernel(const float* __restric
   gate_topk<QE>(h, sel_bias, lane, E, k, gate, renorm, tt, probs, topk_idx, topk_w);
 }
 
+// Noisy top-k gate (one wave per token): H = h + eps * softplus_c(n) from the
+// stacked clean|noise logits (one fp32 multiply and one fp32 add; no
+// contraction), then the softmax gate on H, renormalised over the k selected.
+#pragma clang fp contract(off)
+template <int QE>
+__global__ __launch_bounds__(256) void noisy_gate_kernel(const float* __restrict__ logits2,
+                                                         const float* __restrict__ noise, float* __restrict__ probs,
+                                                         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                         int T, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tt >= T) return;
+  float H[QE];
+#pragma unroll
+  for (int q = 0; q < QE; ++q) {
+    const int e = lane + 64 * q;
+    H[q] = 0.0f;
+    if (e < E) {
+      const float sp = softplus_c(logits2[tt * 2 * E + E + e]);
+      const float prod = noise[tt * E + e] * sp;
+      H[q] = logits2[tt * 2 * E + e] + prod;
+    }
+  }
+  gate_topk<QE>(H, nullptr, lane, E, k, MOE_GATE_SOFTMAX, 1, tt, probs, topk_idx, topk_w);
+}
+#pragma clang fp contract(on)
+
 // Register-tiled variant for wide d_model, where streaming x once per
 // workgroup matters more than occupancy. A workgroup owns TT = TG * TPT tokens
 // and every expert; thread (tg, eg) owns tokens tg*TPT .. +TPT-1 and experts
@@ -530,6 +557,28 @@ hipError_t launch_router_logits(const RouterArgs& a, hipStream_t st, bool* offse
   b.gate = kGateLogitsOnly;
   if (a.dtype == MOE_DT_BF16) return launch_router_wide<uint16_t>(b, st);
   return launch_router_wide<float>(b, st);
+}
+
+// Noisy top-k routing: the logits kernels over the stacked 2E-row router into
+// logits2 [T, 2E], then the noisy gate.
+hipError_t launch_route_noisy(const RouterArgs& a, const float* noise, float* logits2, hipStream_t st) {
+  RouterArgs r = a;
+  r.E = 2 * a.E;
+  r.probs = logits2;
+  r.logit_offset = nullptr;
+  bool applied = false;
+  hipError_t e = launch_router_logits(r, st, &applied);
+  if (e != hipSuccess) return e;
+  const int qe = (a.E + 63) / 64;
+  const dim3 g((a.T + 3) / 4);
+#define MOE_NOISY_LAUNCH(Q)                                                                                  \
+  hipLaunchKernelGGL(noisy_gate_kernel<Q>, g, dim3(256), 0, st, logits2, noise, a.probs, a.topk_idx, a.topk_w, \
+                     a.T, a.E, a.k)
+  if (qe <= 1) MOE_NOISY_LAUNCH(1);
+  else if (qe <= 2) MOE_NOISY_LAUNCH(2);
+  else MOE_NOISY_LAUNCH(4);
+#undef MOE_NOISY_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {

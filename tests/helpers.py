@@ -80,6 +80,8 @@ def gpu_saved_from_oracle(c, fw: dict, info, device="cuda") -> dict:
     if c.shared:
         sv["act_shared"] = torch.from_numpy(fw["act_shared"]).to(dt).to(device)
         sv["h_shared"] = torch.from_numpy(fw["h_shared"]).to(dt).to(device)
+    if "logits2" in fw:
+        sv["noisy_logits"] = torch.from_numpy(fw["logits2"]).float().to(device)
     return sv
 
 

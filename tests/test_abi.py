@@ -134,5 +134,15 @@ def test_entry_points_validate_before_launch():
     assert L.moe_bias_quantile(ctypes.byref(sg), A, N, A, ws_sg, N) == E
     assert L.moe_bias_quantile(ctypes.byref(sg), MIS, A, A, ws_sg, N) == E
     assert L.moe_bias_quantile(ctypes.byref(sg), A, A, A, ws_sg - 1, N) == M.MOE_ERR_WORKSPACE
+    nz = M.make_config(64, 64, 64, 4, 2, gate="noisy_topk", renorm=True)
+    ws_nz = M.moe_plan(nz).workspace_bytes
+    assert L.moe_route(ctypes.byref(nz), A, A, N, N, A, A, A, N) == M.MOE_ERR_UNSUPPORTED  # needs the noise
+    assert L.moe_aux_loss(ctypes.byref(nz), A, A, A, A, ws_nz, N) == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_noisy(ctypes.byref(nz), A, A, N, A, A, A, A, N) == E
+    assert L.moe_aux_noisy(ctypes.byref(nz), A, A, A, A, A, A, ws_nz - 1, N) == M.MOE_ERR_WORKSPACE
+    assert L.moe_route_noisy(c, A, A, A, A, A, A, A, N) == M.MOE_ERR_UNSUPPORTED  # softmax config
+    nz_norenorm = M.make_config(64, 64, 64, 4, 2, gate="noisy_topk", renorm=False)
+    info = M.moe_plan_info()
+    assert L.moe_plan(ctypes.byref(nz_norenorm), ctypes.byref(info)) == M.MOE_ERR_UNSUPPORTED
     bad = M.make_config(64, 60, 64, 4, 2)
     assert L.moe_route(ctypes.byref(bad), A, A, N, N, A, A, A, N) == E

@@ -35,6 +35,17 @@ CASES["sqrt_softplus_f32_drops"] = LayerConfig("sqrt_softplus_f32_drops", T=200,
                                                gate="sqrt_softplus_bias", renorm=False, act="relu", dtype="f32",
                                                cf=0.75, alpha=0.01, sel_bias="uniform")
 
+# noisy top-k gating (stacked clean|noise router, importance + load losses):
+# narrow d with drops, fp32 with a shared expert, and wide d (2E = 128 logits on
+# the register-tiled router kernel)
+_NZ = dict(gate="noisy_topk", renorm=True)
+CASES["noisy_relu_bf16"] = LayerConfig("noisy_relu_bf16", T=777, d=192, f=320, E=8, k=2, act="relu", cf=1.25,
+                                       alpha=0.01, **_NZ)
+CASES["noisy_swiglu_f32_shared"] = LayerConfig("noisy_swiglu_f32_shared", T=130, d=72, f=48, E=6, k=1,
+                                               act="swiglu", dtype="f32", cf=0.0, alpha=0.3, shared=1, **_NZ)
+CASES["noisy_wide_d"] = LayerConfig("noisy_wide_d", T=200, d=1040, f=136, E=64, k=4, act="swiglu", cf=0.0,
+                                    alpha=0.01, **_NZ)
+
 # expert-choice routing (k = E columns): narrow-d logits kernel with a per-expert
 # logit offset, wide-d tile kernel (logits-only mode), fp32 with a shared expert,
 # and C >= T (every expert takes every token)
@@ -67,6 +78,10 @@ def _check_routing(buf, fw, n):
         np.testing.assert_array_equal(t["topk_w"].cpu().numpy(), fw["w"].astype(np.float32))
     else:
         np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), fw["idx"])
+    if "logits2" in fw:
+        # clean and noise logits follow the fp32 logit contract: bit for bit
+        np.testing.assert_array_equal(t["noisy_logits"].cpu().numpy().view(np.uint32),
+                                      fw["logits2"].astype(np.float32).view(np.uint32))
     np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), fw["counts"])
     np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), fw["offsets"])
     np.testing.assert_array_equal(t["slot"].cpu().numpy(), fw["slot"])
