@@ -38,6 +38,13 @@ FULL["gshard_top2_ec"] = CONFIGS["gshard_top2"].replace(name="gshard_top2_ec", r
                                                         renorm=False, alpha=0.0)
 FULL["deepseek_v3_sqrt_softplus"] = CONFIGS["deepseek_v3"].replace(name="deepseek_v3_sqrt_softplus",
                                                                    gate="sqrt_softplus_bias")
+# noisy top-k gating on the GShard shape: routing, clean|noise logits and the
+# importance + load loss at full size (the per-token input-gradient check is
+# left out for this gate: its router term carries batch-wide loss
+# coefficients that a one-token sub-problem does not have; the reduced-size
+# tests compare that gradient element by element)
+FULL["gshard_top2_noisy"] = CONFIGS["gshard_top2"].replace(name="gshard_top2_noisy", gate="noisy_topk",
+                                                           logit_offset="none")
 
 
 def _expert_w(inp, e, shared=False):
@@ -63,7 +70,11 @@ def test_full_size(name):
 
     # ---- routing, every token
     x64 = host64(inp["x"])
-    r = O.route(spec, x64, host64(inp["w_router"]), host64(inp.get("logit_offset")), host64(inp.get("sel_bias")))
+    r = O.route(spec, x64, host64(inp["w_router"]), host64(inp.get("logit_offset")), host64(inp.get("sel_bias")),
+                host64(inp.get("noise")))
+    if "logits2" in r:
+        np.testing.assert_array_equal(t["noisy_logits"].cpu().numpy().view(np.uint32),
+                                      r["logits2"].astype(np.float32).view(np.uint32))
     if c.routing == "expert_choice":
         # the experts compared these probabilities across tokens: bit for bit
         np.testing.assert_array_equal(t["probs"].cpu().numpy().view(np.uint32),
@@ -80,7 +91,7 @@ def test_full_size(name):
     np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), r["row_token"][:n])
     if c.alpha:
         assert abs(float(t["aux"][0]) - r["aux"]) <= TOL_F32 * abs(r["aux"])
-    if spec.gate != O.GATE_SOFTMAX:
+    if spec.gate in (O.GATE_SIGMOID_BIAS, O.GATE_SQRT_SOFTPLUS_BIAS):
         # both selection-bias steps on this batch: sign step from the counts, and
         # Quantile Balancing from the gate values, bit for bit
         b0 = inp["sel_bias"].clone()
@@ -158,7 +169,7 @@ def test_full_size(name):
         assert relerr(host64(t["y"][tt]), yref[0]) <= (TOL_BF16 if c.dtype == "bf16" else TOL_F32), tt
         if not kept and not c.shared:
             assert torch.equal(t["y"][tt].cpu(), inp["x"][tt].cpu())
-        if c.fwd_only:
+        if c.fwd_only or spec.gate == O.GATE_NOISY_TOPK:
             continue
         dO, dg = O.combine_bwd(spec.mode, dy64[tt:tt + 1], yp, lslot, w64[tt:tt + 1], len(kept))
         dXp = np.zeros((len(kept), c.d))
