@@ -109,7 +109,8 @@ def stage_work(c, rows, ne_experts):
         # logits, softmax (probs + transposed copy), selection, token tables, gather
         "route_ec": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 * 6 + rows * (d * eb * 2 + 4)),
         "dispatch": (0, T * k * 4 * 3 + T * d * eb + rows * d * eb + rows * 4),
-        "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * (f1 + f) * eb),
+        # SwiGLU stores the pre-activations and h; ReLU only h
+        "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * ((f1 if c.act == "swiglu" else 0) + f) * eb),
         "ffn_gemm2": (2 * R * f * d, W2 + R * f * eb + R * d * eb),
         "combine": (0, T * d * eb * (2 + (1 if c.shared else 0)) + rows * d * eb + T * k * 8),
         "aux": (0, T * E * 4),

@@ -105,10 +105,10 @@ typedef struct moe_saved {
   const int32_t* expert_counts;  /* [E] assignments per expert before drops */
   const int32_t* expert_offsets; /* [E+1] first permuted row of each expert */
   const void* x_perm;            /* [R, d]  act */
-  const void* act_saved;         /* [R, f1] act: pre-activation(s) */
+  const void* act_saved;         /* [R, f1] act: pre-activation(s); SwiGLU only (ReLU: may be NULL) */
   const void* h_saved;           /* [R, f]  act: activation fed to the second matmul */
   const void* y_perm;            /* [R, d]  act: expert outputs */
-  const void* act_shared;        /* [T, f1] shared expert (NULL without one) */
+  const void* act_shared;        /* [T, f1] shared expert (NULL without one; ReLU: may be NULL) */
   const void* h_shared;          /* [T, f]  shared expert (NULL without one) */
   const float* noisy_logits;     /* [T, 2E] clean | noise logits (noisy gating only, else NULL) */
   const float* noise;            /* [T, E]  eps (noisy gating only, else NULL) */
@@ -239,6 +239,9 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
  *   y_perm = h W2_e^T
  * act and h are stored in the activation type (bf16: round to nearest even
  * from the fp32 accumulator; h is formed from the unrounded accumulators).
+ * With ReLU, act_saved / act_shared are optional (NULL: not written): the
+ * backward takes the derivative from the sign of h, and h > 0 exactly when
+ * act > 0 (a value that rounds to zero gives zero in both).
  * With a shared expert, the same is computed for every token row of x with
  * ws1/ws2 into act_shared [T,f1], h_shared [T,f], y_shared [T,d]; those pointers
  * must be NULL without one. Inputs: x_perm [R,d], expert_offsets [E+1] (device,

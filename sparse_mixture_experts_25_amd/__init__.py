@@ -220,11 +220,16 @@ class LayerBuffers:
         e = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=device)
         t = dict(probs=e((T, E), f32), topk_idx=e((T, k), i32), topk_w=e((T, k), f32),
                  expert_counts=e((E,), i32), expert_offsets=e((E + 1,), i32), slot=e((T, k), i32),
-                 row_token=e((max(R, 1),), i32), x_perm=e((max(R, 1), d), dt), act_saved=e((max(R, 1), f1), dt),
+                 row_token=e((max(R, 1),), i32), x_perm=e((max(R, 1), d), dt),
                  h_saved=e((max(R, 1), f), dt), y_perm=e((max(R, 1), d), dt), y=e((T, d), dt),
                  aux=e((1,), f32), ws=e((max(int(info.workspace_bytes), 256),), torch.uint8))
+        relu = cfg.act == MOE_ACT_RELU  # ReLU keeps only h (its sign is the derivative's mask)
+        if not relu:
+            t.update(act_saved=e((max(R, 1), f1), dt))
         if cfg.num_shared_experts:
-            t.update(act_shared=e((T, f1), dt), h_shared=e((T, f), dt), y_shared=e((T, d), dt))
+            t.update(h_shared=e((T, f), dt), y_shared=e((T, d), dt))
+            if not relu:
+                t.update(act_shared=e((T, f1), dt))
         noisy = cfg.gate == MOE_GATE_NOISY_TOPK
         if noisy:
             t.update(noisy_logits=e((T, 2 * E), f32))
@@ -253,7 +258,7 @@ def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
         moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
                      t["row_token"], t["x_perm"], t["ws"], stream)
     moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
-                   inp.get("ws2"), t["act_saved"], t["h_saved"], t["y_perm"], t.get("act_shared"),
+                   inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
                    t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
     moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
     if aux and c.gate == MOE_GATE_NOISY_TOPK:

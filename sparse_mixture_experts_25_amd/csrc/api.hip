@@ -270,10 +270,13 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   int st = check_config(c);
   if (st) return st;
   const bool empty = c->num_tokens == 0;
-  if (!expert_offsets || !w1 || !w2 || (!empty && (!x_perm || !act_saved || !h_saved || !y_perm)))
+  // ReLU: the pre-activations are optional (the backward takes the sign of h)
+  const bool need_act = c->act == MOE_ACT_SWIGLU;
+  if (!expert_offsets || !w1 || !w2 || (!empty && (!x_perm || (need_act && !act_saved) || !h_saved || !y_perm)))
     return MOE_ERR_INVALID_ARG;
   const bool sh = c->num_shared_experts > 0;
-  if (sh && (!ws1 || !ws2 || (!empty && (!x || !act_shared || !h_shared || !y_shared)))) return MOE_ERR_INVALID_ARG;
+  if (sh && (!ws1 || !ws2 || (!empty && (!x || (need_act && !act_shared) || !h_shared || !y_shared))))
+    return MOE_ERR_INVALID_ARG;
   if (!sh && (ws1 || ws2 || act_shared || h_shared || y_shared)) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x_perm, w1, w2, act_saved, h_saved, y_perm};
   for (const void* p : ptrs)
@@ -379,11 +382,13 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   const bool ec = c->routing == MOE_ROUTING_EXPERT_CHOICE;  // topk_idx is implied (column = expert)
   const bool noisy = c->gate == MOE_GATE_NOISY_TOPK;
   if (noisy && !empty && (!sv->noisy_logits || !sv->noise)) return MOE_ERR_INVALID_ARG;
+  const bool relu = c->act == MOE_ACT_RELU;  // the ReLU mask comes from h > 0, which equals act > 0
   if (!empty && (!dy || !sv->x || !sv->probs || (!ec && !sv->topk_idx) || !sv->topk_w || !sv->slot || !sv->x_perm ||
-                 !sv->act_saved || !sv->h_saved || !sv->y_perm || !g->dx))
+                 (!relu && !sv->act_saved) || !sv->h_saved || !sv->y_perm || !g->dx))
     return MOE_ERR_INVALID_ARG;
   if (!w->w_router || !w->w1 || !w->w2 || !g->dw_router || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
-  if (sh && (!w->ws1 || !w->ws2 || !g->dws1 || !g->dws2 || (!empty && (!sv->act_shared || !sv->h_shared))))
+  if (sh && (!w->ws1 || !w->ws2 || !g->dws1 || !g->dws2 ||
+             (!empty && ((!relu && !sv->act_shared) || !sv->h_shared))))
     return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {dy, sv->x, sv->x_perm, sv->act_saved, sv->h_saved, sv->y_perm, w->w_router,
                         w->w1, w->w2, g->dx, g->dw_router, g->dw1, g->dw2};
@@ -427,7 +432,13 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a2.B = w->w2; a2.ldb = f; a2.strideB = (int64_t)d * f;
   a2.A_sh = dy; a2.B_sh = w->ws2;
   a2.C = dA; a2.ldc = f1; a2.C_sh = dA_sh;
-  a2.X = sv->act_saved; a2.ldx = f1; a2.X_sh = sv->act_shared;
+  // ReLU derivative from the sign of the saved activation h (h > 0 exactly when the
+  // pre-activation is > 0); SwiGLU from the saved [gate | up] pre-activations
+  if (relu) {
+    a2.X = sv->h_saved; a2.ldx = f; a2.X_sh = sv->h_shared;
+  } else {
+    a2.X = sv->act_saved; a2.ldx = f1; a2.X_sh = sv->act_shared;
+  }
   if ((st = gemm(c, a2, s, "bwd_dgrad2"))) return st;
   // weight gradients run the experts with the most rows first
   if ((st = launch_status(moe::launch_group_order(sv->expert_offsets, E, shr, sh ? 1 : 0, order, s)))) return st;

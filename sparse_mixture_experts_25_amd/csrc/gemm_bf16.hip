@@ -500,7 +500,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
           float h[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) h[e] = fmaxf(v[e], 0.0f);
-          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+          if (C) st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));  // pre-activation only if asked for
           st128(C2 + row * a.ldc2 + col, Elem<uint16_t>::pack(h));
         } else if (EPI == EPI_RELU_BWD) {
           float xs[8];

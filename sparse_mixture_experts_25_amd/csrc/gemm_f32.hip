@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     if (EPI == EPI_STORE) {
       C[row * a.ldc + col] = v;
     } else if (EPI == EPI_RELU_FWD) {
-      C[row * a.ldc + col] = v;
+      if (C) C[row * a.ldc + col] = v;  // pre-activation only if asked for
       C2[row * a.ldc2 + col] = fmaxf(v, 0.0f);
     } else if (EPI == EPI_RELU_BWD) {
       C[row * a.ldc + col] = X[row * a.ldx + col] > 0.0f ? v : 0.0f;

@@ -126,14 +126,16 @@ def test_full_size(name):
         W1, W2 = _expert_w(inp, e)
         X = x64[r["row_token"][pick]]
         A, H, Y = O.ffn_fwd(spec.mode, X, W1, W2, spec.act)
-        assert relerr(host64(t["act_saved"][pick]), A) <= tol_for(c), e
+        if "act_saved" in t:  # ReLU layers keep only h
+            assert relerr(host64(t["act_saved"][pick]), A) <= tol_for(c), e
         assert relerr(host64(t["h_saved"][pick]), H) <= tol_for(c), e
         assert relerr(host64(t["y_perm"][pick]), Y) <= tol_for(c), e
     if c.shared:
         tok = sorted({0, c.T - 1, int(rng.integers(0, c.T))})
         W1, W2 = _expert_w(inp, 0, shared=True)
         A, H, Y = O.ffn_fwd(spec.mode, x64[tok], W1, W2, spec.act)
-        assert relerr(host64(t["act_shared"][tok]), A) <= TOL_BF16
+        if "act_shared" in t:
+            assert relerr(host64(t["act_shared"][tok]), A) <= TOL_BF16
         assert relerr(host64(t["y_shared"][tok]), Y) <= TOL_BF16
 
     # ---- sampled tokens: output y (and dx in the backward)

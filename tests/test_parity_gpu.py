@@ -101,7 +101,8 @@ def test_forward_parity(name):
     # the permutation is a bitwise row copy
     np.testing.assert_array_equal(host64(t["x_perm"][:n]), fw["x_perm"])
     tol = tol_for(c)
-    assert relerr(host64(t["act_saved"][:n]), fw["act"]) <= tol
+    if "act_saved" in t:  # ReLU layers keep only h
+        assert relerr(host64(t["act_saved"][:n]), fw["act"]) <= tol
     assert relerr(host64(t["h_saved"][:n]), fw["h"]) <= tol
     assert relerr(host64(t["y_perm"][:n]), fw["y_perm"]) <= tol
     assert relerr(host64(t["y"]), fw["y"]) <= tol
