@@ -126,6 +126,19 @@ struct DmaPlan {
 #pragma unroll
     for (int q = 0; q < Q; ++q) dma16s(voff[q], base, lds_tile + (wave * Q + q) * 1024);
   }
+  // The partial last step of an MN-contiguous operand (make_mn plan): k-rows
+  // at or past kv (1 <= kv < BK) read k-row kv-1 instead, so every address
+  // stays inside the group; the caller zeroes those k-rows in LDS.
+  __device__ void issue_mn_tail(const uint16_t* base, uint32_t lds_tile, int wave, int lane, int kv,
+                                int64_t ld) const {
+    constexpr int CPR = R / 8;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int kr = ((wave * Q + q) * 64 + lane) / CPR;
+      const uint32_t v = kr < kv ? voff[q] : voff[q] - (uint32_t)((int64_t)(kr - kv + 1) * ld * 2);
+      dma16s(v, base, lds_tile + (wave * Q + q) * 1024);
+    }
+  }
 };
 
 // ------------------------------------------------------------ kernel
@@ -133,11 +146,13 @@ struct DmaPlan {
 // per CU) and for 256x256 tiles with 128x128 per wave (one wave per SIMD), or 8
 // waves for 256x256 tiles with 128x64 per wave (two waves per SIMD, so one
 // wave's matrix work covers the other's waits).
-template <int WGN, int BM, int BN>
-constexpr int waves_per_simd() { return WGN == 4 ? 2 : (BM * BN >= 65536 ? 1 : 3); }
+// 128x128 weight-gradient tiles fit 128 registers (four workgroups per CU):
+// their short contractions are latency-bound, so more of them in flight pays.
+template <int WGN, int BM, int BN, int KIND>
+constexpr int waves_per_simd() { return WGN == 4 ? 2 : (BM * BN >= 65536 ? 1 : (KIND == 1 ? 4 : 3)); }
 
 template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN>
-__global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, BM, BN>(), waves_per_simd<WGN, BM, BN>()))) void gemm_bf16_kernel(
+__global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, BM, BN, KIND>(), waves_per_simd<WGN, BM, BN, KIND>()))) void gemm_bf16_kernel(
     GemmArgs a) {
   constexpr int kBK = BK;
   constexpr int NW = 2 * WGN, NTH = 64 * NW;  // waves, threads
@@ -260,15 +275,29 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     pa.issue(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
     pb.issue(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
-  // A partial last K step (k >= K reads as zero) goes through registers. For
-  // the weight gradients (a partial step in almost every group) its loads are
-  // issued in the prologue, right after the first direct loads, and written to
-  // LDS when the step is published; elsewhere (only ragged test shapes have a
-  // partial step) they are issued then, keeping registers free for occupancy.
-  // Every lane issues exactly UA + UB loads (clamped, in-bounds addresses; the
+  // weight gradients: the partial last step is one more direct-load step with
+  // clamped k-rows (both operands MN-contiguous)
+  auto dma_tail = [&](int stage, int k0) {
+    const uint32_t sa = lds0 + stage * kStage * 2;
+    const uint32_t sb = sa + BM * kBK * 2;
+    pa.issue_mn_tail(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
+    pb.issue_mn_tail(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
+  };
+  // A partial last K step (k >= K reads as zero). Weight gradients have one in
+  // almost every group:
+  //   128x128 tiles: one more pipelined direct-load step with clamped k-rows,
+  //     whose k-rows past the group are zeroed in LDS once it lands (no
+  //     registers held across the loop, so four workgroups fit a CU);
+  //   256x256 tiles: registers with zero fill, loaded in the prologue right
+  //     after the first direct loads and written to LDS when the step is
+  //     published.
+  // Row-ragged matmuls (only ragged test shapes have a partial step):
+  // registers with zero fill, loaded when the step is published. Every lane
+  // issues exactly UA + UB register loads (clamped, in-bounds addresses; the
   // value is masked afterwards), so the per-wave vmcnt accounting of the
   // direct loads stays exact.
-  constexpr bool kPrefetchTail = (KIND == 1);
+  constexpr bool kDmaTail = (KIND == 1) && BM < 256;
+  constexpr bool kPrefetchTail = (KIND == 1) && BM >= 256;
   constexpr int UA = BM * BK / 8 / NTH, UB = BN * BK / 8 / NTH;
   constexpr int NT = UA + UB;
   u128 tra[UA], trb[UB];
@@ -370,25 +399,45 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
 
   const int nfull = K / kBK;
   const int nk = nfull + ((K % kBK) ? 1 : 0);
-  // Direct loads issued before publish(k): steps 0 .. min(NS-1, nfull-1) for
-  // k = 0 (prologue); steps 0 .. min(k+NS-2, nfull-1) for k >= 1. The wait lets
-  // the later ones stay in flight.
-  // The tail loads (if any) follow the prologue's direct loads, so they are
-  // younger than steps 0 .. NS-1 and older than every later step.
   const bool has_tail = nk > nfull;
+  const int nd = kDmaTail ? nk : nfull;  // steps brought in by direct loads
+  auto issue_step = [&](int stage, int k) {
+    if (!kDmaTail || k < nfull) dma_step(stage, k * kBK);
+    else dma_tail(stage, k * kBK);
+  };
+  // Direct loads issued before publish(k): steps 0 .. min(NS-1, nd-1) for
+  // k = 0 (prologue); steps 0 .. min(k+NS-2, nd-1) for k >= 1. The wait lets
+  // the later ones stay in flight. Prefetched tail loads follow the
+  // prologue's direct loads: younger than steps 0 .. NS-1, older than every
+  // later step.
   auto publish = [&](int k) {
-    if (k < nfull) {
-      wait_steps<L, NT>(k == 0 ? min(NS - 1, nfull - 1) : min(NS - 2, nfull - 1 - k),
+    if (k < nd) {
+      wait_steps<L, NT>(k == 0 ? min(NS - 1, nd - 1) : min(NS - 2, nd - 1 - k),
                         kPrefetchTail && has_tail && k < NS);
     } else {
-      if (!kPrefetchTail) tail_load(k * kBK);
-      tail_store(k % NS);
+      if constexpr (!kDmaTail) {
+        if (!kPrefetchTail) tail_load(k * kBK);
+        tail_store(k % NS);
+      }
     }
     __syncthreads();
+    if constexpr (kDmaTail) {
+      if (k == nfull && has_tail) {
+        // zero the clamped k-rows (past the group) of both operands
+        const int kv = K - nfull * kBK;
+        uint16_t* ta = stages + (k % NS) * kStage;
+        uint16_t* tb = ta + BM * kBK;
+        for (int u = tid; u < kBK * BM / 8; u += NTH)
+          if (u / (BM / 8) >= kv) st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), zero128());
+        for (int u = tid; u < kBK * BN / 8; u += NTH)
+          if (u / (BN / 8) >= kv) st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), zero128());
+        __syncthreads();
+      }
+    }
   };
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    if (s < nfull) dma_step(s, s * kBK);
+    if (s < nd) issue_step(s, s);
   if (kPrefetchTail && has_tail) tail_load(nfull * kBK);
   // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
   auto inner = [&](int stage) {
@@ -412,7 +461,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       inner(stage);
       // last sub-step of step k (set 1, SUB is even) overlaps the first reads of step k+1
       publish(k + 1);
-      if (k + NS < nfull) dma_step(stage, (k + NS) * kBK);
+      if (k + NS < nd) issue_step(stage, k + NS);
       read_frags(std::integral_constant<int, 0>(), (k + 1) % NS, 0);
       mfmas(std::integral_constant<int, 1>());
       interleave();
