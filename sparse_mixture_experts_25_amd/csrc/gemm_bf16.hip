@@ -126,6 +126,20 @@ struct DmaPlan {
 #pragma unroll
     for (int q = 0; q < Q; ++q) dma16s(voff[q], base, lds_tile + (wave * Q + q) * 1024);
   }
+  // The partial last step of a K-contiguous operand (make_kc plan): 16-byte
+  // chunks at or past kv (kv a multiple of 8, 0 < kv < BK) read chunk 0 of
+  // their row instead; the caller zeroes them in LDS.
+  __device__ void issue_kc_tail(const uint16_t* base, uint32_t lds_tile, int wave, int lane, int kv) const {
+    constexpr int CPR = BK / 8;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int p = (wave * Q + q) * 64 + lane;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ kc_swz<BK>(r);
+      const uint32_t v = 8 * c < kv ? voff[q] : voff[q] - (uint32_t)(16 * c);
+      dma16s(v, base, lds_tile + (wave * Q + q) * 1024);
+    }
+  }
   // The partial last step of an MN-contiguous operand (make_mn plan): k-rows
   // at or past kv (1 <= kv < BK) read k-row kv-1 instead, so every address
   // stays inside the group; the caller zeroes those k-rows in LDS.
@@ -275,29 +289,30 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     pa.issue(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
     pb.issue(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
-  // weight gradients: the partial last step is one more direct-load step with
-  // clamped k-rows (both operands MN-contiguous)
+  // the partial last step as one more direct-load step with clamped addresses
   auto dma_tail = [&](int stage, int k0) {
     const uint32_t sa = lds0 + stage * kStage * 2;
     const uint32_t sb = sa + BM * kBK * 2;
-    pa.issue_mn_tail(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
-    pb.issue_mn_tail(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
+    if (A_KC) pa.issue_kc_tail(Aorig + k0, sa, wave, lane, K - k0);
+    else pa.issue_mn_tail(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
+    if (B_IS_KC) pb.issue_kc_tail(Borig + k0, sb, wave, lane, K - k0);
+    else pb.issue_mn_tail(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
   };
   // A partial last K step (k >= K reads as zero). Weight gradients have one in
-  // almost every group:
-  //   128x128 tiles: one more pipelined direct-load step with clamped k-rows,
-  //     whose k-rows past the group are zeroed in LDS once it lands (no
-  //     registers held across the loop, so four workgroups fit a CU);
-  //   256x256 tiles: registers with zero fill, loaded in the prologue right
-  //     after the first direct loads and written to LDS when the step is
-  //     published.
-  // Row-ragged matmuls (only ragged test shapes have a partial step):
-  // registers with zero fill, loaded when the step is published. Every lane
-  // issues exactly UA + UB register loads (clamped, in-bounds addresses; the
-  // value is masked afterwards), so the per-wave vmcnt accounting of the
-  // direct loads stays exact.
-  constexpr bool kDmaTail = (KIND == 1) && BM < 256;
+  // almost every group, row-ragged matmuls only when K is not a multiple of BK.
+  //   Default: one more pipelined direct-load step with clamped addresses
+  //     (k-rows of an MN-contiguous operand, 16-byte chunks of a K-contiguous
+  //     one), whose parts past K are zeroed in LDS once it lands. No registers
+  //     are held across the loop for it (four 128x128 weight-gradient
+  //     workgroups fit a CU).
+  //   256x256 weight-gradient tiles: registers with zero fill, loaded in the
+  //     prologue right after the first direct loads and written to LDS when
+  //     the step is published (faster there). Every lane issues exactly
+  //     UA + UB register loads (clamped, in-bounds addresses; the value is
+  //     masked afterwards), so the per-wave vmcnt accounting of the direct
+  //     loads stays exact.
   constexpr bool kPrefetchTail = (KIND == 1) && BM >= 256;
+  constexpr bool kDmaTail = !kPrefetchTail;
   constexpr int UA = BM * BK / 8 / NTH, UB = BN * BK / 8 / NTH;
   constexpr int NT = UA + UB;
   u128 tra[UA], trb[UB];
@@ -423,14 +438,24 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     __syncthreads();
     if constexpr (kDmaTail) {
       if (k == nfull && has_tail) {
-        // zero the clamped k-rows (past the group) of both operands
+        // zero what the clamped loads brought in past K, in both operands
         const int kv = K - nfull * kBK;
         uint16_t* ta = stages + (k % NS) * kStage;
         uint16_t* tb = ta + BM * kBK;
-        for (int u = tid; u < kBK * BM / 8; u += NTH)
-          if (u / (BM / 8) >= kv) st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), zero128());
-        for (int u = tid; u < kBK * BN / 8; u += NTH)
-          if (u / (BN / 8) >= kv) st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), zero128());
+        for (int u = tid; u < kBK * BM / 8; u += NTH) {
+          if (A_KC) {
+            if (8 * (u % (BK / 8)) >= kv) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
+          } else if (u / (BM / 8) >= kv) {
+            st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), zero128());
+          }
+        }
+        for (int u = tid; u < kBK * BN / 8; u += NTH) {
+          if (B_IS_KC) {
+            if (8 * (u % (BK / 8)) >= kv) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
+          } else if (u / (BN / 8) >= kv) {
+            st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), zero128());
+          }
+        }
         __syncthreads();
       }
     }
