@@ -147,6 +147,52 @@ def cpu_baseline(c, inp, budget_tokens):
                       f"{dt:.1f} s"}
 
 
+def measure_peaks(torch, M, reps=10):
+    """Attainable peaks from the probe kernels of include/moe_peaks.h (median of `reps` launches each)."""
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    sink = torch.empty(M.moe_peak_sink_bytes() // 4, dtype=torch.float32, device="cuda")
+    nb = 4 << 30  # far above the 256 MB last-level cache
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    M.moe_peak_write(src)  # touch every page before timing
+    out = {}
+    out["hbm_read_GBps"] = nb / timed(lambda: M.moe_peak_read(src, sink)) / 1e9
+    out["hbm_write_GBps"] = nb / timed(lambda: M.moe_peak_write(dst)) / 1e9
+    half = nb // 2
+    out["hbm_copy_GBps"] = 2 * half / timed(lambda: M.moe_peak_copy(dst, src, nbytes=half)) / 1e9
+    torch.cuda.synchronize()
+    del src, dst
+    it = 4000
+    out["mfma_bf16_TFLOPs"] = M.MOE_PEAK_BLOCKS * 4 * it * 4 * 32768 / timed(
+        lambda: M.moe_peak_mfma_bf16(sink, it)) / 1e12
+    it = 5000
+    out["fma_f32_TFLOPs"] = M.MOE_PEAK_BLOCKS * 256 * it * 64 * 2 / timed(lambda: M.moe_peak_fma_f32(sink, it)) / 1e12
+    # library context: the vendor GEMM on a large square bf16 product (not one of the layer's kernels)
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    out["torch_matmul_bf16_8192_TFLOPs"] = 2 * n ** 3 / timed(lambda: torch.matmul(a, b)) / 1e12
+    return {"peaks": {k: round(v, 1) for k, v in out.items()},
+            "published": {"hbm_GBps": PEAK_HBM / 1e9, "mfma_bf16_TFLOPs": PEAK_BF16 / 1e12,
+                          "fma_f32_TFLOPs": PEAK_F32_VALU / 1e12},
+            "probe": "include/moe_peaks.h kernels, median of %d launches; HBM buffers 4 GiB" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +212,9 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "kernel to scale HBM counters against)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the attainable HBM, matrix-core and fp32-ALU peaks with the library's probe "
+                         "kernels, print them as one JSON line and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
@@ -175,6 +224,10 @@ def main():
     import torch
     import sparse_mixture_experts_25_amd as M
     from synth import CONFIGS, make_inputs
+
+    if args.peaks:
+        print(json.dumps(measure_peaks(torch, M)), flush=True)
+        return
 
     c = CONFIGS[args.config]
     if c.fwd_only:

@@ -10,9 +10,12 @@
  * with no other thread calling the library meanwhile.
  *
  * Stage names (one stage = one kernel unless noted):
- *   "route", "dispatch" (4 kernels), "ffn_gemm1", "ffn_gemm2", "combine",
- *   "aux" (2 kernels), "bwd_combine", "bwd_dgrad2", "bwd_wgrad2", "bwd_dgrad1",
- *   "bwd_wgrad1", "bwd_dlogits", "bwd_router_grads" (3 kernels), "bwd_unpermute".
+ *   "route" (moe_route, moe_route_noisy), "route_ec" (moe_route_ec, several
+ *   kernels), "dispatch" (4 kernels), "ffn_gemm1", "ffn_gemm2", "combine",
+ *   "aux" (moe_aux_loss or moe_aux_noisy, 2 kernels), "bias_update",
+ *   "bias_quantile" (several kernels), "bwd_combine", "bwd_dgrad2",
+ *   "bwd_wgrad2", "bwd_dgrad1", "bwd_wgrad1", "bwd_dlogits",
+ *   "bwd_router_grads" (3 kernels), "bwd_unpermute".
  */
 #ifndef MOE_MI355X_PROFILE_H
 #define MOE_MI355X_PROFILE_H

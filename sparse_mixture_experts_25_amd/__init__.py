@@ -35,6 +35,12 @@ EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_disp
            "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
+# attainable-peak probes (include/moe_peaks.h), exported by the same library
+PEAK_EXPORTS = ["moe_peak_sink_bytes", "moe_peak_read", "moe_peak_write", "moe_peak_copy", "moe_peak_mfma_bf16",
+                "moe_peak_fma_f32"]
+MOE_PEAK_BLOCKS = 2048
+
+
 class MoeError(RuntimeError):
     pass
 
@@ -98,6 +104,15 @@ def lib():
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTS[:-1]:
+            getattr(L, n).restype = ctypes.c_int
+        L.moe_peak_sink_bytes.argtypes = []
+        L.moe_peak_sink_bytes.restype = ctypes.c_size_t
+        L.moe_peak_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+        L.moe_peak_write.argtypes = [_vp, ctypes.c_size_t, _vp]
+        L.moe_peak_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_peak_mfma_bf16.argtypes = [_vp, ctypes.c_int, _vp]
+        L.moe_peak_fma_f32.argtypes = [_vp, ctypes.c_int, _vp]
+        for n in PEAK_EXPORTS[1:]:
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -282,3 +297,37 @@ def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream
     weights = {k: inp.get(k) for k in ("w_router", "w1", "w2", "ws1", "ws2")}
     grads = {k: t.get(k) for k in ("dx", "dw_router", "dw1", "dw2", "dws1", "dws2")}
     moe_backward(buf.cfg, dy, sv, weights, grads, t["ws"], stream)
+
+
+# ---- attainable-peak probes (include/moe_peaks.h) ----
+
+def moe_peak_sink_bytes() -> int:
+    return int(lib().moe_peak_sink_bytes())
+
+
+def _peak_check(status: int, what: str):
+    if status != 0:
+        raise MoeError(f"{what}: status {status}")
+
+
+def moe_peak_read(src, sink, nbytes=None, stream=None):
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _peak_check(lib().moe_peak_read(_p(src), n, _p(sink), _stream(stream)), "moe_peak_read")
+
+
+def moe_peak_write(dst, nbytes=None, stream=None):
+    n = dst.numel() * dst.element_size() if nbytes is None else nbytes
+    _peak_check(lib().moe_peak_write(_p(dst), n, _stream(stream)), "moe_peak_write")
+
+
+def moe_peak_copy(dst, src, nbytes=None, stream=None):
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _peak_check(lib().moe_peak_copy(_p(dst), _p(src), n, _stream(stream)), "moe_peak_copy")
+
+
+def moe_peak_mfma_bf16(sink, iters, stream=None):
+    _peak_check(lib().moe_peak_mfma_bf16(_p(sink), int(iters), _stream(stream)), "moe_peak_mfma_bf16")
+
+
+def moe_peak_fma_f32(sink, iters, stream=None):
+    _peak_check(lib().moe_peak_fma_f32(_p(sink), int(iters), _stream(stream)), "moe_peak_fma_f32")

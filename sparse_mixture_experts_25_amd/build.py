@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "router.hip", "router_bwd.hip", "ec_route.hip", "balance.hip", "noisy.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "rows.hip"]
+SOURCES = ["api.hip", "router.hip", "router_bwd.hip", "ec_route.hip", "balance.hip", "noisy.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "rows.hip", "peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

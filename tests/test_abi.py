@@ -13,9 +13,9 @@ from synth import CONFIGS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_symbols():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+def header_symbols(name="moe.h"):
+    src = open(os.path.join(ROOT, "include", name)).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
 
 
 def cfg_of(c, **kw):
@@ -30,6 +30,37 @@ def test_library_exports_every_header_symbol():
     L = M.lib()
     for s in syms:
         assert hasattr(L, s), s
+
+
+def test_every_header_is_covered():
+    heads = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert heads == ["moe.h", "moe_peaks.h", "moe_profile.h"]
+    L = M.lib()
+    for s in header_symbols("moe_profile.h"):
+        assert s in ("moe_profile_arm", "moe_profile_disarm", "moe_profile_stage"), s
+        assert hasattr(L, s), s
+    syms = header_symbols("moe_peaks.h")
+    assert set(syms) == set(M.PEAK_EXPORTS)
+    L = M.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    src = open(os.path.join(ROOT, "include", "moe_peaks.h")).read()
+    assert int(re.search(r"#define MOE_PEAK_BLOCKS (\d+)", src).group(1)) == M.MOE_PEAK_BLOCKS
+    assert M.moe_peak_sink_bytes() == M.MOE_PEAK_BLOCKS * 256 * 4
+
+
+def test_peak_probes_validate_before_launch():
+    L = M.lib()
+    sink = ctypes.c_void_p(1 << 20)
+    assert L.moe_peak_read(None, 1024, sink, None) == -1
+    assert L.moe_peak_read(ctypes.c_void_p(1 << 30), 1000, sink, None) == -1   # not a multiple of 16
+    assert L.moe_peak_read(ctypes.c_void_p((1 << 30) + 8), 1024, sink, None) == -1  # misaligned
+    assert L.moe_peak_write(None, 1024, None) == -1
+    assert L.moe_peak_write(ctypes.c_void_p(1 << 30), 0, None) == -1
+    # overlapping copy ranges
+    assert L.moe_peak_copy(ctypes.c_void_p((1 << 30) + 512), ctypes.c_void_p(1 << 30), 1024, None) == -1
+    assert L.moe_peak_mfma_bf16(sink, 0, None) == -1
+    assert L.moe_peak_fma_f32(None, 10, None) == -1
 
 
 def test_status_strings():
