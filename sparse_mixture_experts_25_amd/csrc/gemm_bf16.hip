@@ -380,35 +380,52 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   // on LDS. Before the first fragments of step k+1 are read, that step is
   // published (its direct loads waited for, one barrier); the LDS slot of step
   // k is then free (all its fragments are in registers) and receives step k+NS.
+  // 128x128 tiles free it one barrier earlier, right after the sub-steps that
+  // read it, so NS-1 later steps are in flight while step k+1 is waited for.
+  //
+  // 128x128 tiles: the wave's 32-row blocks interleave with the other wave
+  // row's (block i of wave row wm holds tile rows (2i + wm) * 32 .. +32), so
+  // the valid rows of a short group split evenly over the SIMDs, and in the
+  // row-ragged kinds the blocks wholly past the group's rows skip their
+  // fragment reads and matrix work: the loop runs with FMV = the count of live
+  // blocks (a compile-time value per instantiation), every instantiation with
+  // the same barriers. 256x256 tiles: wave row wm holds rows wm * 128 .. +128.
+  constexpr bool kInterleave = BM < 256;
+  auto brow = [&](int i) { return kInterleave ? (2 * i + wm) * 32 : wm * WM + i * 32; };
   constexpr int SUB = kBK / 16;  // even: sub-step s always uses register set s & 1
-  constexpr int RD = FM * (A_KC ? 1 : 2) + FN * (B_IS_KC ? 1 : 2);  // LDS reads per sub-step
-  constexpr int MF = FM * FN;                                         // MFMAs per sub-step
   bf16x8 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](auto set, int stage, int s) {
+  auto read_frags = [&](auto fmv, auto set, int stage, int s) {
+    constexpr int FMV = decltype(fmv)::value;
     constexpr int S = decltype(set)::value;
     const uint16_t* ta = stages + stage * kStage;
     const uint16_t* tb = ta + BM * kBK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[S][i] = A_KC ? frag_kc<BK>(ta, wm * WM + i * 32, s, lane) : frag_mn<BM>(ta, wm * WM + i * 32, s, lane);
+    for (int i = 0; i < FMV; ++i)
+      fa[S][i] = A_KC ? frag_kc<BK>(ta, brow(i), s, lane) : frag_mn<BM>(ta, brow(i), s, lane);
+    if (FMV > 0) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[S][j] = B_IS_KC ? frag_kc<BK>(tb, wn * WN + j * 32, s, lane) : frag_mn<BN>(tb, wn * WN + j * 32, s, lane);
+      for (int j = 0; j < FN; ++j)
+        fb[S][j] = B_IS_KC ? frag_kc<BK>(tb, wn * WN + j * 32, s, lane) : frag_mn<BN>(tb, wn * WN + j * 32, s, lane);
+    }
   };
-  auto mfmas = [&](auto set) {
+  auto mfmas = [&](auto fmv, auto set) {
+    constexpr int FMV = decltype(fmv)::value;
     constexpr int S = decltype(set)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMV; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S][i], fb[S][j], acc[i][j], 0, 0, 0);
   };
-  auto interleave = [&]() {
+  auto interleave = [&](auto fmv) {
     // one LDS read, then a share of the MFMAs, RD times
+    constexpr int FMV = decltype(fmv)::value;
+    constexpr int RD = FMV == 0 ? 0 : FMV * (A_KC ? 1 : 2) + FN * (B_IS_KC ? 1 : 2);  // LDS reads per sub-step
+    constexpr int MF = FMV * FN;                                                      // MFMAs per sub-step
 #pragma unroll
     for (int r = 0; r < RD; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (MF + RD - 1) / RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RD > 0 ? (MF + RD - 1) / RD : 1, 0);
     }
   };
 
@@ -416,6 +433,10 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   const int nk = nfull + ((K % kBK) ? 1 : 0);
   const bool has_tail = nk > nfull;
   const int nd = kDmaTail ? nk : nfull;  // steps brought in by direct loads
+  // 128x128 tiles (weight-streaming shapes) refill a slot as soon as every
+  // wave has read it, one barrier earlier than the publish of the next step;
+  // 256x256 tiles (matrix-bound) save that barrier
+  constexpr bool kEarly = BM < 256;
   auto issue_step = [&](int stage, int k) {
     if (!kDmaTail || k < nfull) dma_step(stage, k * kBK);
     else dma_tail(stage, k * kBK);
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   // later step.
   auto publish = [&](int k) {
     if (k < nd) {
-      wait_steps<L, NT>(k == 0 ? min(NS - 1, nd - 1) : min(NS - 2, nd - 1 - k),
+      wait_steps<L, NT>(kEarly || k == 0 ? min(NS - 1, nd - 1 - k) : min(NS - 2, nd - 1 - k),
                         kPrefetchTail && has_tail && k < NS);
     } else {
       if constexpr (!kDmaTail) {
@@ -464,35 +485,55 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   for (int s = 0; s < NS; ++s)
     if (s < nd) issue_step(s, s);
   if (kPrefetchTail && has_tail) tail_load(nfull * kBK);
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
-  auto inner = [&](int stage) {
+  auto inner = [&](auto fmv, int stage) {
 #pragma unroll
     for (int s = 0; s + 1 < SUB; ++s) {
       if (s & 1) {
-        read_frags(std::integral_constant<int, 0>(), stage, s + 1);
-        mfmas(std::integral_constant<int, 1>());
+        read_frags(fmv, Set0(), stage, s + 1);
+        mfmas(fmv, Set1());
       } else {
-        read_frags(std::integral_constant<int, 1>(), stage, s + 1);
-        mfmas(std::integral_constant<int, 0>());
+        read_frags(fmv, Set1(), stage, s + 1);
+        mfmas(fmv, Set0());
       }
-      interleave();
+      interleave(fmv);
     }
   };
-  if (nk > 0) {
+  auto main_loop = [&](auto fmv) {
     publish(0);
-    read_frags(std::integral_constant<int, 0>(), 0, 0);
+    read_frags(fmv, Set0(), 0, 0);
     for (int k = 0; k + 1 < nk; ++k) {
       const int stage = k % NS;
-      inner(stage);
+      inner(fmv, stage);
+      // every fragment of step k is in registers once all waves pass this
+      // barrier (it waits for the wave's LDS reads): its slot takes step k+NS
+      // before step k+1 is waited for, so NS-1 later steps stay in flight
+      if (kEarly && k + NS < nd) {
+        __syncthreads();
+        issue_step(stage, k + NS);
+      }
       // last sub-step of step k (set 1, SUB is even) overlaps the first reads of step k+1
       publish(k + 1);
-      if (k + NS < nd) issue_step(stage, k + NS);
-      read_frags(std::integral_constant<int, 0>(), (k + 1) % NS, 0);
-      mfmas(std::integral_constant<int, 1>());
-      interleave();
+      if (!kEarly && k + NS < nd) issue_step(stage, k + NS);
+      read_frags(fmv, Set0(), (k + 1) % NS, 0);
+      mfmas(fmv, Set1());
+      interleave(fmv);
     }
-    inner((nk - 1) % NS);
-    mfmas(std::integral_constant<int, 1>());
+    inner(fmv, (nk - 1) % NS);
+    mfmas(fmv, Set1());
+  };
+  if (nk > 0) {
+    if constexpr (KIND == 0 && kInterleave && FM == 2) {
+      // live blocks of this wave: those with (2i + wm) * 32 < a_valid
+      const int nvb = __builtin_amdgcn_readfirstlane(a_valid > 64 + wm * 32 ? 2 : (a_valid > wm * 32 ? 1 : 0));
+      if (nvb == 2) main_loop(std::integral_constant<int, 2>());
+      else if (nvb == 1) main_loop(std::integral_constant<int, 1>());
+      else main_loop(std::integral_constant<int, 0>());
+    } else {
+      main_loop(std::integral_constant<int, FM>());
+    }
   }
   __syncthreads();
 
@@ -504,17 +545,18 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   const uint16_t* X = reinterpret_cast<const uint16_t*>(sh ? a.X_sh : a.X);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
+    // the blocks (of every wave, or of wave row `half`) whose rows fall in this half
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (kInterleave ? (i < half * FM / 2 || i >= (half + 1) * FM / 2) : wm != half) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int n = wn * WN + j * 32 + (lane & 31);
-            Cs[m * CP + n] = acc[i][j][e];
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int m = brow(i) - half * HM + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int n = wn * WN + j * 32 + (lane & 31);
+          Cs[m * CP + n] = acc[i][j][e];
+        }
     }
     __syncthreads();
     const int mbase = half * HM;  // tile row of Cs row 0
@@ -716,7 +758,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   if (a.kind == 1)
     return a.epi == EPI_STORE_F32 ? launch_t<128, 128, 32, 2, 1, 0, EPI_STORE_F32>(a, st)
                                   : launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
-  return launch_tiles<128, 128, 32, 3>(a, st);
+  return launch_tiles<128, 128, 64, 2>(a, st);
 }
 
 }  // namespace moe
