@@ -69,6 +69,20 @@ def measured_traffic(workload, stage):
     return val
 
 
+def attainable_peak(bound):
+    """What the probe kernels of include/moe_peaks.h reach on MI355X
+    (profiles/attainable_peaks.txt (JSON), from `bench.py --peaks`), in the roofline's
+    unit: the higher of the streaming read and write rates for "hbm", the
+    register-only MFMA loop for "mfma", the fp32 FMA loop for "alu"."""
+    path = os.path.join(ROOT, "profiles", "attainable_peaks.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        pk = json.load(fh)["peaks"]
+    return {"hbm": max(pk["hbm_read_GBps"], pk["hbm_write_GBps"]), "mfma": pk["mfma_bf16_TFLOPs"],
+            "alu": pk["fma_f32_TFLOPs"]}.get(bound)
+
+
 class HipEvents:
     """Raw HIP events (for the library's stage timing hook)."""
 
@@ -310,6 +324,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": by / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    att = attainable_peak(roof["bound"])
+    if att:
+        roof["attainable_peak"] = att
+        roof["frac_attainable"] = roof["achieved"] / att
     roof["traffic"] = measured_traffic(c.name, dom)
     roof["kernel"] = dom
     roof["launch_ms"] = dom_ms
