@@ -29,6 +29,13 @@ __device__ __forceinline__ u128 ld128(const void* p) {
 __device__ __forceinline__ void st128(void* p, const u128& r) {
   *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }
+// 16-byte store with the non-temporal (streaming) cache policy, for outputs
+// that are written once and not read again soon.
+__device__ __forceinline__ void st128_nt(void* p, const u128& r) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {r.w[0], r.w[1], r.w[2], r.w[3]};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ u128 zero128() {
   u128 r;
   r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0u;

@@ -51,6 +51,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // The global address is a per-lane 32-bit byte offset (VGPR) plus a
 // wave-uniform 64-bit base (SGPR pair), so a K step only moves the base.
 // M0 holds the LDS address for the instruction and is restored afterwards.
+// NT: non-temporal (streaming) cache policy, for data read once.
+template <bool NT = false>
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds_block) {
   // readfirstlane returns int: widen through uint32_t, never sign-extend a half
   const uint64_t b = (uint64_t)(uintptr_t)base;
@@ -58,15 +60,26 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_block))
-      : "memory");
+  if (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_block))
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_block))
+        : "memory");
 }
 
 template <int N>
@@ -122,13 +135,15 @@ struct DmaPlan {
       voff[q] = (uint32_t)(((int64_t)kr * ld + 8 * cc) * 2);
     }
   }
+  template <bool NT>
   __device__ void issue(const uint16_t* base, uint32_t lds_tile, int wave) const {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) dma16s(voff[q], base, lds_tile + (wave * Q + q) * 1024);
+    for (int q = 0; q < Q; ++q) dma16s<NT>(voff[q], base, lds_tile + (wave * Q + q) * 1024);
   }
   // The partial last step of a K-contiguous operand (make_kc plan): 16-byte
   // chunks at or past kv (kv a multiple of 8, 0 < kv < BK) read chunk 0 of
   // their row instead; the caller zeroes them in LDS.
+  template <bool NT>
   __device__ void issue_kc_tail(const uint16_t* base, uint32_t lds_tile, int wave, int lane, int kv) const {
     constexpr int CPR = BK / 8;
 #pragma unroll
@@ -137,12 +152,13 @@ struct DmaPlan {
       const int r = p / CPR;
       const int c = (p % CPR) ^ kc_swz<BK>(r);
       const uint32_t v = 8 * c < kv ? voff[q] : voff[q] - (uint32_t)(16 * c);
-      dma16s(v, base, lds_tile + (wave * Q + q) * 1024);
+      dma16s<NT>(v, base, lds_tile + (wave * Q + q) * 1024);
     }
   }
   // The partial last step of an MN-contiguous operand (make_mn plan): k-rows
   // at or past kv (1 <= kv < BK) read k-row kv-1 instead, so every address
   // stays inside the group; the caller zeroes those k-rows in LDS.
+  template <bool NT>
   __device__ void issue_mn_tail(const uint16_t* base, uint32_t lds_tile, int wave, int lane, int kv,
                                 int64_t ld) const {
     constexpr int CPR = R / 8;
@@ -150,7 +166,7 @@ struct DmaPlan {
     for (int q = 0; q < Q; ++q) {
       const int kr = ((wave * Q + q) * 64 + lane) / CPR;
       const uint32_t v = kr < kv ? voff[q] : voff[q] - (uint32_t)((int64_t)(kr - kv + 1) * ld * 2);
-      dma16s(v, base, lds_tile + (wave * Q + q) * 1024);
+      dma16s<NT>(v, base, lds_tile + (wave * Q + q) * 1024);
     }
   }
 };
@@ -283,20 +299,25 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       return nb * BN + (r < b_valid ? r : b_valid - 1);
     });
   else pb.make_mn(wave, lane, a.ldb, b_valid);
+  // Row-ragged 128x128 launches (groups under 256 rows on average): each
+  // group's weight slab is read by one or two row tiles, adjacent in time, so
+  // the weight loads stream past the caches (non-temporal) and leave L2 to the
+  // activation tiles, which every column tile re-reads.
+  constexpr bool kStreamB = KIND == 0 && BM < 256;
   auto dma_step = [&](int stage, int k0) {
     const uint32_t sa = lds0 + stage * kStage * 2;
     const uint32_t sb = sa + BM * kBK * 2;
-    pa.issue(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
-    pb.issue(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
+    pa.template issue<false>(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
+    pb.template issue<kStreamB>(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
   // the partial last step as one more direct-load step with clamped addresses
   auto dma_tail = [&](int stage, int k0) {
     const uint32_t sa = lds0 + stage * kStage * 2;
     const uint32_t sb = sa + BM * kBK * 2;
-    if (A_KC) pa.issue_kc_tail(Aorig + k0, sa, wave, lane, K - k0);
-    else pa.issue_mn_tail(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
-    if (B_IS_KC) pb.issue_kc_tail(Borig + k0, sb, wave, lane, K - k0);
-    else pb.issue_mn_tail(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
+    if (A_KC) pa.template issue_kc_tail<false>(Aorig + k0, sa, wave, lane, K - k0);
+    else pa.template issue_mn_tail<false>(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
+    if (B_IS_KC) pb.template issue_kc_tail<kStreamB>(Borig + k0, sb, wave, lane, K - k0);
+    else pb.template issue_mn_tail<kStreamB>(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
   };
   // A partial last K step (k >= K reads as zero). Weight gradients have one in
   // almost every group, row-ragged matmuls only when K is not a multiple of BK.
@@ -599,8 +620,9 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
             reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
             continue;
           }
+          // weight gradients are written once and not read in this pass
           uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
-          st128(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
+          st128_nt(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
           continue;
         }
         const int col = nb * BN + n;
