@@ -297,6 +297,7 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g1.has_shared = sh ? 1 : 0;
   g1.offsets = expert_offsets; g1.E = E; g1.shared_rows = shr;
   g1.max_rows = R;
+  g1.row_cap = C > 0 ? C : 0;
   g1.A = x_perm; g1.lda = d;
   g1.B = w1; g1.ldb = d; g1.strideB = (int64_t)f1 * d;
   g1.A_sh = x; g1.B_sh = ws1;
@@ -312,6 +313,7 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g2.has_shared = sh ? 1 : 0;
   g2.offsets = expert_offsets; g2.E = E; g2.shared_rows = shr;
   g2.max_rows = R;
+  g2.row_cap = C > 0 ? C : 0;
   g2.A = h_saved; g2.lda = f;
   g2.B = w2; g2.ldb = f; g2.strideB = (int64_t)d * f;
   g2.A_sh = h_shared; g2.B_sh = ws2;
@@ -428,6 +430,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a2.has_shared = sh ? 1 : 0;
   a2.offsets = sv->expert_offsets; a2.E = E; a2.shared_rows = shr;
   a2.max_rows = R;
+  a2.row_cap = C > 0 ? C : 0;
   a2.A = dO; a2.lda = d;
   a2.B = w->w2; a2.ldb = f; a2.strideB = (int64_t)d * f;
   a2.A_sh = dy; a2.B_sh = w->ws2;
@@ -449,6 +452,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w2g.M = d; w2g.N = f;
   w2g.has_shared = sh ? 1 : 0;
   w2g.max_rows = R;
+  w2g.row_cap = C > 0 ? C : 0;
   w2g.order = order;
   w2g.offsets = sv->expert_offsets; w2g.E = E; w2g.shared_rows = shr;
   w2g.A = dO; w2g.lda = d;
@@ -465,6 +469,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a1.has_shared = sh ? 1 : 0;
   a1.offsets = sv->expert_offsets; a1.E = E; a1.shared_rows = shr;
   a1.max_rows = R;
+  a1.row_cap = C > 0 ? C : 0;
   a1.A = dA; a1.lda = f1;
   a1.B = w->w1; a1.ldb = d; a1.strideB = (int64_t)f1 * d;
   a1.A_sh = dA_sh; a1.B_sh = w->ws1;
@@ -477,6 +482,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w1g.M = f1; w1g.N = d;
   w1g.has_shared = sh ? 1 : 0;
   w1g.max_rows = R;
+  w1g.row_cap = C > 0 ? C : 0;
   w1g.order = order;
   w1g.offsets = sv->expert_offsets; w1g.E = E; w1g.shared_rows = shr;
   w1g.A = dA; w1g.lda = f1;

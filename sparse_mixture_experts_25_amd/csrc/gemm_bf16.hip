@@ -774,7 +774,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // 256x256 tiles also need enough of them to give every CU a workgroup
   const int64_t big_tiles = a.kind == 0 ? ((a.max_rows + 255) / 256) * ((a.N + 255) / 256)
                                         : (groups + (a.has_shared ? 1 : 0)) * ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) && big_tiles >= 256;
+  // Groups capped at 512 rows or fewer (expert capacity) stay on 128x128 tiles
+  // even when the cap allows 256-row tiles: routing that drops tokens leaves
+  // most groups well under the cap, and the weight-streaming small tiles were
+  // faster there (T = 16384, d = 1024, f = 4096, E = 64, C = 512 with about
+  // two thirds of the assignments dropped: 1.76 -> 1.62 ms per layer step).
+  const bool capped = a.row_cap > 0 && a.row_cap <= 512;
+  const bool big = avg_rows >= 256 && !capped && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) &&
+                   big_tiles >= 256;
   if (big) return launch_tiles<256, 256, 32, 3, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
   if (a.kind == 1)

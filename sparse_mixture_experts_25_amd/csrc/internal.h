@@ -112,6 +112,7 @@ struct GemmArgs {
   const void* X; int64_t ldx; const void* X_sh;
   int f;  // SwiGLU half width
   const int32_t* slot; int slot_k; const void* Y; const void* Y_sh;  // EPI_UNPERMUTE
+  int row_cap;  // most rows any routed group can have (expert capacity), 0: no bound but max_rows
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // order[0..E(+1)): groups sorted by row count, largest first (ties: lower index;

@@ -28,6 +28,10 @@ CASES["big_tiles_swiglu"] = LayerConfig("big_tiles_swiglu", T=2048, d=264, f=392
                                         logit_offset="normal")
 CASES["big_tiles_relu_drops"] = LayerConfig("big_tiles_relu_drops", T=2048, d=296, f=520, E=4, k=1,
                                             act="relu", cf=1.1, alpha=0.01, logit_offset="normal")
+# expert capacity 512: groups of up to 512 rows stay on the 128x128 tiles (four row
+# tiles re-reading one streamed weight slab)
+CASES["capped_512_relu"] = LayerConfig("capped_512_relu", T=2048, d=264, f=392, E=4, k=1, act="relu", cf=1.0,
+                                       alpha=0.01, logit_offset="normal")
 # the square-root-softplus gate with the selection bias, with and without renormalisation
 CASES["sqrt_softplus_bf16"] = SMALL["deepseek_v3"].replace(name="sqrt_softplus_bf16", gate="sqrt_softplus_bias",
                                                            alpha=0.01)
