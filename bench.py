@@ -69,6 +69,31 @@ def measured_traffic(workload, stage):
     return val
 
 
+def stage_roofline(stage, work, ms, dtype="bf16"):
+    """Roofline of one launch of `stage` with (flops, bytes) = work taking `ms`:
+    the exact fp32 router stages on the vector units (the logits always; the
+    router gradients of fp32 layers) against the fp32 ALU, the grouped matmuls
+    against the matrix cores when their arithmetic intensity is past the ridge
+    point (else HBM), everything else against HBM (including the bf16 layers'
+    router gradients, which run as split-operand matrix products)."""
+    fl, by = work
+    if stage in ("route", "route_ec") or (stage == "bwd_router_grads" and dtype != "bf16"):
+        # exact fp32 router: sequential fp32 FMA on the vector units
+        roof = {"bound": "alu", "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12,
+                "unit": "TFLOP/s"}
+    elif fl and fl / max(by, 1) > PEAK_BF16 / PEAK_HBM and stage.startswith(("ffn", "bwd_dgrad", "bwd_wgrad")):
+        roof = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    att = attainable_peak(roof["bound"])
+    if att:
+        roof["attainable_peak"] = att
+        roof["frac_attainable"] = roof["achieved"] / att
+    return roof
+
+
 def attainable_peak(bound):
     """What the probe kernels of include/moe_peaks.h reach on MI355X
     (profiles/attainable_peaks.txt (JSON), from `bench.py --peaks`), in the roofline's
@@ -313,21 +338,7 @@ def main():
     rows = int(offs[-1])
     ne = int(((offs[1:] - offs[:-1]) > 0).sum())
     work = stage_work(c, rows, ne)
-    fl, by = work[dom]
-    if dom in ("route", "route_ec", "bwd_router_grads"):
-        # exact fp32 router: sequential fp32 FMA on the vector units
-        roof = {"bound": "alu", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12,
-                "unit": "TFLOP/s"}
-    elif fl and fl / max(by, 1) > PEAK_BF16 / PEAK_HBM and dom.startswith(("ffn", "bwd_dgrad", "bwd_wgrad")):
-        roof = {"bound": "mfma", "achieved": fl / (dom_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": by / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    att = attainable_peak(roof["bound"])
-    if att:
-        roof["attainable_peak"] = att
-        roof["frac_attainable"] = roof["achieved"] / att
+    roof = stage_roofline(dom, work[dom], dom_ms, c.dtype)
     roof["traffic"] = measured_traffic(c.name, dom)
     roof["kernel"] = dom
     roof["launch_ms"] = dom_ms
@@ -350,6 +361,10 @@ def main():
                    "capacity_factor": c.cf, "act": c.act, "gate": c.gate, "kept_rows": rows,
                    "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12},
         "roofline": roof,
+        # every stage against its own roofline, from the per-stage pre-pass times
+        "stage_roofline": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv
+                               for kk, vv in stage_roofline(k, work[k], v, c.dtype).items() if kk != "peak"}
+                           for k, v in per_stage.items() if k in work},
     }
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
