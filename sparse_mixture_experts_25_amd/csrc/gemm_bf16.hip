@@ -239,6 +239,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       r0 = 0;
       rows = a.shared_rows;
     }
+    if (!group_in_part(a, rows)) return;  // the other launch of a split matmul
   }
   const bool sh = g >= a.E;
   const uint16_t* Ab = reinterpret_cast<const uint16_t*>(sh ? a.A_sh : a.A);
@@ -774,20 +775,35 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // 256x256 tiles also need enough of them to give every CU a workgroup
   const int64_t big_tiles = a.kind == 0 ? ((a.max_rows + 255) / 256) * ((a.N + 255) / 256)
                                         : (groups + (a.has_shared ? 1 : 0)) * ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  // Groups capped at 512 rows or fewer (expert capacity) stay on 128x128 tiles
-  // even when the cap allows 256-row tiles: routing that drops tokens leaves
-  // most groups well under the cap, and the weight-streaming small tiles were
-  // faster there (T = 16384, d = 1024, f = 4096, E = 64, C = 512 with about
-  // two thirds of the assignments dropped: 1.76 -> 1.62 ms per layer step).
-  const bool capped = a.row_cap > 0 && a.row_cap <= 512;
-  const bool big = avg_rows >= 256 && !capped && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) &&
+  const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) &&
                    big_tiles >= 256;
-  if (big) return launch_tiles<256, 256, 32, 3, 4>(a, st);
   // short contractions (one or two K steps per tile): two stages suffice
-  if (a.kind == 1)
-    return a.epi == EPI_STORE_F32 ? launch_t<128, 128, 32, 2, 1, 0, EPI_STORE_F32>(a, st)
-                                  : launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(a, st);
-  return launch_tiles<128, 128, 64, 2>(a, st);
+  auto small_tiles = [&](const GemmArgs& s) {
+    if (s.kind == 1)
+      return s.epi == EPI_STORE_F32 ? launch_t<128, 128, 32, 2, 1, 0, EPI_STORE_F32>(s, st)
+                                    : launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(s, st);
+    return launch_tiles<128, 128, 64, 2>(s, st);
+  };
+  if (!big) return small_tiles(a);
+  // Groups capped at 512 rows or fewer (expert capacity): the host knows only
+  // the cap, and the realised groups range from full (expert choice, balanced
+  // routing) to mostly empty (skewed routing that drops most assignments). The
+  // matmul then runs as two launches over the groups, each deciding on the
+  // device from the group's row count: 256 rows or more on 256x256 tiles, the
+  // others (and empty ones) on the weight-streaming 128x128 tiles. Dropless
+  // layers keep one launch: there the zero-fill of empty experts overlaps the
+  // big groups' matrix work, which a second launch would serialise.
+  const bool capped = a.row_cap > 0 && a.row_cap <= 512 && a.E > 1;
+  if (!capped) return launch_tiles<256, 256, 32, 3, 4>(a, st);
+  GemmArgs b = a;
+  b.split_part = 1;
+  b.split_rows = 256;
+  const hipError_t e = launch_tiles<256, 256, 32, 3, 4>(b, st);
+  if (e != hipSuccess) return e;
+  GemmArgs sm = a;
+  sm.split_part = 2;
+  sm.split_rows = 256;
+  return small_tiles(sm);
 }
 
 }  // namespace moe

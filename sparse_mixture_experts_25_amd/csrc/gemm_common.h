@@ -18,7 +18,15 @@ struct TileInfo {
 // Upper bound on the number of row tiles of a ragged-M launch: sum over the
 // groups of ceil(rows_g / BM) <= ceil(R / BM) + E (+ the shared group's tiles).
 __host__ __device__ inline int64_t row_tile_bound(const GemmArgs& a, int BM) {
-  return (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
+  const int64_t b = (a.max_rows + BM - 1) / BM + a.E + (a.shared_rows + BM - 1) / BM;
+  if (a.split_part != 2) return b;
+  // only groups under split_rows rows: at most ceil(split_rows / BM) tiles each
+  const int64_t s = (int64_t)(a.E + 1) * ((a.split_rows + BM - 1) / BM);
+  return s < b ? s : b;
+}
+// whether a group with `rows` rows belongs to this launch (GemmArgs::split_part)
+__host__ __device__ inline bool group_in_part(const GemmArgs& a, int rows) {
+  return a.split_part == 0 || (a.split_part == 1 ? rows >= a.split_rows : rows < a.split_rows);
 }
 
 // XCD-aware grouped rasterization. The dispatcher hands workgroup ids to the
@@ -68,7 +76,7 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
       const int g = lane * per + i;
       if (g < ngroups) {
         const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        local += (rows + BM - 1) / BM;
+        if (group_in_part(a, rows)) local += (rows + BM - 1) / BM;
       }
     }
     int64_t incl = local;
@@ -90,7 +98,7 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
       const int g = lane * per + i;
       if (g < ngroups) {
         const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        local += (rows + BM - 1) / BM;
+        if (group_in_part(a, rows)) local += (rows + BM - 1) / BM;
       }
     }
     int64_t incl = local;
@@ -104,7 +112,7 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
       for (int i = 0; i < per; ++i) {
         const int g = lane * per + i;
         const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        const int64_t nt = (rows + BM - 1) / BM;
+        const int64_t nt = group_in_part(a, rows) ? (rows + BM - 1) / BM : 0;
         if (row < accum + nt) {
           lds[0] = g;
           lds[1] = (g < a.E) ? a.offsets[g] : 0;

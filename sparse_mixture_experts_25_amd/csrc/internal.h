@@ -113,6 +113,10 @@ struct GemmArgs {
   int f;  // SwiGLU half width
   const int32_t* slot; int slot_k; const void* Y; const void* Y_sh;  // EPI_UNPERMUTE
   int row_cap;  // most rows any routed group can have (expert capacity), 0: no bound but max_rows
+  // set by launch_gemm_bf16 when one grouped matmul runs as two launches:
+  // 0 all groups; 1 only groups with at least split_rows rows (the extra dense
+  // group counts shared_rows); 2 only groups with fewer
+  int split_part; int split_rows;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // order[0..E(+1)): groups sorted by row count, largest first (ties: lower index;
