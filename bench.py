@@ -40,11 +40,17 @@ GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "mfma_tile.h", "internal.h", "
 
 
 def sources_sha(names):
+    """Hash of the kernel sources with comments and blank space removed, so an
+    edit to comments alone keeps a measured figure valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_25_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_25_amd", "csrc", n)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,24 +13,27 @@
 //     over that group's rows; a group without rows writes zeros. Groups run
 //     largest first.
 //
-// Main loop: an NS-stage pipeline over BK-deep K steps. Every full step is
+// Main loop: an NS-stage pipeline over BK-deep K steps. Every step is
 // brought into LDS with direct global->LDS 16-byte loads (each wave fills
 // 1 KB blocks; lane i of a load lands at +16*i, so the XOR swizzle of the LDS
 // layout is applied by choosing which global chunk each lane fetches). Up to
 // NS-1 steps are in flight while the matrix cores work on the current one; a
-// per-wave vmcnt wait plus one barrier per step publishes a stage. A ragged
-// K tail (last partial step) goes through registers with zero fill.
-//   K-contiguous operand ([rows][K] in memory): LDS rows of BK k, 16-byte
-//     chunk c of row r at c ^ (r & 7); fragments read with ds_read_b128.
+// per-wave vmcnt wait plus one barrier per step publishes a stage. A partial
+// last K step loads clamped addresses and zeroes what lies past K in LDS
+// (the 256x256 weight gradients load it through registers with zero fill).
+//   K-contiguous operand ([rows][K] in memory): LDS rows of BK k, with the
+//     16-byte chunks XOR-swizzled by row (mfma_tile.h); fragments read with
+//     ds_read_b128.
 //   MN-contiguous operand ([K][rows] in memory, the gradient matmuls): LDS
-//     k-rows as in memory, chunk c of k-row k at (c & ~7) | ((c ^ k) & 7);
-//     fragments read with the gfx950 LDS transpose read (ds_read_b64_tr_b16),
-//     which turns a 4(k) x 16(mn) block into per-lane k-vectors.
-// Four waves, each owning a (BM/2) x (BN/2) sub-tile computed with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Rows or columns past the end
-// of a group read clamped (finite) data and are never stored. The epilogue
-// stages the fp32 tile in LDS (half at a time) and writes 16-byte rows, fusing
-// the activation (forward) or its derivative (backward).
+//     k-rows as in memory with the chunks swizzled by k-row; fragments read
+//     with the gfx950 LDS transpose read (ds_read_b64_tr_b16), which turns a
+//     4(k) x 16(mn) block into per-lane k-vectors.
+// Two wave rows by WGN wave columns (4 or 8 waves), each wave computing its
+// sub-tile with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Rows or
+// columns past the end of a group read clamped (finite) data and are never
+// stored. The epilogue stages the fp32 tile in LDS (half at a time) and
+// writes 16-byte rows, fusing the activation (forward) or its derivative
+// (backward), or the unpermute of the input gradient.
 #include <type_traits>
 
 #include "gemm_common.h"
