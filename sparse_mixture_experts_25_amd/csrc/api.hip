@@ -499,6 +499,12 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   } else if (T > 0) {
     moe::DlogitsArgs dla{sv->probs, ec ? nullptr : sv->topk_idx, sv->topk_w, dg, sv->expert_counts, dl, T, E, k, c->gate,
                          c->renormalize ? 1 : 0, c->aux_alpha};
+    if (c->dtype == MOE_DT_BF16) {  // the split operands straight from the dlogits kernel
+      dla.dlogits = nullptr;
+      dla.gx = (uint16_t*)(base + L.gx);
+      dla.gw = (uint16_t*)(base + L.gw);
+      dla.kp = moe::router_dx_k(E);
+    }
     StageTimer pt("bwd_dlogits", s);
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;
   }
@@ -509,6 +515,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   moe::RouterGradArgs rg{dl, sv->x, w->w_router, g->dw_router, dxr, part, (uint16_t*)(base + L.gx),
                          (uint16_t*)(base + L.gw), (uint16_t*)(base + L.wsp), (int32_t*)(base + L.offs), T, d,
                          (int)router_rows(c), c->dtype, dy, sv->slot, k, dXp, dX_sh, fuse_dx ? g->dx : nullptr};
+  rg.split_done = (!noisy && T > 0 && c->dtype == MOE_DT_BF16) ? 1 : 0;
   {
     StageTimer pt("bwd_router_grads", s);
     if ((st = launch_status(moe::launch_router_grads(rg, s)))) return st;

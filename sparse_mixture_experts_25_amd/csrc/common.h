@@ -49,6 +49,23 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   bf16 h = (bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+
+// An fp32 value as three bf16 terms hi + mid + lo (each the RNE rounding of
+// what the previous terms leave), exact to about 2^-24 relative: products of
+// two such terms are exact in fp32, so fp32-accumulated bf16 matrix products
+// of the terms reproduce fp32 products.
+struct Split3 {
+  uint16_t h, m, l;
+};
+__device__ __forceinline__ Split3 split3(float v) {
+  Split3 s;
+  s.h = f2bf(v);
+  const float r1 = v - bf2f(s.h);
+  s.m = f2bf(r1);
+  const float r2 = r1 - bf2f(s.m);
+  s.l = f2bf(r2);
+  return s;
+}
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }

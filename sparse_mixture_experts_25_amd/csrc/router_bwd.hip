@@ -26,18 +26,6 @@ namespace moe {
 
 namespace {
 
-struct Split3 {
-  uint16_t h, m, l;
-};
-__device__ __forceinline__ Split3 split3(float v) {
-  Split3 s;
-  s.h = f2bf(v);
-  const float r1 = v - bf2f(s.h);
-  s.m = f2bf(r1);
-  const float r2 = r1 - bf2f(s.m);
-  s.l = f2bf(r2);
-  return s;
-}
 
 // Split operands, all of width Kp = router_dx_k(E):
 //   gx[t]  = [g_hi | g_hi | g_mid | 0 ...]      dx_r:   gx[t] . wsp[:, j]
@@ -49,9 +37,10 @@ __device__ __forceinline__ Split3 split3(float v) {
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ g, const float* __restrict__ w,
                                                            int T, int E, int d, int kp, int nsw, int chunk,
                                                            uint16_t* __restrict__ gx, uint16_t* __restrict__ gw,
-                                                           uint16_t* __restrict__ wsp, int32_t* __restrict__ offs) {
+                                                           uint16_t* __restrict__ wsp, int32_t* __restrict__ offs,
+                                                           int tokens_done) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t ng = (int64_t)T * (kp / 8);
+  const int64_t ng = tokens_done ? 0 : (int64_t)T * (kp / 8);
   if (u <= nsw) offs[2 + u] = (int)min((int64_t)u * chunk, (int64_t)T);
   if (u == 0) {
     offs[0] = 0;
@@ -152,10 +141,10 @@ hipError_t launch_router_dw_gemm(const RouterGradArgs& a, hipStream_t st) {
   const int kp = router_dx_k(a.E);
   const int nsw = router_dw_splits(a.T, a.E, a.d);
   const int chunk = (a.T + nsw - 1) / nsw;
-  const int64_t n = (int64_t)a.T * (kp / 8) + (int64_t)kp * (a.d / 8);
+  const int64_t n = (a.split_done ? 0 : (int64_t)a.T * (kp / 8)) + (int64_t)kp * (a.d / 8);
   const int64_t nthreads = n > nsw + 1 ? n : nsw + 1;
   hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a.dlogits,
-                     a.w_router, a.T, a.E, a.d, kp, nsw, chunk, a.gx, a.gw, a.wsplit, a.offs);
+                     a.w_router, a.T, a.E, a.d, kp, nsw, chunk, a.gx, a.gw, a.wsplit, a.offs, a.split_done);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmArgs g{};

@@ -201,7 +201,8 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
                                                       const float* __restrict__ dg,
                                                       const int32_t* __restrict__ counts,
                                                       float* __restrict__ dlogits, int T, int E, int k, int gate,
-                                                      int renorm, float alpha) {
+                                                      int renorm, float alpha, uint16_t* __restrict__ gx,
+                                                      uint16_t* __restrict__ gw, int kp) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -262,8 +263,25 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
       }
       if (alpha != 0.0f) v += c * (float)counts[j] * invTk * gd;
     }
-    dlogits[(int64_t)t * E + j] = v;
+    if (dlogits) dlogits[(int64_t)t * E + j] = v;
+    if (gx) {
+      // gx[t] = [hi | hi | mid | 0 ...], gw[t] = [hi | mid | lo | 0 ...]
+      const Split3 sp = split3(v);
+      uint16_t* xr = gx + (int64_t)t * kp;
+      uint16_t* wr = gw + (int64_t)t * kp;
+      xr[j] = sp.h;
+      xr[E + j] = sp.h;
+      xr[2 * E + j] = sp.m;
+      wr[j] = sp.h;
+      wr[E + j] = sp.m;
+      wr[2 * E + j] = sp.l;
+    }
   }
+  if (gx)
+    for (int cp = 3 * E + lane; cp < kp; cp += 64) {
+      gx[(int64_t)t * kp + cp] = 0;
+      gw[(int64_t)t * kp + cp] = 0;
+    }
 }
 
 // C[M,N] (+)= sum_k A[k,m] * B[k,n] over one chunk of k (fp32 SIMT, 64x64 tiles).
@@ -453,7 +471,7 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
 
 hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(dlogits_kernel, dim3((a.T + 3) / 4), dim3(256), 0, st, a.probs, a.topk_idx, a.topk_w, a.dg,
-                     a.counts, a.dlogits, a.T, a.E, a.k, a.gate, a.renorm, a.alpha);
+                     a.counts, a.dlogits, a.T, a.E, a.k, a.gate, a.renorm, a.alpha, a.gx, a.gw, a.kp);
   return hipGetLastError();
 }
 
