@@ -175,6 +175,20 @@ def stage_work(c, rows, ne_experts):
     }
 
 
+def cpu_sample_tokens(c, ref_tokens=6144):
+    """Tokens of `c` whose oracle forward+backward costs about as much as
+    `ref_tokens` of the Switch-Base-shaped layer (flops per token of the expert
+    FFNs, shared expert and router)."""
+    from synth import CONFIGS
+
+    def per_token(x):
+        f1 = 2 * x.f if x.act == "swiglu" else x.f
+        return 2 * x.d * (f1 + x.f) * (x.k + (1 if x.shared else 0)) + 2 * x.d * x.E
+
+    n = int(ref_tokens * per_token(CONFIGS["switch_base"]) / per_token(c))
+    return max(64, min(c.T, n))
+
+
 def cpu_baseline(c, inp, budget_tokens):
     """Oracle forward+backward of the same layer on the first `budget_tokens` tokens
     (an independent batch of that size; capacity follows the formula for it)."""
@@ -251,7 +265,9 @@ def main():
                     help="expert_choice: every expert takes its top tokens (k = E, capacity from cf)")
     ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias", "noisy_topk"],
                     help="override the workload's gate (a bias-carrying gate draws the selection bias)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="oracle sample size for cpu_baseline (default: 6144 tokens of the Switch-Base-shaped "
+                         "layer, about 10-15 s of host work, or a sample of the same estimated cost)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -384,7 +400,8 @@ def main():
         print(json.dumps({"stage_ms": per_stage}), file=sys.stderr)
     line["stage_ms"] = {k: round(v, 4) for k, v in per_stage.items()}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, {k: v for k, v in inp.items()}, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(c, {k: v for k, v in inp.items()},
+                                            args.cpu_tokens or cpu_sample_tokens(c))
     print(json.dumps(line), flush=True)
 
 
