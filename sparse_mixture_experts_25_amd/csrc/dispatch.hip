@@ -26,7 +26,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kChunk = 2048;      // assignments per chunk
+constexpr int kChunk = 1024;      // assignments per chunk
 constexpr int kSub = kChunk / 4;  // assignments per wave inside a chunk
 
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int total, int E,
