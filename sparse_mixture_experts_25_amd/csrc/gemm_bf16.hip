@@ -19,8 +19,7 @@
 // layout is applied by choosing which global chunk each lane fetches). Up to
 // NS-1 steps are in flight while the matrix cores work on the current one; a
 // per-wave vmcnt wait plus one barrier per step publishes a stage. A partial
-// last K step loads clamped addresses and zeroes what lies past K in LDS
-// (the 256x256 weight gradients load it through registers with zero fill).
+// last K step loads clamped addresses and zeroes what lies past K in LDS.
 //   K-contiguous operand ([rows][K] in memory): LDS rows of BK k, with the
 //     16-byte chunks XOR-swizzled by row (mfma_tile.h); fragments read with
 //     ds_read_b128.
@@ -90,21 +89,15 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait until at most `steps` later pipeline steps (L loads each) are in flight
-// Wait until at most steps * L + X vector-memory instructions of this wave
-// are outstanding (X: younger non-step loads, 0 or NT).
-template <int L, int X>
-__device__ __forceinline__ void wait_steps_x(int steps) {
-  if (steps <= 0) wait_vm<X>();
-  else if (steps == 1) wait_vm<L + X>();
-  else if (steps == 2) wait_vm<2 * L + X>();
-  else if (steps == 3) wait_vm<3 * L + X>();
-  else wait_vm<4 * L + X>();
-}
-template <int L, int NT>
-__device__ __forceinline__ void wait_steps(int steps, bool tail_younger) {
-  if (tail_younger) wait_steps_x<L, NT>(steps);
-  else wait_steps_x<L, 0>(steps);
+// wait until at most `steps` later pipeline steps (L loads each) of this wave
+// are in flight
+template <int L>
+__device__ __forceinline__ void wait_steps(int steps) {
+  if (steps <= 0) wait_vm<0>();
+  else if (steps == 1) wait_vm<L>();
+  else if (steps == 2) wait_vm<2 * L>();
+  else if (steps == 3) wait_vm<3 * L>();
+  else wait_vm<4 * L>();
 }
 
 // Per-lane byte offsets of the direct loads of one tile, computed once per
@@ -175,17 +168,17 @@ struct DmaPlan {
 };
 
 // ------------------------------------------------------------ kernel
-// WGN waves along N (2 along M): 4 waves for 128x128 tiles (three workgroups
-// per CU) and for 256x256 tiles with 128x128 per wave (one wave per SIMD), or 8
-// waves for 256x256 tiles with 128x64 per wave (two waves per SIMD, so one
-// wave's matrix work covers the other's waits).
-// 128x128 weight-gradient tiles fit 128 registers (four workgroups per CU):
-// their short contractions are latency-bound, so more of them in flight pays.
-template <int WGN, int BM, int BN, int KIND>
-constexpr int waves_per_simd() { return WGN == 4 ? 2 : (BM * BN >= 65536 ? 1 : (KIND == 1 ? 4 : 3)); }
+// WGN waves along N (2 along M): 4 waves for 128x128 tiles, or 8 waves for
+// 256x256 tiles with 128x64 per wave (two waves per SIMD, so one wave's matrix
+// work covers the other's waits). Row-ragged 128x128 tiles are held to the
+// registers of three workgroups per CU (their 64 KB of LDS admits two);
+// weight-gradient tiles fit 128 registers (four workgroups per CU): their
+// short contractions are latency-bound, so more of them in flight pays.
+template <int WGN, int KIND>
+constexpr int waves_per_simd() { return WGN == 4 ? 2 : (KIND == 1 ? 4 : 3); }
 
 template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN>
-__global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, BM, BN, KIND>(), waves_per_simd<WGN, BM, BN, KIND>()))) void gemm_bf16_kernel(
+__global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, KIND>(), waves_per_simd<WGN, KIND>()))) void gemm_bf16_kernel(
     GemmArgs a) {
   constexpr int kBK = BK;
   constexpr int NW = 2 * WGN, NTH = 64 * NW;  // waves, threads
@@ -323,73 +316,12 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     if (B_IS_KC) pb.template issue_kc_tail<kStreamB>(Borig + k0, sb, wave, lane, K - k0);
     else pb.template issue_mn_tail<kStreamB>(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
   };
-  // A partial last K step (k >= K reads as zero). Weight gradients have one in
-  // almost every group, row-ragged matmuls only when K is not a multiple of BK.
-  //   Default: one more pipelined direct-load step with clamped addresses
-  //     (k-rows of an MN-contiguous operand, 16-byte chunks of a K-contiguous
-  //     one), whose parts past K are zeroed in LDS once it lands. No registers
-  //     are held across the loop for it (four 128x128 weight-gradient
-  //     workgroups fit a CU).
-  //   256x256 weight-gradient tiles: registers with zero fill, loaded in the
-  //     prologue right after the first direct loads and written to LDS when
-  //     the step is published (faster there). Every lane issues exactly
-  //     UA + UB register loads (clamped, in-bounds addresses; the value is
-  //     masked afterwards), so the per-wave vmcnt accounting of the direct
-  //     loads stays exact.
-  constexpr bool kPrefetchTail = (KIND == 1) && BM >= 256;
-  constexpr bool kDmaTail = !kPrefetchTail;
-  constexpr int UA = BM * BK / 8 / NTH, UB = BN * BK / 8 / NTH;
-  constexpr int NT = UA + UB;
-  u128 tra[UA], trb[UB];
-  auto tail_load = [&](int k0) {
-    const int kv = K - k0;
-#pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * NTH;
-      if (A_KC) {
-        const int r = u / (BK / 8), c = u % (BK / 8);
-        const bool ok = 8 * c < kv;
-        const u128 v = ld128(a_row(r, k0) + 8 * (ok ? c : 0));
-        tra[i] = ok ? v : zero128();
-      } else {
-        const int kr = u / (BM / 8), c = u % (BM / 8);
-        const bool ok = kr < kv && c < a_valid;
-        const u128 v = ld128(Aorig + (int64_t)(k0 + (kr < kv ? kr : kv - 1)) * a.lda + 8 * (c < a_valid ? c : a_valid - 1));
-        tra[i] = ok ? v : zero128();
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < UB; ++i) {
-      const int u = tid + i * NTH;
-      if (B_IS_KC) {
-        const int r = u / (BK / 8), c = u % (BK / 8);
-        const bool ok = 8 * c < kv;
-        const u128 v = ld128(b_row(r, k0) + 8 * (ok ? c : 0));
-        trb[i] = ok ? v : zero128();
-      } else {
-        const int kr = u / (BN / 8), c = u % (BN / 8);
-        const bool ok = kr < kv && c < b_valid;
-        const u128 v = ld128(Borig + (int64_t)(k0 + (kr < kv ? kr : kv - 1)) * a.ldb + 8 * (c < b_valid ? c : b_valid - 1));
-        trb[i] = ok ? v : zero128();
-      }
-    }
-  };
-  auto tail_store = [&](int stage) {
-    uint16_t* ta = stages + stage * kStage;
-    uint16_t* tb = ta + BM * kBK;
-#pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int u = tid + i * NTH;
-      if (A_KC) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), tra[i]);
-      else st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), tra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < UB; ++i) {
-      const int u = tid + i * NTH;
-      if (B_IS_KC) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), trb[i]);
-      else st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), trb[i]);
-    }
-  };
+  // A partial last K step (k >= K reads as zero; weight gradients have one in
+  // almost every group, row-ragged matmuls only when K is not a multiple of
+  // BK) is one more pipelined direct-load step with clamped addresses (k-rows
+  // of an MN-contiguous operand, 16-byte chunks of a K-contiguous one), whose
+  // parts past K are zeroed in LDS once it lands. No registers are held across
+  // the loop for it.
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -457,59 +389,45 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   const int nfull = K / kBK;
   const int nk = nfull + ((K % kBK) ? 1 : 0);
   const bool has_tail = nk > nfull;
-  const int nd = kDmaTail ? nk : nfull;  // steps brought in by direct loads
   // 128x128 tiles (weight-streaming shapes) refill a slot as soon as every
   // wave has read it, one barrier earlier than the publish of the next step;
   // 256x256 tiles (matrix-bound) save that barrier
   constexpr bool kEarly = BM < 256;
   auto issue_step = [&](int stage, int k) {
-    if (!kDmaTail || k < nfull) dma_step(stage, k * kBK);
+    if (k < nfull) dma_step(stage, k * kBK);
     else dma_tail(stage, k * kBK);
   };
-  // Direct loads issued before publish(k): steps 0 .. min(NS-1, nd-1) for
-  // k = 0 (prologue); steps 0 .. min(k+NS-2, nd-1) for k >= 1. The wait lets
-  // the later ones stay in flight. Prefetched tail loads follow the
-  // prologue's direct loads: younger than steps 0 .. NS-1, older than every
-  // later step.
+  // Direct loads issued before publish(k): steps 0 .. min(NS-1, nk-1) for
+  // k = 0 (prologue); steps 0 .. min(k+NS-2, nk-1) for k >= 1. The wait lets
+  // the later ones stay in flight.
   auto publish = [&](int k) {
-    if (k < nd) {
-      wait_steps<L, NT>(kEarly || k == 0 ? min(NS - 1, nd - 1 - k) : min(NS - 2, nd - 1 - k),
-                        kPrefetchTail && has_tail && k < NS);
-    } else {
-      if constexpr (!kDmaTail) {
-        if (!kPrefetchTail) tail_load(k * kBK);
-        tail_store(k % NS);
-      }
-    }
+    wait_steps<L>(kEarly || k == 0 ? min(NS - 1, nk - 1 - k) : min(NS - 2, nk - 1 - k));
     __syncthreads();
-    if constexpr (kDmaTail) {
-      if (k == nfull && has_tail) {
-        // zero what the clamped loads brought in past K, in both operands
-        const int kv = K - nfull * kBK;
-        uint16_t* ta = stages + (k % NS) * kStage;
-        uint16_t* tb = ta + BM * kBK;
-        for (int u = tid; u < kBK * BM / 8; u += NTH) {
-          if (A_KC) {
-            if (8 * (u % (BK / 8)) >= kv) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
-          } else if (u / (BM / 8) >= kv) {
-            st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), zero128());
-          }
+    if (k == nfull && has_tail) {
+      // zero what the clamped loads brought in past K, in both operands
+      const int kv = K - nfull * kBK;
+      uint16_t* ta = stages + (k % NS) * kStage;
+      uint16_t* tb = ta + BM * kBK;
+      for (int u = tid; u < kBK * BM / 8; u += NTH) {
+        if (A_KC) {
+          if (8 * (u % (BK / 8)) >= kv) st128(ta + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
+        } else if (u / (BM / 8) >= kv) {
+          st128(ta + mn_off<BM>(u / (BM / 8), u % (BM / 8)), zero128());
         }
-        for (int u = tid; u < kBK * BN / 8; u += NTH) {
-          if (B_IS_KC) {
-            if (8 * (u % (BK / 8)) >= kv) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
-          } else if (u / (BN / 8) >= kv) {
-            st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), zero128());
-          }
-        }
-        __syncthreads();
       }
+      for (int u = tid; u < kBK * BN / 8; u += NTH) {
+        if (B_IS_KC) {
+          if (8 * (u % (BK / 8)) >= kv) st128(tb + kc_off<BK>(u / (BK / 8), u % (BK / 8)), zero128());
+        } else if (u / (BN / 8) >= kv) {
+          st128(tb + mn_off<BN>(u / (BN / 8), u % (BN / 8)), zero128());
+        }
+      }
+      __syncthreads();
     }
   };
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    if (s < nd) issue_step(s, s);
-  if (kPrefetchTail && has_tail) tail_load(nfull * kBK);
+    if (s < nk) issue_step(s, s);
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
   // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
@@ -535,13 +453,13 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       // every fragment of step k is in registers once all waves pass this
       // barrier (it waits for the wave's LDS reads): its slot takes step k+NS
       // before step k+1 is waited for, so NS-1 later steps stay in flight
-      if (kEarly && k + NS < nd) {
+      if (kEarly && k + NS < nk) {
         __syncthreads();
         issue_step(stage, k + NS);
       }
       // last sub-step of step k (set 1, SUB is even) overlaps the first reads of step k+1
       publish(k + 1);
-      if (!kEarly && k + NS < nd) issue_step(stage, k + NS);
+      if (!kEarly && k + NS < nk) issue_step(stage, k + NS);
       read_frags(fmv, Set0(), (k + 1) % NS, 0);
       mfmas(fmv, Set1());
       interleave(fmv);
@@ -765,13 +683,13 @@ hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, in
 }
 
 // Tile choice: 256x256 on eight waves (128x64 each, two waves per SIMD;
-// 32-deep K steps, three stages, one workgroup per CU) when the groups are
-// large enough to fill it on average; otherwise 128x128 on four waves
-// (32-deep K steps, three stages, 48 KB of LDS and at most 168 registers per
-// lane, so that three workgroups share a CU and their loads overlap each
-// other's matrix work and epilogues: small expert batches, where the weights
-// stream from HBM and the row tile is mostly padding). 64-deep K steps do not
-// fit the register file with the transposed-operand fragment reads.
+// 64-deep K steps, two stages, one workgroup per CU) when the groups are large
+// enough to fill it on average. Otherwise 128x128 on four waves: row-ragged
+// matmuls with 64-deep steps and two stages (two workgroups per CU, a full
+// 128-byte line per weight row and step), weight gradients with 32-deep steps
+// and two stages (four workgroups per CU: their one to three steps per tile
+// are latency-bound). Those are the small expert batches, where the weights
+// stream from HBM and the row tile is mostly padding.
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = a.E > 0 ? a.E : 1;
   const int64_t avg_rows = a.max_rows / groups;
@@ -797,11 +715,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // layers keep one launch: there the zero-fill of empty experts overlaps the
   // big groups' matrix work, which a second launch would serialise.
   const bool capped = a.row_cap > 0 && a.row_cap <= 512 && a.E > 1;
-  if (!capped) return launch_tiles<256, 256, 32, 3, 4>(a, st);
+  if (!capped) return launch_tiles<256, 256, 64, 2, 4>(a, st);
   GemmArgs b = a;
   b.split_part = 1;
   b.split_rows = 256;
-  const hipError_t e = launch_tiles<256, 256, 32, 3, 4>(b, st);
+  const hipError_t e = launch_tiles<256, 256, 64, 2, 4>(b, st);
   if (e != hipSuccess) return e;
   GemmArgs sm = a;
   sm.split_part = 2;
