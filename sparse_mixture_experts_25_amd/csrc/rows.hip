@@ -53,10 +53,164 @@ __device__ __forceinline__ int kept_columns(const int32_t* __restrict__ srow, in
   return n;
 }
 
-// y[t] = x[t] + sum_kept w[t,r] * y_perm[slot[t,r]] (+ y_shared[t]), kept
-// columns in ascending r
-template <typename TX, bool WIDE>
-__global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, const TX* __restrict__ y_perm,
+// Narrow token tables (k <= KM <= 8): one token per wave. The token's slots
+// and weights are read once (wave-uniform); for each 16-byte vector of the row
+// the loads of all k rows are issued before any of them is summed, so a lane
+// has k + 1 loads in flight. A dropped column (slot < 0) loads the token's own
+// row of the first operand instead (always valid memory) and is not summed.
+template <int KM>
+struct TokenCols {
+  int s[KM];
+  float w[KM];
+  __device__ void load(const int32_t* __restrict__ slot, const float* __restrict__ topk_w, int64_t t, int k) {
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      s[r] = r < k ? slot[t * k + r] : -1;
+      w[r] = r < k && topk_w ? topk_w[t * k + r] : 0.0f;
+    }
+  }
+};
+
+// combine for k <= KM: y[t] = x[t] + sum_kept w y_perm[s] (+ y_shared[t]), ascending r
+template <typename TX, int KM>
+__global__ __launch_bounds__(256) void combine_narrow_kernel(const TX* __restrict__ x, const TX* __restrict__ y_perm,
+                                                             const int32_t* __restrict__ slot,
+                                                             const float* __restrict__ topk_w,
+                                                             const TX* __restrict__ y_shared, TX* __restrict__ y,
+                                                             int T, int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);  // wave-uniform: scalar table reads
+  if (t >= T) return;
+  TokenCols<KM> c;
+  c.load(slot, topk_w, t, k);
+  const TX* xr = x + (int64_t)t * d;
+  const TX* rows[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? y_perm + (int64_t)c.s[r] * d : xr;
+  for (int v = lane; v < d / V; v += 64) {
+    u128 raw[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    float acc[V], tmp[V];
+    Elem<TX>::unpack(ld128(xr + v * V), acc);
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      if (c.s[r] < 0) continue;
+      Elem<TX>::unpack(raw[r], tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = __builtin_fmaf(c.w[r], tmp[e], acc[e]);
+    }
+    if (y_shared) {
+      Elem<TX>::unpack(ld128(y_shared + (int64_t)t * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    st128(y + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  }
+}
+
+// combine backward for k <= KM: dO[s] = w dy[t] and dg[t,r] = <dy[t], y_perm[s]>
+// for every kept column; dg = 0 for dropped ones. dy is read once per token.
+template <typename TX, int KM>
+__global__ __launch_bounds__(256) void combine_bwd_narrow_kernel(const TX* __restrict__ dy,
+                                                                 const TX* __restrict__ y_perm,
+                                                                 const int32_t* __restrict__ slot,
+                                                                 const float* __restrict__ topk_w,
+                                                                 TX* __restrict__ dO, float* __restrict__ dg, int T,
+                                                                 int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);  // wave-uniform: scalar table reads
+  if (t >= T) return;
+  TokenCols<KM> c;
+  c.load(slot, topk_w, t, k);
+  const TX* gr = dy + (int64_t)t * d;
+  const TX* rows[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? y_perm + (int64_t)c.s[r] * d : gr;
+  float dot[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) dot[r] = 0.0f;
+  for (int v = lane; v < d / V; v += 64) {
+    u128 raw[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    float g[V], yv[V], o[V];
+    Elem<TX>::unpack(ld128(gr + v * V), g);
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      if (c.s[r] < 0) continue;
+      Elem<TX>::unpack(raw[r], yv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        dot[r] = __builtin_fmaf(g[e], yv[e], dot[r]);
+        o[e] = c.w[r] * g[e];
+      }
+      st128(dO + (int64_t)c.s[r] * d + v * V, Elem<TX>::pack(o));
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+    if (r >= k) break;
+    const float sum = wave_sum(dot[r]);
+    if (lane == 0) dg[(int64_t)t * k + r] = c.s[r] >= 0 ? sum : 0.0f;
+  }
+}
+
+// unpermute backward for k <= KM: dx = dy + sum_kept dX_perm[s] (ascending r)
+// (+ dx_router) (+ dx_shared)
+template <typename TX, int KM>
+__global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __restrict__ dy,
+                                                                   const TX* __restrict__ dX_perm,
+                                                                   const int32_t* __restrict__ slot,
+                                                                   const float* __restrict__ dx_router,
+                                                                   const TX* __restrict__ dx_shared,
+                                                                   TX* __restrict__ dx, int T, int d, int k) {
+  constexpr int V = Elem<TX>::kVec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);  // wave-uniform: scalar table reads
+  if (t >= T) return;
+  TokenCols<KM> c;
+  c.load(slot, nullptr, t, k);
+  const TX* gr = dy + (int64_t)t * d;
+  const TX* rows[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? dX_perm + (int64_t)c.s[r] * d : gr;
+  for (int v = lane; v < d / V; v += 64) {
+    u128 raw[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    float acc[V], tmp[V];
+    Elem<TX>::unpack(ld128(gr + v * V), acc);
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      if (c.s[r] < 0) continue;
+      Elem<TX>::unpack(raw[r], tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    if (dx_router) {
+      const float* pr = dx_router + (int64_t)t * d + v * V;
+#pragma unroll
+      for (int e = 0; e < V; e += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(pr + e);
+        acc[e] += q.x; acc[e + 1] += q.y; acc[e + 2] += q.z; acc[e + 3] += q.w;
+      }
+    }
+    if (dx_shared) {
+      Elem<TX>::unpack(ld128(dx_shared + (int64_t)t * d + v * V), tmp);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += tmp[e];
+    }
+    st128(dx + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  }
+}
+
+// Wide tables (k > 8): y[t] = x[t] + sum_kept w[t,r] * y_perm[slot[t,r]]
+// (+ y_shared[t]), kept columns (compacted first) in ascending r
+template <typename TX>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const TX* __restrict__ x, const TX* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot,
                                                       const float* __restrict__ topk_w,
                                                       const TX* __restrict__ y_shared, TX* __restrict__ y,
@@ -66,22 +220,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const TX* __restrict__ x, 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
-  int n = k;
-  const int32_t* ls = nullptr;
-  const int32_t* lr = nullptr;
-  if constexpr (WIDE) {
-    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
-    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
-    ls = lsb[wave];
-    lr = lrb[wave];
-  }
+  __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+  const int n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+  const int32_t* ls = lsb[wave];
+  const int32_t* lr = lrb[wave];
   for (int v = lane; v < nvec; v += 64) {
     float acc[V], tmp[V];
     Elem<TX>::unpack(ld128(x + (int64_t)t * d + v * V), acc);
     for (int i = 0; i < n; ++i) {
-      const int r = WIDE ? lr[i] : i;
-      const int s = WIDE ? ls[i] : slot[(int64_t)t * k + r];
-      if (s < 0) continue;
+      const int r = lr[i];
+      const int s = ls[i];
       const float w = topk_w[(int64_t)t * k + r];
       Elem<TX>::unpack(ld128(y_perm + (int64_t)s * d + v * V), tmp);
 #pragma unroll
@@ -148,8 +296,8 @@ __global__ __launch_bounds__(kAuxFin) void aux_final_kernel(const float* __restr
 }
 
 // dO[slot] = w * dy[t]; dg[t,r] = <dy[t], y_perm[slot]> (0 when dropped)
-template <typename TX, bool WIDE>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const TX* __restrict__ dy, const TX* __restrict__ y_perm,
+template <typename TX>
+__global__ __launch_bounds__(256) void combine_bwd_wide_kernel(const TX* __restrict__ dy, const TX* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot,
                                                           const float* __restrict__ topk_w, TX* __restrict__ dO,
                                                           float* __restrict__ dg, int T, int d, int k) {
@@ -158,24 +306,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TX* __restrict__
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
-  int n = k;
-  const int32_t* ls = nullptr;
-  const int32_t* lr = nullptr;
-  if constexpr (WIDE) {
-    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
-    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
-    ls = lsb[wave];
-    lr = lrb[wave];
-    for (int r = lane; r < k; r += 64)
-      if (slot[(int64_t)t * k + r] < 0) dg[(int64_t)t * k + r] = 0.0f;
-  }
+  __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+  const int n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+  const int32_t* ls = lsb[wave];
+  const int32_t* lr = lrb[wave];
+  for (int r = lane; r < k; r += 64)
+    if (slot[(int64_t)t * k + r] < 0) dg[(int64_t)t * k + r] = 0.0f;
   for (int i = 0; i < n; ++i) {
-    const int r = WIDE ? lr[i] : i;
-    const int s = WIDE ? ls[i] : slot[(int64_t)t * k + r];
-    if (s < 0) {
-      if (lane == 0) dg[(int64_t)t * k + r] = 0.0f;
-      continue;
-    }
+    const int r = lr[i];
+    const int s = ls[i];
     const float w = topk_w[(int64_t)t * k + r];
     float dot = 0.0f;
     for (int v = lane; v < nvec; v += 64) {
@@ -374,8 +513,8 @@ __global__ __launch_bounds__(256) void gemm_nn_f32_kernel(const float* __restric
 }
 
 // dx[t] = dy[t] + sum_kept dX_perm[slot] + dx_router[t] (+ dx_shared[t])
-template <typename TX, bool WIDE>
-__global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict__ dy,
+template <typename TX>
+__global__ __launch_bounds__(256) void unpermute_bwd_wide_kernel(const TX* __restrict__ dy,
                                                             const TX* __restrict__ dX_perm,
                                                             const int32_t* __restrict__ slot,
                                                             const float* __restrict__ dx_router,
@@ -386,19 +525,14 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
-  int n = k;
-  const int32_t* ls = nullptr;
-  if constexpr (WIDE) {
-    __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
-    n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
-    ls = lsb[wave];
-  }
+  __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
+  const int n = kept_columns(slot + (int64_t)t * k, k, lane, lsb[wave], lrb[wave]);
+  const int32_t* ls = lsb[wave];
   for (int v = lane; v < nvec; v += 64) {
     float acc[V], tmp[V];
     Elem<TX>::unpack(ld128(dy + (int64_t)t * d + v * V), acc);
     for (int i = 0; i < n; ++i) {
-      const int s = WIDE ? ls[i] : slot[(int64_t)t * k + i];
-      if (s < 0) continue;
+      const int s = ls[i];
       Elem<TX>::unpack(ld128(dX_perm + (int64_t)s * d + v * V), tmp);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
@@ -422,21 +556,27 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const TX* __restrict
 
 }  // namespace
 
-template <typename TX, bool WIDE>
+// k <= 8: the narrow kernels with KM = k rounded up to 1, 2, 4 or 8; wider
+// tables: the compacted kernels
+template <typename TX>
 void launch_combine_t(const CombineArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.x,
-                     (const TX*)a.y_perm, a.slot, a.topk_w, (const TX*)a.y_shared, (TX*)a.y, a.T, a.d, a.k);
+  const dim3 g((a.T + 3) / 4), b(256);
+#define MOE_LAUNCH(KM)                                                                                        \
+  hipLaunchKernelGGL((combine_narrow_kernel<TX, KM>), g, b, 0, st, (const TX*)a.x, (const TX*)a.y_perm, a.slot, \
+                     a.topk_w, (const TX*)a.y_shared, (TX*)a.y, a.T, a.d, a.k)
+  if (a.k <= 1) MOE_LAUNCH(1);
+  else if (a.k <= 2) MOE_LAUNCH(2);
+  else if (a.k <= 4) MOE_LAUNCH(4);
+  else if (a.k <= kWideK) MOE_LAUNCH(8);
+  else
+    hipLaunchKernelGGL((combine_wide_kernel<TX>), g, b, 0, st, (const TX*)a.x, (const TX*)a.y_perm, a.slot,
+                       a.topk_w, (const TX*)a.y_shared, (TX*)a.y, a.T, a.d, a.k);
+#undef MOE_LAUNCH
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  const bool wide = a.k > kWideK;
-  if (a.dtype == MOE_DT_BF16) {
-    if (wide) launch_combine_t<uint16_t, true>(a, st);
-    else launch_combine_t<uint16_t, false>(a, st);
-  } else {
-    if (wide) launch_combine_t<float, true>(a, st);
-    else launch_combine_t<float, false>(a, st);
-  }
+  if (a.dtype == MOE_DT_BF16) launch_combine_t<uint16_t>(a, st);
+  else launch_combine_t<float>(a, st);
   return hipGetLastError();
 }
 
@@ -451,21 +591,25 @@ hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename TX, bool WIDE>
+template <typename TX>
 void launch_combine_bwd_t(const CombineBwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((combine_bwd_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.dy,
-                     (const TX*)a.y_perm, a.slot, a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k);
+  const dim3 g((a.T + 3) / 4), b(256);
+#define MOE_LAUNCH(KM)                                                                                   \
+  hipLaunchKernelGGL((combine_bwd_narrow_kernel<TX, KM>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.y_perm, \
+                     a.slot, a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k)
+  if (a.k <= 1) MOE_LAUNCH(1);
+  else if (a.k <= 2) MOE_LAUNCH(2);
+  else if (a.k <= 4) MOE_LAUNCH(4);
+  else if (a.k <= kWideK) MOE_LAUNCH(8);
+  else
+    hipLaunchKernelGGL((combine_bwd_wide_kernel<TX>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.y_perm, a.slot,
+                       a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k);
+#undef MOE_LAUNCH
 }
 
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
-  const bool wide = a.k > kWideK;
-  if (a.dtype == MOE_DT_BF16) {
-    if (wide) launch_combine_bwd_t<uint16_t, true>(a, st);
-    else launch_combine_bwd_t<uint16_t, false>(a, st);
-  } else {
-    if (wide) launch_combine_bwd_t<float, true>(a, st);
-    else launch_combine_bwd_t<float, false>(a, st);
-  }
+  if (a.dtype == MOE_DT_BF16) launch_combine_bwd_t<uint16_t>(a, st);
+  else launch_combine_bwd_t<float>(a, st);
   return hipGetLastError();
 }
 
@@ -516,21 +660,25 @@ hipError_t launch_router_grads(const RouterGradArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename TX, bool WIDE>
+template <typename TX>
 void launch_unpermute_bwd_t(const UnpermuteArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((unpermute_bwd_kernel<TX, WIDE>), dim3((a.T + 3) / 4), dim3(256), 0, st, (const TX*)a.dy,
-                     (const TX*)a.dX_perm, a.slot, a.dx_router, (const TX*)a.dx_shared, (TX*)a.dx, a.T, a.d, a.k);
+  const dim3 g((a.T + 3) / 4), b(256);
+#define MOE_LAUNCH(KM)                                                                                     \
+  hipLaunchKernelGGL((unpermute_bwd_narrow_kernel<TX, KM>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.dX_perm, \
+                     a.slot, a.dx_router, (const TX*)a.dx_shared, (TX*)a.dx, a.T, a.d, a.k)
+  if (a.k <= 1) MOE_LAUNCH(1);
+  else if (a.k <= 2) MOE_LAUNCH(2);
+  else if (a.k <= 4) MOE_LAUNCH(4);
+  else if (a.k <= kWideK) MOE_LAUNCH(8);
+  else
+    hipLaunchKernelGGL((unpermute_bwd_wide_kernel<TX>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.dX_perm, a.slot,
+                       a.dx_router, (const TX*)a.dx_shared, (TX*)a.dx, a.T, a.d, a.k);
+#undef MOE_LAUNCH
 }
 
 hipError_t launch_unpermute_bwd(const UnpermuteArgs& a, hipStream_t st) {
-  const bool wide = a.k > kWideK;
-  if (a.dtype == MOE_DT_BF16) {
-    if (wide) launch_unpermute_bwd_t<uint16_t, true>(a, st);
-    else launch_unpermute_bwd_t<uint16_t, false>(a, st);
-  } else {
-    if (wide) launch_unpermute_bwd_t<float, true>(a, st);
-    else launch_unpermute_bwd_t<float, false>(a, st);
-  }
+  if (a.dtype == MOE_DT_BF16) launch_unpermute_bwd_t<uint16_t>(a, st);
+  else launch_unpermute_bwd_t<float>(a, st);
   return hipGetLastError();
 }
 
