@@ -504,6 +504,10 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
       dla.gx = (uint16_t*)(base + L.gx);
       dla.gw = (uint16_t*)(base + L.gw);
       dla.kp = moe::router_dx_k(E);
+      dla.w_router = w->w_router;
+      dla.wsplit = (uint16_t*)(base + L.wsp);
+      dla.offs = (int32_t*)(base + L.offs);
+      dla.d = d;
     }
     StageTimer pt("bwd_dlogits", s);
     if ((st = launch_status(moe::launch_dlogits(dla, s)))) return st;

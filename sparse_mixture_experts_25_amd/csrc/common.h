@@ -66,6 +66,34 @@ __device__ __forceinline__ Split3 split3(float v) {
   s.l = f2bf(r2);
   return s;
 }
+
+// Thread u of the router-weight split: the 16 bytes (8 values of row r) of the
+// split weights wsp [kp, d] = [W_hi ; W_mid ; W_hi ; 0 ...] (bf16), for
+// u < kp * d / 8, and the row ranges of the router products (offs[0..1] = the
+// single input-gradient group, offs[2 + c] = the first token of weight-gradient
+// chunk c, for c <= nsw). Threads past both do nothing.
+__device__ __forceinline__ void split_router_weights(int64_t u, const float* __restrict__ w, int E, int d, int kp,
+                                                     uint16_t* __restrict__ wsp, int T, int nsw, int chunk,
+                                                     int32_t* __restrict__ offs) {
+  if (u <= nsw) offs[2 + u] = (int)min((int64_t)u * chunk, (int64_t)T);
+  if (u == 0) {
+    offs[0] = 0;
+    offs[1] = T;
+  }
+  if (u >= (int64_t)kp * (d / 8)) return;
+  const int r = (int)(u / (d / 8)), j0 = (int)(u % (d / 8)) * 8;
+  const int e = r % E, band = r / E;
+  u128 o = zero128();
+  if (band < 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Split3 p = split3(w[(int64_t)e * d + j0 + 2 * i]), q = split3(w[(int64_t)e * d + j0 + 2 * i + 1]);
+      const uint16_t x0 = band == 1 ? p.m : p.h, x1 = band == 1 ? q.m : q.h;
+      o.w[i] = (uint32_t)x0 | ((uint32_t)x1 << 16);
+    }
+  }
+  st128(wsp + (int64_t)r * d + j0, o);
+}
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }

@@ -168,10 +168,11 @@ struct DlogitsArgs {
   float* dlogits;  // [T, E] (nullable when gx is set)
   int T, E, k, gate, renorm;
   float alpha;
-  // bf16 layers: also write the split operands of the router products
-  // (RouterGradArgs::gx, gw, router_dx_k(E) wide), so the split kernel only
-  // splits the router weights
+  // bf16 layers: also write every split operand of the router products
+  // (RouterGradArgs::gx, gw, wsplit, router_dx_k(E) wide) and their row ranges
+  // (offs), in extra workgroups for the weights, so no split kernel runs
   uint16_t* gx; uint16_t* gw; int kp;
+  const float* w_router; uint16_t* wsplit; int32_t* offs; int d;
 };
 hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st);
 
@@ -191,7 +192,7 @@ struct RouterGradArgs {
   // gradient, dx = dy + sum_kept dX_perm[slot] + dx_router (+ dx_shared), and
   // dx_router is not stored (dx non-null selects this)
   const void* dy; const int32_t* slot; int k; const void* dX_perm; const void* dX_sh; void* dx;
-  int split_done;  // gx and gw already written (by the dlogits kernel)
+  int split_done;  // gx, gw, wsplit and offs already written (by the dlogits kernel)
 };
 // width of the split operands: 3E rounded up to 8
 inline int router_dx_k(int E) { return (3 * E + 7) / 8 * 8; }

@@ -32,20 +32,15 @@ namespace {
 //   wsp    = [W_hi ; W_mid ; W_hi ; 0 ...]              = hi.hi + hi.mid + mid.hi
 //   gw[t]  = [g_hi | g_mid | g_lo | 0 ...]      dW_r:   sum_t gw[t][p E + e] x[t][j],
 //                                                       summed over the three bands p
-// One thread per 8 elements. Also writes the row ranges: offs[0..1] = the
-// single dx group, offs[2 + c] = the start of token chunk c of dW_r.
+// One thread per 8 elements; the weight threads also write the row ranges
+// (split_router_weights). bf16 layers with the plain gates get all of it from
+// the dlogits kernel instead.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ g, const float* __restrict__ w,
                                                            int T, int E, int d, int kp, int nsw, int chunk,
                                                            uint16_t* __restrict__ gx, uint16_t* __restrict__ gw,
-                                                           uint16_t* __restrict__ wsp, int32_t* __restrict__ offs,
-                                                           int tokens_done) {
+                                                           uint16_t* __restrict__ wsp, int32_t* __restrict__ offs) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t ng = tokens_done ? 0 : (int64_t)T * (kp / 8);
-  if (u <= nsw) offs[2 + u] = (int)min((int64_t)u * chunk, (int64_t)T);
-  if (u == 0) {
-    offs[0] = 0;
-    offs[1] = T;
-  }
+  const int64_t ng = (int64_t)T * (kp / 8);
   if (u < ng) {
     const int t = (int)(u / (kp / 8)), c0 = (int)(u % (kp / 8)) * 8;
     u128 ox, ow;
@@ -70,20 +65,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     st128(gw + (int64_t)t * kp + c0, ow);
     return;
   }
-  const int64_t v = u - ng;
-  if (v >= (int64_t)kp * (d / 8)) return;
-  const int r = (int)(v / (d / 8)), j0 = (int)(v % (d / 8)) * 8;
-  const int e = r % E, band = r / E;
-  u128 o = zero128();
-  if (band < 3) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const Split3 p = split3(w[(int64_t)e * d + j0 + 2 * i]), q = split3(w[(int64_t)e * d + j0 + 2 * i + 1]);
-      const uint16_t x0 = band == 1 ? p.m : p.h, x1 = band == 1 ? q.m : q.h;
-      o.w[i] = (uint32_t)x0 | ((uint32_t)x1 << 16);
-    }
-  }
-  st128(wsp + (int64_t)r * d + j0, o);
+  split_router_weights(u - ng, w, E, d, kp, wsp, T, nsw, chunk, offs);
 }
 
 // dW_r[e][j] = sum over chunks c and bands p of part[c][p E + e][j], in that
@@ -141,12 +123,14 @@ hipError_t launch_router_dw_gemm(const RouterGradArgs& a, hipStream_t st) {
   const int kp = router_dx_k(a.E);
   const int nsw = router_dw_splits(a.T, a.E, a.d);
   const int chunk = (a.T + nsw - 1) / nsw;
-  const int64_t n = (a.split_done ? 0 : (int64_t)a.T * (kp / 8)) + (int64_t)kp * (a.d / 8);
-  const int64_t nthreads = n > nsw + 1 ? n : nsw + 1;
-  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a.dlogits,
-                     a.w_router, a.T, a.E, a.d, kp, nsw, chunk, a.gx, a.gw, a.wsplit, a.offs, a.split_done);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!a.split_done) {  // else the dlogits kernel wrote every split operand and the row ranges
+    const int64_t nw = (int64_t)kp * (a.d / 8) > nsw + 1 ? (int64_t)kp * (a.d / 8) : nsw + 1;
+    const int64_t nthreads = (int64_t)a.T * (kp / 8) + nw;
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a.dlogits,
+                       a.w_router, a.T, a.E, a.d, kp, nsw, chunk, a.gx, a.gw, a.wsplit, a.offs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   GemmArgs g{};
   g.kind = 1;
   g.epi = EPI_STORE_F32;

@@ -341,7 +341,16 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ counts,
                                                       float* __restrict__ dlogits, int T, int E, int k, int gate,
                                                       int renorm, float alpha, uint16_t* __restrict__ gx,
-                                                      uint16_t* __restrict__ gw, int kp) {
+                                                      uint16_t* __restrict__ gw, int kp,
+                                                      const float* __restrict__ w_router,
+                                                      uint16_t* __restrict__ wsplit, int32_t* __restrict__ offs,
+                                                      int d, int nsw, int chunk) {
+  const int tok_blocks = (T + 3) / 4;
+  if ((int)blockIdx.x >= tok_blocks) {  // the router-weight split (bf16 layers)
+    split_router_weights((int64_t)(blockIdx.x - tok_blocks) * 256 + threadIdx.x, w_router, E, d, kp, wsplit, T, nsw,
+                         chunk, offs);
+    return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -614,8 +623,17 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_dlogits(const DlogitsArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(dlogits_kernel, dim3((a.T + 3) / 4), dim3(256), 0, st, a.probs, a.topk_idx, a.topk_w, a.dg,
-                     a.counts, a.dlogits, a.T, a.E, a.k, a.gate, a.renorm, a.alpha, a.gx, a.gw, a.kp);
+  int64_t blocks = (a.T + 3) / 4;
+  int nsw = 0, chunk = 0;
+  if (a.gx) {  // extra workgroups: the weight split and the row ranges
+    nsw = router_dw_splits(a.T, a.E, a.d);
+    chunk = (a.T + nsw - 1) / nsw;
+    const int64_t nw = (int64_t)a.kp * (a.d / 8) > nsw + 1 ? (int64_t)a.kp * (a.d / 8) : nsw + 1;
+    blocks += (nw + 255) / 256;
+  }
+  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.probs, a.topk_idx, a.topk_w, a.dg,
+                     a.counts, a.dlogits, a.T, a.E, a.k, a.gate, a.renorm, a.alpha, a.gx, a.gw, a.kp, a.w_router,
+                     a.wsplit, a.offs, a.d, nsw, chunk);
   return hipGetLastError();
 }
 
