@@ -416,8 +416,11 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   void* dX_sh = sh ? base + L.dX_sh : nullptr;
   int32_t* order = (int32_t*)(base + L.order);
 
+  // the weight-gradient launches run the experts with the most rows first; the
+  // ranking rides along as the last workgroup of the combine backward launch
   if (T > 0) {
-    moe::CombineBwdArgs cb{dy, sv->y_perm, sv->slot, sv->topk_w, dO, dg, T, d, k, c->dtype};
+    moe::CombineBwdArgs cb{dy, sv->y_perm, sv->slot, sv->topk_w, dO, dg, T, d, k, c->dtype,
+                           sv->expert_offsets, E, shr, sh ? 1 : 0, order};
     StageTimer pt("bwd_combine", s);
     if ((st = launch_status(moe::launch_combine_bwd(cb, s)))) return st;
   }
@@ -443,8 +446,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
     a2.X = sv->act_saved; a2.ldx = f1; a2.X_sh = sv->act_shared;
   }
   if ((st = gemm(c, a2, s, "bwd_dgrad2"))) return st;
-  // weight gradients run the experts with the most rows first
-  if ((st = launch_status(moe::launch_group_order(sv->expert_offsets, E, shr, sh ? 1 : 0, order, s)))) return st;
+  if (T == 0 && (st = launch_status(moe::launch_group_order(sv->expert_offsets, E, shr, sh ? 1 : 0, order, s))))
+    return st;
   // dW2_e = dO^T h over the expert's rows
   moe::GemmArgs w2g{};
   w2g.kind = 1;

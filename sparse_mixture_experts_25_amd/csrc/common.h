@@ -67,6 +67,27 @@ __device__ __forceinline__ Split3 split3(float v) {
   return s;
 }
 
+// Rank of each expert group by row count (largest first, ties by lower index),
+// computed by one workgroup of `nthreads` threads: order[rank] = group. The
+// weight-gradient launches then start the longest contractions first.
+// rows_s: LDS scratch of at least E + has_shared ints (at most 1025).
+__device__ __forceinline__ void rank_groups_by_rows(const int32_t* __restrict__ offsets, int E, int shared_rows,
+                                                    int has_shared, int32_t* __restrict__ order, int* rows_s,
+                                                    int nthreads) {
+  const int G = E + has_shared;
+  for (int g = threadIdx.x; g < G; g += nthreads) rows_s[g] = g < E ? offsets[g + 1] - offsets[g] : shared_rows;
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += nthreads) {
+    const int r = rows_s[g];
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const int rh = rows_s[h];
+      rank += (rh > r) || (rh == r && h < g);
+    }
+    order[rank] = g;
+  }
+}
+
 // Thread u of the router-weight split: the 16 bytes (8 values of row r) of the
 // split weights wsp [kp, d] = [W_hi ; W_mid ; W_hi ; 0 ...] (bf16), for
 // u < kp * d / 8, and the row ranges of the router products (offs[0..1] = the

@@ -654,24 +654,13 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   }
 }
 
-// Rank of each group by row count (largest first, ties by lower index): the
-// weight-gradient launches then start the longest contractions first.
+// Group ranking alone (batches without tokens; otherwise the combine backward
+// launch does it in an extra workgroup).
 __global__ __launch_bounds__(512) void group_order_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int shared_rows, int has_shared,
                                                          int32_t* __restrict__ order) {
-  __shared__ int rows_s[1024];
-  const int G = E + has_shared;
-  for (int g = threadIdx.x; g < G; g += 512) rows_s[g] = g < E ? offsets[g + 1] - offsets[g] : shared_rows;
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += 512) {
-    const int r = rows_s[g];
-    int rank = 0;
-    for (int h = 0; h < G; ++h) {
-      const int rh = rows_s[h];
-      rank += (rh > r) || (rh == r && h < g);
-    }
-    order[rank] = g;
-  }
+  __shared__ int rows_s[1025];
+  rank_groups_by_rows(offsets, E, shared_rows, has_shared, order, rows_s, 512);
 }
 
 }  // namespace

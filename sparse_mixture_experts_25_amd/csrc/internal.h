@@ -156,6 +156,9 @@ struct CombineBwdArgs {
   void* dO;      // [R, d]
   float* dg;     // [T, k]
   int T, d, k, dtype;
+  // when order is set, one extra workgroup also ranks the expert groups by row
+  // count into order (as launch_group_order)
+  const int32_t* offsets; int E, shared_rows, has_shared; int32_t* order;
 };
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st);
 

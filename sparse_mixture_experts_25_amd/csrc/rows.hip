@@ -58,6 +58,24 @@ __device__ __forceinline__ int kept_columns(const int32_t* __restrict__ srow, in
 // the loads of all k rows are issued before any of them is summed, so a lane
 // has k + 1 loads in flight. A dropped column (slot < 0) loads the token's own
 // row of the first operand instead (always valid memory) and is not summed.
+// The expert-group ranking of the weight-gradient launches, folded into the
+// combine backward launch as its first workgroup (one dependent launch fewer;
+// first, so that it runs beside the row work instead of after it).
+struct GroupRank {
+  const int32_t* offsets;
+  int E, shared_rows, has_shared;
+  int32_t* order;  // null: no extra workgroup
+  // workgroups before the row work
+  __device__ int skip() const { return order ? 1 : 0; }
+  // true in the extra workgroup, after it has done the ranking
+  __device__ bool run() const {
+    if (!order || blockIdx.x != 0) return false;
+    __shared__ int rows_s[1025];
+    rank_groups_by_rows(offsets, E, shared_rows, has_shared, order, rows_s, 256);
+    return true;
+  }
+};
+
 template <int KM>
 struct TokenCols {
   int s[KM];
@@ -118,10 +136,12 @@ __global__ __launch_bounds__(256) void combine_bwd_narrow_kernel(const TX* __res
                                                                  const int32_t* __restrict__ slot,
                                                                  const float* __restrict__ topk_w,
                                                                  TX* __restrict__ dO, float* __restrict__ dg, int T,
-                                                                 int d, int k) {
+                                                                 int d, int k, GroupRank gr_job) {
+  if (gr_job.run()) return;
   constexpr int V = Elem<TX>::kVec;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);  // wave-uniform: scalar table reads
+  // wave-uniform: scalar table reads
+  const int t = __builtin_amdgcn_readfirstlane(((int)blockIdx.x - gr_job.skip()) * 4 + wave);
   if (t >= T) return;
   TokenCols<KM> c;
   c.load(slot, topk_w, t, k);
@@ -300,10 +320,12 @@ template <typename TX>
 __global__ __launch_bounds__(256) void combine_bwd_wide_kernel(const TX* __restrict__ dy, const TX* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot,
                                                           const float* __restrict__ topk_w, TX* __restrict__ dO,
-                                                          float* __restrict__ dg, int T, int d, int k) {
+                                                          float* __restrict__ dg, int T, int d, int k,
+                                                          GroupRank gr_job) {
+  if (gr_job.run()) return;
   constexpr int V = Elem<TX>::kVec;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = ((int)blockIdx.x - gr_job.skip()) * 4 + wave;
   if (t >= T) return;
   const int nvec = d / V;
   __shared__ int32_t lsb[4][kListMax], lrb[4][kListMax];
@@ -602,17 +624,19 @@ hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
 
 template <typename TX>
 void launch_combine_bwd_t(const CombineBwdArgs& a, hipStream_t st) {
-  const dim3 g((a.T + 3) / 4), b(256);
+  const int tok_blocks = (a.T + 3) / 4;
+  const GroupRank job{a.offsets, a.E, a.shared_rows, a.has_shared, a.order};
+  const dim3 g(tok_blocks + (a.order ? 1 : 0)), b(256);
 #define MOE_LAUNCH(KM)                                                                                   \
   hipLaunchKernelGGL((combine_bwd_narrow_kernel<TX, KM>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.y_perm, \
-                     a.slot, a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k)
+                     a.slot, a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k, job)
   if (a.k <= 1) MOE_LAUNCH(1);
   else if (a.k <= 2) MOE_LAUNCH(2);
   else if (a.k <= 4) MOE_LAUNCH(4);
   else if (a.k <= kWideK) MOE_LAUNCH(8);
   else
     hipLaunchKernelGGL((combine_bwd_wide_kernel<TX>), g, b, 0, st, (const TX*)a.dy, (const TX*)a.y_perm, a.slot,
-                       a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k);
+                       a.topk_w, (TX*)a.dO, a.dg, a.T, a.d, a.k, job);
 #undef MOE_LAUNCH
 }
 
