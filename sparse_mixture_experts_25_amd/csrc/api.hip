@@ -417,7 +417,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   int32_t* order = (int32_t*)(base + L.order);
 
   // the weight-gradient launches run the experts with the most rows first; the
-  // ranking rides along as the last workgroup of the combine backward launch
+  // ranking rides along as the first workgroup of the combine backward launch
   if (T > 0) {
     moe::CombineBwdArgs cb{dy, sv->y_perm, sv->slot, sv->topk_w, dO, dg, T, d, k, c->dtype,
                            sv->expert_offsets, E, shr, sh ? 1 : 0, order};
