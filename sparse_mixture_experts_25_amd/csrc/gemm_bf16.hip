@@ -342,11 +342,11 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   //
   // 128x128 tiles: the wave's 32-row blocks interleave with the other wave
   // row's (block i of wave row wm holds tile rows (2i + wm) * 32 .. +32), so
-  // the valid rows of a short group split evenly over the SIMDs, and in the
-  // row-ragged kinds the blocks wholly past the group's rows skip their
-  // fragment reads and matrix work: the loop runs with FMV = the count of live
-  // blocks (a compile-time value per instantiation), every instantiation with
-  // the same barriers. 256x256 tiles: wave row wm holds rows wm * 128 .. +128.
+  // the valid rows of a short group split evenly over the SIMDs. 256x256
+  // tiles: wave row wm holds rows wm * 128 .. +128. In the row-ragged kinds the
+  // blocks wholly past the group's rows skip their fragment reads and matrix
+  // work: the loop runs with FMV = the count of live blocks (a compile-time
+  // value per instantiation), every instantiation with the same barriers.
   constexpr bool kInterleave = BM < 256;
   auto brow = [&](int i) { return kInterleave ? (2 * i + wm) * 32 : wm * WM + i * 32; };
   constexpr int SUB = kBK / 16;  // even: sub-step s always uses register set s & 1
@@ -468,10 +468,19 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     mfmas(fmv, Set1());
   };
   if (nk > 0) {
+    // live 32-row blocks of this wave: those with brow(i) < a_valid, a prefix
+    // of its FM blocks in both layouts
     if constexpr (KIND == 0 && kInterleave && FM == 2) {
-      // live blocks of this wave: those with (2i + wm) * 32 < a_valid
       const int nvb = __builtin_amdgcn_readfirstlane(a_valid > 64 + wm * 32 ? 2 : (a_valid > wm * 32 ? 1 : 0));
       if (nvb == 2) main_loop(std::integral_constant<int, 2>());
+      else if (nvb == 1) main_loop(std::integral_constant<int, 1>());
+      else main_loop(std::integral_constant<int, 0>());
+    } else if constexpr (KIND == 0 && !kInterleave && FM == 4) {
+      const int lv = a_valid - wm * WM;  // valid rows from this wave row's first
+      const int nvb = __builtin_amdgcn_readfirstlane(lv <= 0 ? 0 : (lv >= 128 ? 4 : (lv + 31) / 32));
+      if (nvb == 4) main_loop(std::integral_constant<int, 4>());
+      else if (nvb == 3) main_loop(std::integral_constant<int, 3>());
+      else if (nvb == 2) main_loop(std::integral_constant<int, 2>());
       else if (nvb == 1) main_loop(std::integral_constant<int, 1>());
       else main_loop(std::integral_constant<int, 0>());
     } else {
