@@ -708,20 +708,22 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // the cap, and the realised groups range from full (expert choice, balanced
   // routing) to mostly empty (skewed routing that drops most assignments). The
   // matmul then runs as two launches over the groups, each deciding on the
-  // device from the group's row count: 256 rows or more on 256x256 tiles, the
-  // others (and empty ones) on the weight-streaming 128x128 tiles. Dropless
-  // layers keep one launch: there the zero-fill of empty experts overlaps the
-  // big groups' matrix work, which a second launch would serialise.
+  // device from the group's row count: 128 rows or more on 256x256 tiles (a
+  // group of 128-255 rows reads each weight slab once, and the waves past its
+  // rows skip their matrix work), the others (and empty ones) on the
+  // weight-streaming 128x128 tiles. Dropless layers keep one launch: there the
+  // zero-fill of empty experts overlaps the big groups' matrix work, which a
+  // second launch would serialise.
   const bool capped = a.row_cap > 0 && a.row_cap <= 512 && a.E > 1;
   if (!capped) return launch_tiles<256, 256, 64, 2, 4>(a, st);
   GemmArgs b = a;
   b.split_part = 1;
-  b.split_rows = 256;
+  b.split_rows = 128;
   const hipError_t e = launch_tiles<256, 256, 64, 2, 4>(b, st);
   if (e != hipSuccess) return e;
   GemmArgs sm = a;
   sm.split_part = 2;
-  sm.split_rows = 256;
+  sm.split_rows = 128;
   return small_tiles(sm);
 }
 
