@@ -4,9 +4,13 @@ One step = the whole layer on one batch: moe_route, moe_dispatch,
 moe_expert_ffn, moe_combine, moe_aux_loss, moe_backward (all through the C ABI,
 inputs already resident in HBM), plus moe_bias_update for the gates that carry
 a selection bias (the aux-loss-free balancing step, gamma = 1e-3, or with
---balance quantile the Quantile-Balancing step). Default workload: the Switch-Base-shaped layer
-(T=8192 tokens as 16x512, d_model=768, 128 ReLU experts 768->3072->768, top-1,
-capacity factor 1.25, bf16 activations and weights, fp32 router, aux alpha 0.01).
+--balance quantile the Quantile-Balancing step). Default workload: the
+DeepSeek-V3-shaped layer, the largest of the five that fits one GPU (T=16384
+tokens, d_model=7168, 256 routed SwiGLU experts 7168->2048->7168 plus one
+always-on shared expert of the same shape, sigmoid gate with a per-expert
+selection bias, top-8 renormalised, dropless, bf16 activations and weights, fp32
+router). --config picks another (switch_base, gshard_top2, finegrained_top8,
+tiny_f32).
 
 Prints one JSON line (see the keys below). Also measured and reported:
   roofline: the stage with the largest per-launch time, timed with HIP events on
@@ -22,6 +26,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -189,19 +195,58 @@ def cpu_sample_tokens(c, ref_tokens=6144):
     return max(64, min(c.T, n))
 
 
+class _ExpertsF64:
+    """Per-expert float64 view of a [E, ...] weight tensor, widened on first use
+    (the oracle reads only the experts the sampled tokens reach, so the full
+    expert weights are never widened at once)."""
+
+    def __init__(self, t, f64):
+        self.t, self.f64, self.cache = t, f64, {}
+        self.shape = tuple(t.shape)
+
+    def __len__(self):
+        return self.shape[0]
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = self.f64(self.t[e])
+        return self.cache[e]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(c, inp, budget_tokens):
     """Oracle forward+backward of the same layer on the first `budget_tokens` tokens
     (an independent batch of that size; capacity follows the formula for it)."""
     import oracle as O
     sub = c.replace(T=budget_tokens)
-    oin = {k: O.f64(v[:budget_tokens] if k in ("x", "dy") else v) for k, v in inp.items()}
+    oin = {}
+    for k, v in inp.items():
+        if k in ("w1", "w2"):
+            oin[k] = _ExpertsF64(v, O.f64)
+        else:
+            oin[k] = O.f64(v[:budget_tokens] if k in ("x", "dy", "noise") else v)
     spec = O.Spec.of(sub)
+    fw = O.route(spec, oin["x"], oin["w_router"], oin.get("logit_offset"), oin.get("sel_bias"), oin.get("noise"))
+    for e in np.unique(fw["idx"]):  # widen the reached experts' weights before the clock starts
+        oin["w1"][e], oin["w2"][e]
     t0 = time.perf_counter()
     fw = O.forward(spec, oin)
     O.backward(spec, oin, fw, oin["dy"])
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{budget_tokens}-token batch of the same layer (same weights), forward+backward, "
                       f"{dt:.1f} s"}
 
@@ -257,7 +302,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="switch_base")
+    ap.add_argument("--config", default="deepseek_v3")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--balance", default="sign", choices=["sign", "quantile"],
                     help="selection-bias step of the bias-carrying gates: sign (fixed step) or quantile")
@@ -270,6 +315,10 @@ def main():
                          "layer, about 10-15 s of host work, or a sample of the same estimated cost)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write a scratch buffer of this many MiB before every timed step, so the 256 MB "
+                         "last-level cache cannot serve the step's reads from the previous one; the per-step "
+                         "median and min then exclude it (ms_per_step still brackets all K steps)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "kernel to scale HBM counters against)")
@@ -340,20 +389,28 @@ def main():
     per_stage = {k: sum(v) / len(v) for k, v in per_stage.items()}
     dom = max(per_stage, key=per_stage.get)
 
-    # timed region: K steps; the dominant stage's launches are bracketed by events
+    # timed region: K steps; the dominant stage's launches are bracketed by events,
+    # and every step by a pair of its own (for the median and min)
     evd = HipEvents(2 * args.steps)
     M.lib().moe_profile_arm(dom.encode(), ctypes.cast(evd.ev, ctypes.c_void_p), args.steps)
+    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda") if args.flush_mib else None
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        sev[i][0].record(stream)
         step()
+        sev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     nd = M.lib().moe_profile_disarm()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
+    per_step = sorted(a.elapsed_time(b) for a, b in sev)
     dom_ms = sum(evd.elapsed_ms(2 * i, 2 * i + 1) for i in range(nd)) / max(nd, 1)
 
     offs = buf.t["expert_offsets"].cpu()
@@ -366,6 +423,16 @@ def main():
     roof["launch_ms"] = dom_ms
 
     total_flops = sum(v[0] for v in work.values())
+    # weight gradients are overwritten: experts without rows get zeros, written
+    # inside the two weight-gradient launches (reported on its own line)
+    f1 = 2 * c.f if c.act == "swiglu" else c.f
+    eb = 2 if c.dtype == "bf16" else 4
+    zero_bytes = (c.E - ne) * (f1 * c.d + c.d * c.f) * eb
+    wr = attainable_peak("hbm")
+    zero_fill = {"empty_experts": c.E - ne, "bytes": zero_bytes,
+                 "ms_at_8TBps": zero_bytes / PEAK_HBM * 1e3,
+                 "ms_at_measured_write_rate": (zero_bytes / (wr * 1e9) * 1e3) if wr else None,
+                 "in_stages": ["bwd_wgrad1", "bwd_wgrad2"]}
     line = {
         "metric": "MoE layer fwd+bwd tokens/sec on 1 MI355X",
         "value": c.T / (ms_step * 1e-3),
@@ -374,6 +441,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": per_step[len(per_step) // 2],
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -383,6 +452,7 @@ def main():
                    "capacity_factor": c.cf, "act": c.act, "gate": c.gate, "kept_rows": rows,
                    "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12},
         "roofline": roof,
+        "zero_fill": zero_fill,
         # every stage against its own roofline, from the per-stage pre-pass times
         "stage_roofline": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv
                                for kk, vv in stage_roofline(k, work[k], v, c.dtype).items() if kk != "peak"}

@@ -2,9 +2,11 @@
  * moe.h - C ABI of the MI355X (gfx950) token-routed Mixture-of-Experts layer.
  *
  * One layer, forward and backward, on one GPU. Every call enqueues HIP kernels
- * on the caller's stream and returns at once: no host synchronisation, no
- * device allocation, no global state. The caller owns every buffer, including
- * the tensors the forward produces and the backward consumes.
+ * on the caller's stream and returns at once: no host synchronisation and no
+ * device allocation. The calls keep no state between them (the opt-in timing
+ * hook of moe_profile.h is per host thread), so they are re-entrant. The caller
+ * owns every buffer, including the tensors the forward produces and the
+ * backward consumes.
  *
  * Pages cited by title:
  *   [SW]   "Mixture of Experts (MoE) を1から解説 — Switch Transformerのルーティングと負荷分散"
@@ -18,7 +20,9 @@
  *     storage type: bf16 (MOE_DT_BF16) or fp32 (MOE_DT_F32). Router tensors
  *     (w_router, probs, topk_w, logit_offset, sel_bias, dw_router) are fp32.
  *   - Device pointers must be 16-byte aligned. d_model and d_ff must be
- *     multiples of 8.
+ *     multiples of 8. One expert's weight matrix (f1 x d_model elements, f1 =
+ *     d_ff, or 2 d_ff for SwiGLU) must be under 4 GiB: larger configs are
+ *     MOE_ERR_UNSUPPORTED (the matmuls address it with 32-bit offsets).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Arguments are validated on the host before any HIP call; a bad argument
  *     returns an error and enqueues nothing. MOE_ERR_HIP reports a launch error
@@ -75,12 +79,12 @@ typedef struct moe_config {
   int32_t d_ff;             /* f: expert hidden width (each half, for SwiGLU) */
   int32_t num_experts;      /* E: routed experts */
   int32_t top_k;            /* k: experts per token, 1 <= k <= E */
-  float capacity_factor;    /* > 0: capacity mode ([SW] eq. (3)); <= 0: dropless */
+  float capacity_factor;    /* > 0: capacity mode ([SW] eq. (3)); <= 0: dropless; must be finite */
   int32_t renormalize;      /* 1: the k selected weights are divided by their sum */
   int32_t gate;             /* MOE_GATE_* */
   int32_t act;              /* MOE_ACT_* */
   int32_t dtype;            /* MOE_DT_*: activations and expert weights */
-  float aux_alpha;          /* alpha of [SW] eq. (4); 0 disables the aux loss */
+  float aux_alpha;          /* alpha of [SW] eq. (4); 0 disables the aux loss; must be finite */
   int32_t num_shared_experts; /* 0 or 1: an always-on expert added with weight 1 ([WIKI]) */
   int32_t routing;          /* MOE_ROUTING_*; expert choice needs the softmax gate, renormalize = 0,
                                aux_alpha = 0, capacity_factor > 0 and top_k = num_experts */

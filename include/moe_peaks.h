@@ -1,6 +1,7 @@
 /*
- * moe_peaks.h - attainable-peak probes of one MI355X (gfx950), exported by the
- * same libmoe.so as moe.h.
+ * moe_peaks.h - attainable-peak probes of one MI355X (gfx950), exported by
+ * libmoe_peaks.so, a measuring aid built beside (and kept out of) the layer
+ * library libmoe.so.
  *
  * The layer's kernels are reported against published peaks (HBM 8 TB/s, bf16
  * matrix core 2.5 PFLOP/s, fp32 vector 78.6 TFLOP/s without packed FMA). These

@@ -6,8 +6,9 @@
  * runs on, so the caller can read per-launch kernel durations with
  * hipEventElapsedTime. Disarmed (the default) it costs one branch per stage.
  *
- * The hook is process-wide state: arm, run, and disarm from one host thread,
- * with no other thread calling the library meanwhile.
+ * The hook is per host thread: arm, run and disarm on one thread; only the
+ * calls made on that thread are timed, and calls on other threads are not
+ * affected (each thread has its own hook, disarmed until it arms it).
  *
  * Stage names (one stage = one kernel unless noted):
  *   "route" (moe_route, moe_route_noisy), "route_ec" (moe_route_ec, several

@@ -31,7 +31,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB may point at another build of the same source (the sanitizer test's)
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.cpp")
 
 MODE_EXACT, MODE_F32, MODE_BF16 = 0, 1, 2
@@ -276,6 +277,35 @@ def ffn_fwd(mode, X, W1, W2, act):
     if n:
         lib().orc_ffn_fwd(mode, n, d, f, act, _d(X), _d(W1), _d(W2), _d(A), _d(H), _d(Y))
     return A, H, Y
+
+
+def relu_ambiguous(X, W1, A):
+    """Pre-activations of a ReLU expert whose sign an fp32 accumulation may not
+    decide: |a| <= gamma_d * sum_j |x_j w_j| with gamma_d = d u / (1 - d u), the
+    standard bound on a d-term floating-point sum. u is taken as 2^-23 (twice the
+    fp32 unit roundoff, so the bound holds whichever rounding the matrix cores'
+    fp32 accumulation uses), and A holds the bf16-rounded pre-activations, so the
+    bound is widened by one bf16 rounding (2^-8, doubled). Both masks of such an
+    element are correct results; everywhere else the mask is fixed.
+    X [n, d], W1 [f, d] (the ReLU layer's first matrix), A [n, f]."""
+    n, d = X.shape
+    if n == 0:
+        return np.zeros((0, W1.shape[0]), bool)
+    u = 2.0 ** -23
+    gamma = d * u / (1.0 - d * u)
+    bound = np.abs(X) @ np.abs(W1).T
+    return np.abs(A) <= gamma * bound * (1.0 + 2.0 ** -7)
+
+
+def relu_ambiguous_rows(x_perm, w1, offsets, act):
+    """relu_ambiguous over every expert's rows of the permuted buffers -> [n, f] mask."""
+    n = int(offsets[-1])
+    out = np.zeros((n, act.shape[1]), bool)
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            out[a:b] = relu_ambiguous(x_perm[a:b], w1[e], act[a:b])
+    return out
 
 
 def combine(mode, x, y_perm, slot, w, y_shared=None):

@@ -22,6 +22,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 # MOE_LIB may point at another build of the same library (same C ABI)
 LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
+# the attainable-peak probes (include/moe_peaks.h) are a library of their own
+PEAKS_LIB_PATH = os.path.join(HERE, "libmoe_peaks.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SQRT_SOFTPLUS_BIAS, MOE_GATE_NOISY_TOPK = 0, 1, 2, 3
@@ -35,7 +37,7 @@ EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_disp
            "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
-# attainable-peak probes (include/moe_peaks.h), exported by the same library
+# attainable-peak probes (include/moe_peaks.h), exported by libmoe_peaks.so
 PEAK_EXPORTS = ["moe_peak_sink_bytes", "moe_peak_read", "moe_peak_write", "moe_peak_copy", "moe_peak_mfma_bf16",
                 "moe_peak_fma_f32"]
 MOE_PEAK_BLOCKS = 2048
@@ -105,6 +107,20 @@ def lib():
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTS[:-1]:
             getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+_peaks_lib = None
+
+
+def peaks_lib():
+    """Load libmoe_peaks.so, the attainable-peak probes (raises if it has not been built)."""
+    global _peaks_lib
+    if _peaks_lib is None:
+        if not os.path.exists(PEAKS_LIB_PATH):
+            raise MoeError(f"{PEAKS_LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_25_amd.build`")
+        L = ctypes.CDLL(PEAKS_LIB_PATH)
         L.moe_peak_sink_bytes.argtypes = []
         L.moe_peak_sink_bytes.restype = ctypes.c_size_t
         L.moe_peak_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
@@ -114,8 +130,8 @@ def lib():
         L.moe_peak_fma_f32.argtypes = [_vp, ctypes.c_int, _vp]
         for n in PEAK_EXPORTS[1:]:
             getattr(L, n).restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _peaks_lib = L
+    return _peaks_lib
 
 
 def moe_status_string(status: int) -> str:
@@ -302,7 +318,7 @@ def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream
 # ---- attainable-peak probes (include/moe_peaks.h) ----
 
 def moe_peak_sink_bytes() -> int:
-    return int(lib().moe_peak_sink_bytes())
+    return int(peaks_lib().moe_peak_sink_bytes())
 
 
 def _peak_check(status: int, what: str):
@@ -312,22 +328,22 @@ def _peak_check(status: int, what: str):
 
 def moe_peak_read(src, sink, nbytes=None, stream=None):
     n = src.numel() * src.element_size() if nbytes is None else nbytes
-    _peak_check(lib().moe_peak_read(_p(src), n, _p(sink), _stream(stream)), "moe_peak_read")
+    _peak_check(peaks_lib().moe_peak_read(_p(src), n, _p(sink), _stream(stream)), "moe_peak_read")
 
 
 def moe_peak_write(dst, nbytes=None, stream=None):
     n = dst.numel() * dst.element_size() if nbytes is None else nbytes
-    _peak_check(lib().moe_peak_write(_p(dst), n, _stream(stream)), "moe_peak_write")
+    _peak_check(peaks_lib().moe_peak_write(_p(dst), n, _stream(stream)), "moe_peak_write")
 
 
 def moe_peak_copy(dst, src, nbytes=None, stream=None):
     n = src.numel() * src.element_size() if nbytes is None else nbytes
-    _peak_check(lib().moe_peak_copy(_p(dst), _p(src), n, _stream(stream)), "moe_peak_copy")
+    _peak_check(peaks_lib().moe_peak_copy(_p(dst), _p(src), n, _stream(stream)), "moe_peak_copy")
 
 
 def moe_peak_mfma_bf16(sink, iters, stream=None):
-    _peak_check(lib().moe_peak_mfma_bf16(_p(sink), int(iters), _stream(stream)), "moe_peak_mfma_bf16")
+    _peak_check(peaks_lib().moe_peak_mfma_bf16(_p(sink), int(iters), _stream(stream)), "moe_peak_mfma_bf16")
 
 
 def moe_peak_fma_f32(sink, iters, stream=None):
-    _peak_check(lib().moe_peak_fma_f32(_p(sink), int(iters), _stream(stream)), "moe_peak_fma_f32")
+    _peak_check(peaks_lib().moe_peak_fma_f32(_p(sink), int(iters), _stream(stream)), "moe_peak_fma_f32")

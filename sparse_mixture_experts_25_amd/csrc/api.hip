@@ -1,6 +1,8 @@
 // C ABI of the MoE layer: argument validation, sizes, workspace carving and
-// the launch sequence of each call. No allocation, no host synchronisation,
-// no global state.
+// the launch sequence of each call. No allocation and no host synchronisation.
+// The only state kept between calls is the opt-in stage-timing hook of
+// moe_profile.h, which is per host thread (a call reads the hook of the thread
+// that makes it), so calls from different threads never share it.
 #include <math.h>
 #include <string.h>
 
@@ -40,7 +42,15 @@ int check_config(const moe_config* c) {
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (c->dtype != MOE_DT_F32 && c->dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->num_shared_experts != 0 && c->num_shared_experts != 1) return MOE_ERR_UNSUPPORTED;
-  if (!(c->capacity_factor == c->capacity_factor) || !(c->aux_alpha == c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(c->capacity_factor) || !isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  // The matmuls address one expert's weight matrix (and a 256-row activation
+  // tile) as a base plus a 32-bit per-lane byte offset: each expert matrix must
+  // stay under 4 GiB.
+  const uint64_t f1 = c->act == MOE_ACT_SWIGLU ? 2 * (uint64_t)c->d_ff : (uint64_t)c->d_ff;  // < 2^32
+  const uint64_t eb = c->dtype == MOE_DT_BF16 ? 2 : 4;
+  const uint64_t wide = f1 > (uint64_t)c->d_model ? f1 : (uint64_t)c->d_model;
+  const uint64_t lim = uint64_t(1) << 32;
+  if (f1 * (uint64_t)c->d_model >= lim / eb || 256 * wide >= lim / eb) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -48,7 +58,7 @@ int capacity_of(const moe_config* c) {
   if (c->capacity_factor <= 0.0f) return -1;
   // evaluated in double in the order of the capacity formula
   const double v = ceil((double)c->num_tokens / (double)c->num_experts * (double)c->capacity_factor);
-  return v > 2147483647.0 ? 2147483647 : (int)v;
+  return v < 2147483647.0 ? (int)v : 2147483647;  // v >= 0: T >= 0, E >= 1, cf > 0 and finite
 }
 
 int64_t max_rows_of(const moe_config* c, int C) {
@@ -120,7 +130,8 @@ size_t workspace_of(const moe_config* c, int64_t R) {
 int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Opt-in timing hook (moe_profile.h): an event pair around each launch of the
-// armed stage. Process-wide; used from one host thread by benchmarks.
+// armed stage. One per host thread: arming it on one thread changes nothing for
+// calls made on another.
 constexpr int kMaxProfPairs = 4096;
 struct Prof {
   bool armed = false;
@@ -130,7 +141,7 @@ struct Prof {
   int max = 0, n = 0;
   const char* names[kMaxProfPairs];
 };
-Prof g_prof;
+thread_local Prof g_prof;
 
 struct StageTimer {
   int idx = -1;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void router_dw_sum_kernel(const float* __restr
 //  - large products (at least 512 workgroups' worth of 256x256 tiles over
 //    256-token chunks): about 512 workgroups of 256x256 tiles, partials capped
 //    at 128 MB, chunks of at least 2048 tokens (fine-grained top-8 shape: 16
-//    chunks; DeepSeek-V3 shape: 5);
+//    chunks; DeepSeek-V3 shape: 6);
 //  - small products: 128x128 tiles (the matmul picks them when 256x256 tiles
 //    would leave CUs idle), about 256 workgroups, chunks of at least 1024 tokens.
 int router_dw_splits(int T, int E, int d) {

@@ -41,16 +41,18 @@ def test_every_header_is_covered():
         assert hasattr(L, s), s
     syms = header_symbols("moe_peaks.h")
     assert set(syms) == set(M.PEAK_EXPORTS)
-    L = M.lib()
+    P = M.peaks_lib()
     for s in syms:
-        assert hasattr(L, s), s
+        assert hasattr(P, s), s
+        # the probes are not part of the layer library
+        assert not hasattr(L, s), s
     src = open(os.path.join(ROOT, "include", "moe_peaks.h")).read()
     assert int(re.search(r"#define MOE_PEAK_BLOCKS (\d+)", src).group(1)) == M.MOE_PEAK_BLOCKS
     assert M.moe_peak_sink_bytes() == M.MOE_PEAK_BLOCKS * 256 * 4
 
 
 def test_peak_probes_validate_before_launch():
-    L = M.lib()
+    L = M.peaks_lib()
     sink = ctypes.c_void_p(1 << 20)
     assert L.moe_peak_read(None, 1024, sink, None) == -1
     assert L.moe_peak_read(ctypes.c_void_p(1 << 30), 1000, sink, None) == -1   # not a multiple of 16
@@ -98,11 +100,16 @@ def test_plan_capacity_limits_rows():
     (dict(k=0), M.MOE_ERR_INVALID_ARG),
     (dict(T=-1), M.MOE_ERR_INVALID_ARG),
     (dict(E=1024), M.MOE_ERR_UNSUPPORTED),
+    (dict(cf=float("inf")), M.MOE_ERR_INVALID_ARG),   # capacity from a non-finite factor
+    (dict(cf=float("inf"), T=0), M.MOE_ERR_INVALID_ARG),
+    (dict(cf=float("nan")), M.MOE_ERR_INVALID_ARG),
+    (dict(alpha=float("inf")), M.MOE_ERR_INVALID_ARG),
+    (dict(cf=1e30), M.MOE_OK),                        # huge but finite: capacity clamps
 ])
 def test_plan_rejects(bad, code):
-    p = dict(T=64, d=64, f=64, E=4, k=1)
+    p = dict(T=64, d=64, f=64, E=4, k=1, cf=1.0, alpha=0.0)
     p.update(bad)
-    cfg = M.make_config(p["T"], p["d"], p["f"], p["E"], p["k"])
+    cfg = M.make_config(p["T"], p["d"], p["f"], p["E"], p["k"], cf=p["cf"], alpha=p["alpha"])
     info = M.moe_plan_info()
     assert M.lib().moe_plan(ctypes.byref(cfg), ctypes.byref(info)) == code
 
@@ -177,3 +184,28 @@ def test_entry_points_validate_before_launch():
     assert L.moe_plan(ctypes.byref(nz_norenorm), ctypes.byref(info)) == M.MOE_ERR_UNSUPPORTED
     bad = M.make_config(64, 60, 64, 4, 2)
     assert L.moe_route(ctypes.byref(bad), A, A, N, N, A, A, A, N) == E
+
+
+@pytest.mark.parametrize("d,f,act,dtype,ok", [
+    (32768, 65528, "relu", "bf16", True),      # f x d x 2 bytes just under 4 GiB
+    (32768, 65536, "relu", "bf16", False),     # exactly 4 GiB per expert matrix
+    (32768, 32768, "swiglu", "bf16", False),   # [W_g; W_u] stacked: 2f x d x 2 = 4 GiB
+    (32768, 32760, "swiglu", "bf16", True),
+    (16384, 65536, "relu", "f32", False),      # fp32 storage: 4 bytes per element
+    (7168, 2048, "swiglu", "bf16", True),      # the DeepSeek-V3 expert shape
+])
+def test_plan_rejects_expert_matrices_past_32bit_offsets(d, f, act, dtype, ok):
+    """The matmuls address one expert's weight matrix with 32-bit per-lane byte
+    offsets from a 64-bit base: host validation refuses configs where that matrix
+    reaches 4 GiB, so such a call returns before any launch (fake pointers here)."""
+    L = M.lib()
+    cfg = M.make_config(64, d, f, 4, 1, act=act, dtype=dtype)
+    info = M.moe_plan_info()
+    st = L.moe_plan(ctypes.byref(cfg), ctypes.byref(info))
+    assert st == (M.MOE_OK if ok else M.MOE_ERR_UNSUPPORTED)
+    if not ok:
+        c = ctypes.byref(cfg)
+        assert L.moe_expert_ffn(c, A, A, A, A, N, N, N, A, A, A, N, N, N, A, 1 << 40, N) == M.MOE_ERR_UNSUPPORTED
+        s, w, g = M.moe_saved(), M.moe_weights(), M.moe_grads()
+        assert L.moe_backward(c, A, ctypes.byref(s), ctypes.byref(w), ctypes.byref(g), A, 1 << 40, N) == \
+            M.MOE_ERR_UNSUPPORTED

@@ -521,7 +521,7 @@ def _check_routing_invariants(spec, fw):
     for e in range(E):
         rows = fw["row_token"][offsets[e]:offsets[e + 1]]
         assert np.all(np.diff(rows) > 0)
-        assert np.all(idx[rows] == e) if False else True
+        assert np.all((idx[rows] == e).any(1))
     assert counts.sum() == T * k
 
 
@@ -789,3 +789,59 @@ def test_empty_expert_weight_gradient_is_zero():
     G = np.zeros((0, 5))
     V = np.zeros((0, 3))
     assert np.all(O.wgrad(O.MODE_BF16, G, V) == 0.0)
+
+
+def _fp32_sum(terms, order):
+    acc = np.float32(0.0)
+    for v in terms[order]:
+        acc = np.float32(acc + v)
+    return acc
+
+
+def test_relu_ambiguity_bound_holds_for_fp32_accumulation():
+    """oracle.relu_ambiguous (the S22 reading): outside the flagged elements, an
+    fp32 accumulation of the exact bf16 products in any order gives the sign of
+    the exact pre-activation. Checked on bf16 operands drawn so that many sums
+    are near zero, against sequential sums in the natural, reversed and random
+    orders and numpy's pairwise fp32 sum; an exactly cancelling row is flagged and
+    a clearly signed one is not."""
+    rng = np.random.default_rng(7)
+    n, d, f = 48, 264, 40
+    X = O.round_array(O.MODE_BF16, rng.standard_normal((n, d)))
+    W = O.round_array(O.MODE_BF16, rng.standard_normal((f, d)) / np.sqrt(d))
+    # pull some pre-activations towards zero: row n-1 of X cancels against W row 0
+    # in exact arithmetic (pairs of equal and opposite products)
+    X[-1, :] = 1.0
+    W[0, 0::2] = O.round_array(O.MODE_BF16, np.abs(rng.standard_normal(d // 2)))
+    W[0, 1::2] = -W[0, 0::2]
+    exact = X @ W.T                       # products of bf16 values are exact in double
+    A = O.round_array(O.MODE_BF16, exact)
+    amb = O.relu_ambiguous(X, W, A)
+    assert amb[-1, 0] and exact[-1, 0] == 0.0
+    assert not amb[np.abs(exact) > 1e-2].any()
+    X32, W32 = X.astype(np.float32), W.astype(np.float32)
+    orders = [np.arange(d), np.arange(d)[::-1]] + [rng.permutation(d) for _ in range(6)]
+    checked = 0
+    for i in range(n):
+        for j in range(f):
+            if amb[i, j]:
+                continue
+            terms = X32[i] * W32[j]           # exact in fp32 (8-bit significands)
+            s = np.sign(exact[i, j])
+            for o in orders:
+                assert np.sign(_fp32_sum(terms, o)) == s, (i, j)
+            assert np.sign(np.sum(terms, dtype=np.float32)) == s
+            checked += 1
+    assert checked > 0.9 * n * f
+
+
+def test_relu_ambiguity_bound_is_not_vacuous():
+    """The flagged fraction at unit-scale pre-activations stays small: about
+    the probability that |a| is under gamma_d * sum |x w|."""
+    rng = np.random.default_rng(3)
+    n, d, f = 4096, 256, 64
+    X = O.round_array(O.MODE_BF16, rng.standard_normal((n, d)))
+    W = O.round_array(O.MODE_BF16, rng.standard_normal((f, d)) / np.sqrt(d))
+    A = O.round_array(O.MODE_BF16, X @ W.T)
+    frac = O.relu_ambiguous(X, W, A).mean()
+    assert 0 < frac < 1e-3

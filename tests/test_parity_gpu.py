@@ -21,17 +21,19 @@ CASES = dict(SMALL)
 CASES["tiny_f32_bwd"] = CONFIGS["tiny_f32"].replace(name="tiny_f32_bwd", k=2, renorm=True, fwd_only=False,
                                                     alpha=0.01, cf=1.25)
 CASES["swiglu_f32_shared"] = SMALL["deepseek_v3"].replace(name="swiglu_f32_shared", dtype="f32", T=130)
-# groups averaging >= 256 rows select the 256x256 tiles; d and f are not multiples of
-# 32 (partial K steps in every matmul, partial column tiles), plus a shared expert
-CASES["big_tiles_swiglu"] = LayerConfig("big_tiles_swiglu", T=2048, d=264, f=392, E=8, k=2, gate="softmax",
-                                        renorm=True, act="swiglu", cf=0.0, alpha=0.01, shared=1,
-                                        logit_offset="normal")
-CASES["big_tiles_relu_drops"] = LayerConfig("big_tiles_relu_drops", T=2048, d=296, f=520, E=4, k=1,
-                                            act="relu", cf=1.1, alpha=0.01, logit_offset="normal")
-# expert capacity 512: groups of up to 512 rows stay on the 128x128 tiles (four row
-# tiles re-reading one streamed weight slab)
-CASES["capped_512_relu"] = LayerConfig("capped_512_relu", T=2048, d=264, f=392, E=4, k=1, act="relu", cf=1.0,
-                                       alpha=0.01, logit_offset="normal")
+# groups of several hundred rows on the 128x128 tiles (these launches have too few
+# 256x256 tiles to fill the GPU, so the launcher keeps the small tiles; the 256x256
+# tiles are covered by test_parity_big_tiles_gpu.py); d and f are not multiples of
+# 64 (partial K steps in every matmul, partial column tiles), plus a shared expert
+CASES["deep_groups_swiglu"] = LayerConfig("deep_groups_swiglu", T=2048, d=264, f=392, E=8, k=2, gate="softmax",
+                                          renorm=True, act="swiglu", cf=0.0, alpha=0.01, shared=1,
+                                          logit_offset="normal")
+CASES["deep_groups_relu_drops"] = LayerConfig("deep_groups_relu_drops", T=2048, d=296, f=520, E=4, k=1,
+                                              act="relu", cf=1.1, alpha=0.01, logit_offset="normal")
+# expert capacity 512 with too few tiles for the split pair: groups of up to 512
+# rows on the 128x128 tiles (four row tiles re-reading one streamed weight slab)
+CASES["capped_512_relu_small_tiles"] = LayerConfig("capped_512_relu_small_tiles", T=2048, d=264, f=392, E=4, k=1,
+                                                   act="relu", cf=1.0, alpha=0.01, logit_offset="normal")
 # the square-root-softplus gate with the selection bias, with and without renormalisation
 CASES["sqrt_softplus_bf16"] = SMALL["deepseek_v3"].replace(name="sqrt_softplus_bf16", gate="sqrt_softplus_bias",
                                                            alpha=0.01)
@@ -149,27 +151,36 @@ def test_backward_parity_stage_isolated(name):
 @pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].fwd_only])
 def test_backward_parity_end_to_end(name):
     """GPU forward -> GPU backward against oracle forward -> oracle backward.
-    Where a ReLU pre-activation is within rounding of zero (|a| <= 1e-4) both
-    masks are correct results; the gradients that depend on such an element are
-    left out of the element comparison (they are covered by the stage-isolated test)."""
+    Where fp32 accumulation cannot decide the sign of a ReLU pre-activation
+    (|a| <= gamma_d * sum_j |x_j w_j|, oracle.relu_ambiguous) both masks are
+    correct results; the gradients that depend on such an element are left out
+    of the element comparison (they are covered by the stage-isolated test), and
+    their count is printed."""
     c = CASES[name]
     print(f"[backward e2e] {name}", flush=True)
     inp, dev, buf, spec, fw = _forward_both(c)
     run_backward(buf, dev)
     torch.cuda.synchronize()
-    bw = O.backward(spec, oracle_inputs(inp), fw, host64(inp["dy"]))
+    inp64 = oracle_inputs(inp)
+    bw = O.backward(spec, inp64, fw, host64(inp["dy"]))
     t = buf.t
     tol = tol_for(c)
     n = int(fw["n_rows"])
+    amb_sh = None
     if c.act == "relu":
-        amb = np.abs(fw["act"]) <= 1e-4
+        amb = O.relu_ambiguous_rows(fw["x_perm"], inp64["w1"], fw["offsets"], fw["act"])
+        if c.shared:
+            amb_sh = O.relu_ambiguous(inp64["x"], inp64["ws1"], fw["act_shared"])
     else:
         amb = np.zeros_like(fw["act"], bool)
+    print(f"  ReLU pre-activations within accumulation error of zero: {int(amb.sum())}", flush=True)
     row_ok = ~amb.any(1)
     tok_ok = np.ones(c.T, bool)
     for tt, r in zip(*np.nonzero(fw["slot"] >= 0)):
         if not row_ok[fw["slot"][tt, r]]:
             tok_ok[tt] = False
+    if amb_sh is not None:
+        tok_ok &= ~amb_sh.any(1)
     assert relerr(host64(t["dx"]), bw["dx"], np.repeat(tok_ok[:, None], c.d, 1)) <= tol
     # dW1 rows i of expert e are comparable if no row of e is ambiguous at column i
     f1 = fw["act"].shape[1]
@@ -182,7 +193,10 @@ def test_backward_parity_end_to_end(name):
     assert relerr(host64(t["dw2"]), bw["dw2"]) <= tol
     assert relerr(host64(t["dw_router"]), bw["dw_router"]) <= tol
     if c.shared:
-        assert relerr(host64(t["dws1"]), bw["dws1"]) <= tol
+        ms = np.ones_like(bw["dws1"], bool)
+        if amb_sh is not None:
+            ms[amb_sh.any(0), :] = False
+        assert relerr(host64(t["dws1"]), bw["dws1"], ms) <= tol
         assert relerr(host64(t["dws2"]), bw["dws2"]) <= tol
 
 
