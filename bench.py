@@ -181,18 +181,17 @@ def stage_work(c, rows, ne_experts):
     }
 
 
-def cpu_sample_tokens(c, ref_tokens=6144):
-    """Tokens of `c` whose oracle forward+backward costs about as much as
-    `ref_tokens` of the Switch-Base-shaped layer (flops per token of the expert
-    FFNs, shared expert and router)."""
-    from synth import CONFIGS
-
-    def per_token(x):
-        f1 = 2 * x.f if x.act == "swiglu" else x.f
-        return 2 * x.d * (f1 + x.f) * (x.k + (1 if x.shared else 0)) + 2 * x.d * x.E
-
-    n = int(ref_tokens * per_token(CONFIGS["switch_base"]) / per_token(c))
-    return max(64, min(c.T, n))
+def cpu_baseline_sized(c, inp, target_s=20.0, probe_tokens=16):
+    """Oracle timing on a sample of about `target_s` seconds: a `probe_tokens`
+    sample first; if that already took at least half the target (the largest
+    layers, whose oracle cost is mostly per expert) it is the result, else a
+    sample scaled linearly from it is timed."""
+    probe = min(probe_tokens, c.T)
+    first = cpu_baseline(c, inp, probe)
+    if first["seconds"] >= 0.5 * target_s or probe == c.T:
+        return first
+    n = int(probe * target_s / max(first["seconds"], 1e-3))
+    return cpu_baseline(c, inp, max(probe, min(c.T, n)))
 
 
 class _ExpertsF64:
@@ -246,7 +245,7 @@ def cpu_baseline(c, inp, budget_tokens):
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "seconds": dt,
             "sample": f"{budget_tokens}-token batch of the same layer (same weights), forward+backward, "
                       f"{dt:.1f} s"}
 
@@ -311,8 +310,8 @@ def main():
     ap.add_argument("--gate", default=None, choices=["softmax", "sigmoid_bias", "sqrt_softplus_bias", "noisy_topk"],
                     help="override the workload's gate (a bias-carrying gate draws the selection bias)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
-                    help="oracle sample size for cpu_baseline (default: 6144 tokens of the Switch-Base-shaped "
-                         "layer, about 10-15 s of host work, or a sample of the same estimated cost)")
+                    help="oracle sample size for cpu_baseline (default: sized from a 16-token probe for about "
+                         "20 s of host work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -470,8 +469,8 @@ def main():
         print(json.dumps({"stage_ms": per_stage}), file=sys.stderr)
     line["stage_ms"] = {k: round(v, 4) for k, v in per_stage.items()}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, {k: v for k, v in inp.items()},
-                                            args.cpu_tokens or cpu_sample_tokens(c))
+        line["cpu_baseline"] = (cpu_baseline(c, inp, args.cpu_tokens) if args.cpu_tokens
+                                else cpu_baseline_sized(c, inp))
     print(json.dumps(line), flush=True)
 
 

@@ -31,6 +31,50 @@ def relerr(a, r, mask=None) -> float:
     return float(np.max(np.abs(a - r) / den))
 
 
+def relerr_sum(a, r, terms_abs, mask=None) -> float:
+    """relerr for a tensor that is a sum of terms each rounded to bf16 before the
+    sum (the layer output y and the input gradient dx): an element's error is
+    measured against the larger of |r_i|, rms(r) and the sum of its terms'
+    magnitudes (the usual bound on the error of a floating-point sum is
+    proportional to sum |x_i|, not |sum x_i|, so where terms cancel a one-ulp
+    rounding difference in a large term is a correct result)."""
+    a = np.asarray(a, np.float64).reshape(-1)
+    r = np.asarray(r, np.float64).reshape(-1)
+    t = np.asarray(terms_abs, np.float64).reshape(-1)
+    if mask is not None:
+        m = np.asarray(mask, bool).reshape(-1)
+        a, r, t = a[m], r[m], t[m]
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    den = np.maximum(np.maximum(np.abs(r), t), max(rms, 1e-30))
+    return float(np.max(np.abs(a - r) / den))
+
+
+def dx_terms_abs(fw, bw, dy64):
+    """Per element: |dy| + sum over kept rows |dX_perm| + |dx_router| (+ |dx_shared|)."""
+    t = np.abs(dy64) + np.abs(bw["dx_router"])
+    slot = fw["slot"]
+    for r in range(slot.shape[1]):
+        kept = slot[:, r] >= 0
+        t[kept] += np.abs(bw["dX_perm"][slot[kept, r]])
+    if "dx_shared" in bw:
+        t += np.abs(bw["dx_shared"])
+    return t
+
+
+def y_terms_abs(fw, x64):
+    """Per element: |x| + sum over kept rows |w * y_perm| (+ |y_shared|)."""
+    t = np.abs(x64).copy()
+    slot = fw["slot"]
+    for r in range(slot.shape[1]):
+        kept = slot[:, r] >= 0
+        t[kept] += np.abs(fw["w"][kept, r][:, None] * fw["y_perm"][slot[kept, r]])
+    if "y_shared" in fw:
+        t += np.abs(fw["y_shared"])
+    return t
+
+
 def tol_for(c):
     return TOL_F32 if c.dtype == "f32" else TOL_BF16
 

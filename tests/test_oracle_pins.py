@@ -845,3 +845,19 @@ def test_relu_ambiguity_bound_is_not_vacuous():
     A = O.round_array(O.MODE_BF16, X @ W.T)
     frac = O.relu_ambiguous(X, W, A).mean()
     assert 0 < frac < 1e-3
+
+
+def test_relerr_sum_measures_against_the_terms():
+    """helpers.relerr_sum: equal to relerr when the terms are no larger than the
+    result; at a cancellation a one-ulp difference in a large term stays small."""
+    from helpers import relerr, relerr_sum
+    rng = np.random.default_rng(0)
+    r = rng.standard_normal(1000)
+    a = r * (1 + 1e-3 * rng.standard_normal(1000))
+    assert relerr_sum(a, r, np.abs(r)) == pytest.approx(relerr(a, r))
+    # 2.0625 - 2.15625 = -0.09375: the second term off by one bf16 ulp (2^-6)
+    r2 = np.array([-0.09375, 1.0, -1.0])
+    a2 = r2 + np.array([2.0 ** -6, 0.0, 0.0])
+    terms = np.array([2.0625 + 2.15625, 1.0, 1.0])
+    assert relerr(a2, r2) > 0.01
+    assert relerr_sum(a2, r2, terms) < 0.004

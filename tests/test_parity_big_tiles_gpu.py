@@ -31,7 +31,9 @@ B K-contiguous, epilogue, waves along N>):
                          epilogue <256,256,64,2,0,0,6,4> with the shared expert
 
 Each case checks, with the oracle computed once: the forward (routing, slots and
-drops bit for bit; every float output within 2e-2, router outputs within 1e-5);
+drops bit for bit; every float output within 2e-2, router outputs within 1e-5;
+the layer output y and the input gradient dx, sums of terms each rounded to
+bf16, measured against the sum of their terms' magnitudes, helpers.relerr_sum);
 the backward end to end (GPU forward -> GPU backward, 2e-2); and the backward
 stage-isolated (the oracle's saved tensors fed to moe_backward: every gradient
 within 2e-2, the router weight gradient within 1e-5). ReLU pre-activations whose
@@ -47,8 +49,8 @@ import torch
 import oracle as O
 from synth import LayerConfig, make_inputs
 
-from helpers import TOL_BF16, TOL_F32, gpu_saved_from_oracle, host64, oracle_inputs, relerr, run_backward, \
-    run_forward, to_dev
+from helpers import TOL_BF16, TOL_F32, dx_terms_abs, gpu_saved_from_oracle, host64, oracle_inputs, relerr, \
+    relerr_sum, run_backward, run_forward, to_dev, y_terms_abs
 
 
 def _router_dw_splits(T, E, d):
@@ -142,10 +144,34 @@ def test_tile_plan(name):
         assert plan[key] == v, (key, plan)
 
 
+def run_forward_backward_again(buf, dev):
+    import sparse_mixture_experts_25_amd as M
+    M.forward(buf, dev, aux=True)
+    run_backward(buf, dev)
+    torch.cuda.synchronize()
+
+
+def _report_dx(c, fw, bw, inp64, dx, what):
+    """Print the worst input-gradient elements with the oracle's terms of the sum
+    (dy, the kept expert rows, the router term, the shared expert)."""
+    r = bw["dx"]
+    rms = float(np.sqrt(np.mean(r * r)))
+    err = np.abs(dx - r) / np.maximum(np.abs(r), rms)
+    flat = np.argsort(err, axis=None)[-3:][::-1]
+    for i in flat:
+        tt, j = np.unravel_index(i, err.shape)
+        rows = [int(sl) for sl in fw["slot"][tt] if sl >= 0]
+        terms = [inp64["dy"][tt, j]] + [bw["dX_perm"][sl, j] for sl in rows] + [bw["dx_router"][tt, j]]
+        if c.shared:
+            terms.append(bw["dx_shared"][tt, j])
+        print(f"  {what} dx worst: relerr {err[tt, j]:.4f} token {tt} col {j} gpu {dx[tt, j]:.6g} oracle {r[tt, j]:.6g} "
+              f"rms {rms:.3g} terms " + " ".join(f"{v:.5g}" for v in terms), flush=True)
+
+
 def _relu_ambiguity(c, inp64, fw):
     """(row mask [n, f] of ambiguous pre-activations, shared-expert mask [T, f] or None)."""
     if c.act != "relu":
-        return np.zeros((int(fw["n_rows"]), c.f), bool), None
+        return np.zeros(fw["act"].shape, bool), None
     amb = O.relu_ambiguous_rows(fw["x_perm"], inp64["w1"], fw["offsets"], fw["act"])
     amb_sh = O.relu_ambiguous(inp64["x"], inp64["ws1"], fw["act_shared"]) if c.shared else None
     return amb, amb_sh
@@ -195,13 +221,29 @@ def test_big_tiles_parity(name):
         assert relerr(host64(t["act_saved"][:n]), fw["act"]) <= TOL_BF16
     assert relerr(host64(t["h_saved"][:n]), fw["h"]) <= TOL_BF16
     assert relerr(host64(t["y_perm"][:n]), fw["y_perm"]) <= TOL_BF16
-    assert relerr(host64(t["y"]), fw["y"]) <= TOL_BF16
+    assert relerr_sum(host64(t["y"]), fw["y"], y_terms_abs(fw, inp64["x"])) <= TOL_BF16
     if c.shared:
         assert relerr(host64(t["y_shared"]), fw["y_shared"]) <= TOL_BF16
     if c.alpha:
         assert abs(float(t["aux"][0]) - fw["aux"]) <= TOL_F32 * abs(fw["aux"])
 
+    # ---- backward, stage-isolated: every element, router weight gradient at 1e-5
+    saved = gpu_saved_from_oracle(c, fw, buf.info)
+    run_backward(buf, dev, saved=saved)
+    torch.cuda.synchronize()
+    _report_dx(c, fw, bw, inp64, host64(t["dx"]), "stage-isolated")
+    dx_terms = dx_terms_abs(fw, bw, inp64["dy"])
+    assert relerr_sum(host64(t["dx"]), bw["dx"], dx_terms) <= TOL_BF16
+    assert relerr(host64(t["dw1"]), bw["dw1"]) <= TOL_BF16
+    assert relerr(host64(t["dw2"]), bw["dw2"]) <= TOL_BF16
+    assert relerr(host64(t["dw_router"]), bw["dw_router"]) <= TOL_F32
+    if c.shared:
+        assert relerr(host64(t["dws1"]), bw["dws1"]) <= TOL_BF16
+        assert relerr(host64(t["dws2"]), bw["dws2"]) <= TOL_BF16
+
     # ---- backward, end to end (ambiguous ReLU signs left out)
+    run_forward_backward_again(buf, dev)
+    _report_dx(c, fw, bw, inp64, host64(t["dx"]), "end-to-end")
     amb, amb_sh = _relu_ambiguity(c, inp64, fw)
     print(f"  ReLU pre-activations within accumulation error of zero: {int(amb.sum())}"
           + (f" (+{int(amb_sh.sum())} shared)" if amb_sh is not None else ""), flush=True)
@@ -218,7 +260,7 @@ def test_big_tiles_parity(name):
         a, b = fw["offsets"][e], fw["offsets"][e + 1]
         m1[e, amb[a:b].any(0), :] = False
     tokm = np.repeat(tok_ok[:, None], c.d, 1)
-    assert relerr(host64(t["dx"]), bw["dx"], tokm) <= TOL_BF16
+    assert relerr_sum(host64(t["dx"]), bw["dx"], dx_terms, tokm) <= TOL_BF16
     assert relerr(host64(t["dw1"]), bw["dw1"], m1) <= TOL_BF16
     assert relerr(host64(t["dw2"]), bw["dw2"]) <= TOL_BF16
     # the router gradient sums every token's logit gradient: a token with an
@@ -234,15 +276,3 @@ def test_big_tiles_parity(name):
     if empty.any():
         assert torch.all(t["dw1"][torch.from_numpy(empty).cuda()] == 0)
         assert torch.all(t["dw2"][torch.from_numpy(empty).cuda()] == 0)
-
-    # ---- backward, stage-isolated: every element, router weight gradient at 1e-5
-    saved = gpu_saved_from_oracle(c, fw, buf.info)
-    run_backward(buf, dev, saved=saved)
-    torch.cuda.synchronize()
-    assert relerr(host64(t["dx"]), bw["dx"]) <= TOL_BF16
-    assert relerr(host64(t["dw1"]), bw["dw1"]) <= TOL_BF16
-    assert relerr(host64(t["dw2"]), bw["dw2"]) <= TOL_BF16
-    assert relerr(host64(t["dw_router"]), bw["dw_router"]) <= TOL_F32
-    if c.shared:
-        assert relerr(host64(t["dws1"]), bw["dws1"]) <= TOL_BF16
-        assert relerr(host64(t["dws2"]), bw["dws2"]) <= TOL_BF16
