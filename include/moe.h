@@ -4,7 +4,9 @@
  * One layer, forward and backward, on one GPU. Every call enqueues HIP kernels
  * on the caller's stream and returns at once: no host synchronisation and no
  * device allocation. The calls keep no state between them (the opt-in timing
- * hook of moe_profile.h is per host thread), so they are re-entrant. The caller
+ * hook of moe_profile.h is per host thread), so they are re-entrant; the one
+ * exception is moe_dispatch_noalloc, whose fixed scratch array is shared by
+ * its calls on one GPU (see there). The caller
  * owns every buffer, including the tensors the forward produces and the
  * backward consumes.
  *
@@ -234,6 +236,23 @@ int moe_route_ec(const moe_config* cfg, const void* x, const float* w_router,
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot,
                  int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_dispatch without a workspace, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments (less ws, ws_bytes),
+ * outputs and semantics as moe_dispatch, with the same kernels; its scratch
+ * (the per-chunk expert histograms, ceil(T*k / 1024) * E int32) lives in a
+ * fixed 4 MiB device array of the library, one per GPU, kept until the process
+ * ends. Returns MOE_ERR_WORKSPACE, enqueuing nothing, when ceil(T*k / 1024) * E
+ * exceeds 2^20 (e.g. T*k above 4M assignments at E = 256). It calls no
+ * allocator: the first call on a device looks up the array's device address
+ * (hipGetSymbolAddress, with that device current) and keeps it. Every call on
+ * one GPU uses that GPU's one array: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller. Nothing in
+ * the array needs clearing between calls (each call writes what it reads). */
+int moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot,
+                         int32_t* row_token, void* x_perm, void* stream);
 
 /* Expert FFNs over the compacted rows (grouped matmul over ragged groups),
  * [SW] section on replacing the FFN by N expert copies; [LRMOE] variable-size

@@ -6,6 +6,7 @@ fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
 Entry points mirror the C ABI: moe_plan, moe_route, moe_route_noisy, moe_route_ec, moe_dispatch,
+moe_dispatch_noalloc,
 moe_expert_ffn, moe_combine, moe_aux_loss, moe_aux_noisy, moe_bias_update, moe_bias_quantile, moe_backward,
 moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
@@ -33,7 +34,8 @@ MOE_ROUTING_TOKEN_CHOICE, MOE_ROUTING_EXPERT_CHOICE = 0, 1
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
-EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_dispatch", "moe_expert_ffn",
+EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_dispatch", "moe_dispatch_noalloc",
+           "moe_expert_ffn",
            "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
@@ -96,6 +98,7 @@ def lib():
         L.moe_aux_noisy.argtypes = [cfg] + [_vp] * 6 + [ctypes.c_size_t, _vp]
         L.moe_route_ec.argtypes = [cfg] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         L.moe_dispatch.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_dispatch_noalloc.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_aux_loss.argtypes = [cfg, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -194,6 +197,11 @@ def moe_dispatch(cfg, x, topk_idx, expert_counts, expert_offsets, slot, row_toke
     _check(lib().moe_dispatch(ctypes.byref(cfg), _p(x), _p(topk_idx), _p(expert_counts), _p(expert_offsets),
                               _p(slot), _p(row_token), _p(x_perm), _p(ws), ws.numel() * ws.element_size(),
                               _stream(stream)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(cfg, x, topk_idx, expert_counts, expert_offsets, slot, row_token, x_perm, stream=None):
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(cfg), _p(x), _p(topk_idx), _p(expert_counts), _p(expert_offsets),
+                                      _p(slot), _p(row_token), _p(x_perm), _stream(stream)), "moe_dispatch_noalloc")
 
 
 def moe_expert_ffn(cfg, x_perm, expert_offsets, w1, w2, x, ws1, ws2, act_saved, h_saved, y_perm, act_shared,

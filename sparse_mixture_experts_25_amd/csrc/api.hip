@@ -1,8 +1,9 @@
 // C ABI of the MoE layer: argument validation, sizes, workspace carving and
 // the launch sequence of each call. No allocation and no host synchronisation.
-// The only state kept between calls is the opt-in stage-timing hook of
-// moe_profile.h, which is per host thread (a call reads the hook of the thread
-// that makes it), so calls from different threads never share it.
+// State kept between calls: the opt-in stage-timing hook of moe_profile.h,
+// which is per host thread (a call reads the hook of the thread that makes it),
+// and, for moe_dispatch_noalloc only, its fixed device scratch array (one per
+// GPU) with the cached per-device address of it (dispatch.hip).
 #include <math.h>
 #include <string.h>
 
@@ -272,6 +273,23 @@ int moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, in
                       c->num_tokens, c->d_model, c->num_experts, c->top_k, C, elem_bytes(c)};
   StageTimer pt("dispatch", (hipStream_t)stream);
   return launch_status(moe::launch_dispatch(a, (hipStream_t)stream));
+}
+
+int moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk_idx, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* slot, int32_t* row_token, void* x_perm, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+  const bool empty = c->num_tokens == 0;
+  if (!expert_counts || !expert_offsets || (!empty && (!x || !topk_idx || !slot || !row_token || !x_perm)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  // the per-chunk histograms must fit the library's fixed scratch array
+  if (!moe::dispatch_fits_scratch(c->num_tokens, c->top_k, c->num_experts)) return MOE_ERR_WORKSPACE;
+  moe::DispatchArgs a{x, topk_idx, expert_counts, expert_offsets, slot, row_token, x_perm, nullptr,
+                      c->num_tokens, c->d_model, c->num_experts, c->top_k, capacity_of(c), elem_bytes(c)};
+  StageTimer pt("dispatch", (hipStream_t)stream);
+  return launch_status(moe::launch_dispatch_noalloc(a, (hipStream_t)stream));
 }
 
 int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets, const void* w1,

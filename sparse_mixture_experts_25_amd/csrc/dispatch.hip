@@ -19,6 +19,8 @@
 //      giving pos, slot and row_token
 //   4. per token: copy the row of x into each of its kept slots (16-byte moves;
 //      each row of x is read once)
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -165,7 +167,51 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint8_t* __rest
   }
 }
 
+// Per-chunk histograms of the allocation-free dispatch: a file-scope device
+// array, one copy per GPU, held until the process ends. Its host-side name is a
+// stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the device (cached per device below).
+static __device__ __align__(256) int32_t scratch[kDispatchScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the device `st` belongs to (the current device
+// for the null stream); looked up once per device with that device current.
+hipError_t scratch_address(hipStream_t st, int32_t** out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);  // racing lookups store the same address
+  }
+  *out = reinterpret_cast<int32_t*>(p);
+  return hipSuccess;
+}
+
 }  // namespace
+
+bool dispatch_fits_scratch(int T, int k, int E) {
+  return (int64_t)dispatch_num_chunks(T, k) * E <= kDispatchScratchInts;
+}
+
+hipError_t launch_dispatch_noalloc(const DispatchArgs& a_in, hipStream_t st) {
+  if (!dispatch_fits_scratch(a_in.T, a_in.k, a_in.E)) return hipErrorInvalidValue;
+  DispatchArgs a = a_in;
+  hipError_t e = scratch_address(st, &a.ws_chunk);
+  if (e != hipSuccess) return e;
+  // every histogram entry the launch reads is written by it first: nothing to clear
+  return launch_dispatch(a, st);
+}
 
 int dispatch_num_chunks(int T, int k) {
   const int64_t total = (int64_t)T * k;

@@ -71,6 +71,12 @@ struct DispatchArgs {
 };
 int dispatch_num_chunks(int T, int k);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);
+// The same launches with the per-chunk histograms in a file-scope device array
+// of kDispatchScratchInts int32 (4 MiB) instead of a workspace; a.ws_chunk is
+// ignored. Needs dispatch_fits_scratch(T, k, E).
+constexpr int64_t kDispatchScratchInts = int64_t(1) << 20;
+bool dispatch_fits_scratch(int T, int k, int E);
+hipError_t launch_dispatch_noalloc(const DispatchArgs& a, hipStream_t st);
 
 // One grouped matmul launch.
 //  ragged-M kind (forward and input-gradient matmuls): for each group g,

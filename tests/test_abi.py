@@ -209,3 +209,25 @@ def test_plan_rejects_expert_matrices_past_32bit_offsets(d, f, act, dtype, ok):
         s, w, g = M.moe_saved(), M.moe_weights(), M.moe_grads()
         assert L.moe_backward(c, A, ctypes.byref(s), ctypes.byref(w), ctypes.byref(g), A, 1 << 40, N) == \
             M.MOE_ERR_UNSUPPORTED
+
+
+def test_dispatch_noalloc_validates_before_launch():
+    """The allocation-free dispatch refuses bad arguments, and configs whose
+    per-chunk histograms (ceil(T*k / 1024) * E int32) exceed its fixed 2^20-entry
+    scratch array, before any HIP call."""
+    L = M.lib()
+    Ei = M.MOE_ERR_INVALID_ARG
+    cfg = M.make_config(64, 64, 64, 4, 2, cf=1.0)
+    c = ctypes.byref(cfg)
+    assert L.moe_dispatch_noalloc(c, N, A, A, A, A, A, A, N) == Ei
+    assert L.moe_dispatch_noalloc(c, MIS, A, A, A, A, A, A, N) == Ei
+    assert L.moe_dispatch_noalloc(c, A, A, A, A, A, A, MIS, N) == Ei
+    assert L.moe_dispatch_noalloc(None, A, A, A, A, A, A, A, N) == Ei
+    ec = M.make_config(64, 64, 64, 4, 4, cf=1.0, routing="expert_choice")
+    assert L.moe_dispatch_noalloc(ctypes.byref(ec), A, A, A, A, A, A, A, N) == M.MOE_ERR_UNSUPPORTED
+    # 4096 chunks x 256 experts = 2^20 entries fits; one more chunk does not
+    fits = M.make_config(4096 * 1024 // 8, 64, 64, 256, 8)
+    over = M.make_config(4096 * 1024 // 8 + 128, 64, 64, 256, 8)
+    assert L.moe_dispatch_noalloc(ctypes.byref(over), A, A, A, A, A, A, A, N) == M.MOE_ERR_WORKSPACE
+    info = M.moe_plan_info()
+    assert L.moe_plan(ctypes.byref(fits), ctypes.byref(info)) == M.MOE_OK
