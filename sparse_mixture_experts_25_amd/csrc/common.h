@@ -67,9 +67,14 @@ __device__ __forceinline__ Split3 split3(float v) {
   return s;
 }
 
-// Rank of each expert group by row count (largest first, ties by lower index),
-// computed by one workgroup of `nthreads` threads: order[rank] = group. The
-// weight-gradient launches then start the longest contractions first.
+// Processing order of the groups of a weight-gradient launch, computed by one
+// workgroup of `nthreads` threads: order[position] = group. Groups with rows
+// come largest first (ties: lower index), so the longest contractions start
+// first; groups without rows (whose gradient is all zeros, a pure store) are
+// spread evenly between them, so their stores overlap other workgroups' matrix
+// work instead of forming a store-bound tail. With N groups with rows and Z
+// without, the i-th with rows sits at time (2i+1)/(2N) and the j-th without at
+// (2j+1)/(2Z) (ties: the one with rows first); position = rank by time.
 // rows_s: LDS scratch of at least E + has_shared ints (at most 1025).
 __device__ __forceinline__ void rank_groups_by_rows(const int32_t* __restrict__ offsets, int E, int shared_rows,
                                                     int has_shared, int32_t* __restrict__ order, int* rows_s,
@@ -77,14 +82,27 @@ __device__ __forceinline__ void rank_groups_by_rows(const int32_t* __restrict__ 
   const int G = E + has_shared;
   for (int g = threadIdx.x; g < G; g += nthreads) rows_s[g] = g < E ? offsets[g + 1] - offsets[g] : shared_rows;
   __syncthreads();
+  int Z = 0;
+  for (int h = 0; h < G; ++h) Z += rows_s[h] == 0;
+  const int N = G - Z;
   for (int g = threadIdx.x; g < G; g += nthreads) {
     const int r = rows_s[g];
-    int rank = 0;
+    int rank = 0;  // among the groups of the same kind
     for (int h = 0; h < G; ++h) {
       const int rh = rows_s[h];
-      rank += (rh > r) || (rh == r && h < g);
+      rank += r > 0 ? ((rh > r) || (rh == r && h < g)) : (rh == 0 && h < g);
     }
-    order[rank] = g;
+    int before;  // groups of the other kind placed before it
+    if (r > 0) {
+      const int64_t x = (int64_t)(2 * rank + 1) * Z - N;
+      before = x <= 0 ? 0 : (int)((x + 2 * (int64_t)N - 1) / (2 * (int64_t)N));
+      before = before < Z ? before : Z;
+    } else {
+      const int64_t x = (int64_t)(2 * rank + 1) * N - Z;
+      before = x < 0 ? 0 : (int)(x / (2 * (int64_t)Z)) + 1;
+      before = before < N ? before : N;
+    }
+    order[rank + before] = g;
   }
 }
 

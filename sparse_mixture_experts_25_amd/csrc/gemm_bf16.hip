@@ -10,8 +10,9 @@
 //     comes from the device offsets; the workgroup id is decoded in-kernel into
 //     (group, row tile, column tile), so no host round trip is needed.
 //   ragged-K (weight gradients): a fixed [M, N] output per group, contracted
-//     over that group's rows; a group without rows writes zeros. Groups run
-//     largest first.
+//     over that group's rows; a group without rows writes zeros. Groups with
+//     rows run largest first, the ones without spread between them
+//     (rank_groups_by_rows).
 //
 // Main loop: an NS-stage pipeline over BK-deep K steps. Every step is
 // brought into LDS with direct global->LDS 16-byte loads (each wave fills
@@ -44,6 +45,16 @@ namespace {
 
 
 // ------------------------------------------------------------ direct loads
+// A pointer every lane holds the same value of, returned as a wave-uniform
+// value (two readfirstlanes, each half widened through uint32_t), so that
+// arithmetic on it stays on the scalar unit.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return reinterpret_cast<const uint16_t*>((uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -200,7 +211,9 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   const uint32_t lds0 = lds_addr(smem);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is the same in every lane: as a scalar, the LDS block
+  // addresses of the direct loads are scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- locate the tile
@@ -236,6 +249,16 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       rows = a.shared_rows;
     }
     if (!group_in_part(a, rows)) return;  // the other launch of a split matmul
+    if (EPI == EPI_STORE && rows == 0) {
+      // a group without rows: its weight gradient is zero, stored straight from
+      // registers (no operand loads, no LDS staging)
+      uint16_t* Cg = reinterpret_cast<uint16_t*>(g < a.E ? a.C : a.C_sh) + (g < a.E ? (int64_t)g * a.strideC : 0);
+      for (int u = threadIdx.x; u < BM * BN / 8; u += 128 * WGN) {
+        const int mm = mb * BM + u / (BN / 8), nn = nb * BN + (u % (BN / 8)) * 8;
+        if (mm < a.M && nn < a.N) st128_nt(Cg + (int64_t)mm * a.ldc + nn, zero128());
+      }
+      return;
+    }
   }
   const bool sh = g >= a.E;
   const uint16_t* Ab = reinterpret_cast<const uint16_t*>(sh ? a.A_sh : a.A);
@@ -282,6 +305,10 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     return Borig + src * a.ldb + k0;
   };
 
+  // the operand origins are the same for the whole workgroup (the tile decode
+  // reaches every lane through LDS): as scalars, each K step moves a scalar base
+  Aorig = uniform_ptr(Aorig);
+  Borig = uniform_ptr(Borig);
   DmaPlan<BM, BK, NW> pa;
   DmaPlan<BN, BK, NW> pb;
   if (A_KC) pa.make_kc(wave, lane, a.lda, [&](int r) { return r < a_valid ? r : a_valid - 1; });
@@ -375,14 +402,26 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S][i], fb[S][j], acc[i][j], 0, 0, 0);
   };
   auto interleave = [&](auto fmv) {
-    // one LDS read, then a share of the MFMAs, RD times
     constexpr int FMV = decltype(fmv)::value;
     constexpr int RD = FMV == 0 ? 0 : FMV * (A_KC ? 1 : 2) + FN * (B_IS_KC ? 1 : 2);  // LDS reads per sub-step
     constexpr int MF = FMV * FN;                                                      // MFMAs per sub-step
+    if constexpr (A_KC && B_IS_KC) {
+      // both operands K-contiguous (one 16-byte read per fragment): every read of
+      // the next sub-step first, then this sub-step's MFMAs. The two register
+      // sets then stay distinct, and the reads have the whole sub-step to land
+      // (mixing them in let the compiler reuse the current set's registers, so
+      // each sub-step's first MFMAs waited for reads issued just before them).
+      if (RD > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+      }
+    } else {
+      // transposed reads (two per fragment): one LDS read, then a share of the MFMAs, RD times
 #pragma unroll
-    for (int r = 0; r < RD; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, RD > 0 ? (MF + RD - 1) / RD : 1, 0);
+      for (int r = 0; r < RD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, RD > 0 ? (MF + RD - 1) / RD : 1, 0);
+      }
     }
   };
 

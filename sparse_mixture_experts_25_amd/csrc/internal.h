@@ -125,8 +125,9 @@ struct GemmArgs {
   int split_part; int split_rows;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
-// order[0..E(+1)): groups sorted by row count, largest first (ties: lower index;
-// the shared group, index E, counts shared_rows rows).
+// order[0..E(+1)): the groups with rows sorted by row count, largest first
+// (ties: lower index; the shared group, index E, counts shared_rows rows), with
+// the groups without rows spread evenly between them (rank_groups_by_rows).
 hipError_t launch_group_order(const int32_t* offsets, int E, int shared_rows, int has_shared, int32_t* order,
                               hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
