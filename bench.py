@@ -41,8 +41,11 @@ PEAK_F32_VALU = 78.6e12
 # step of the aux-loss-free selection-bias update (the pages give no value)
 BIAS_GAMMA = 1e-3
 
-# Kernel sources whose hash a measured HBM-traffic figure is tied to.
-GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.h", "mfma_tile.h", "internal.h", "common.h", "api.hip")
+# Kernel sources whose hash a measured HBM-traffic figure is tied to (all of them:
+# the counter summaries cover every stage).
+KERNEL_SOURCES = ("api.hip", "balance.hip", "common.h", "dispatch.hip", "ec_route.hip", "gate_math.h", "gemm_bf16.hip",
+                  "gemm_common.h", "gemm_f32.hip", "internal.h", "mfma_tile.h", "noisy.hip", "router.hip",
+                  "router_bwd.hip", "rows.hip")
 
 
 def sources_sha(names):
@@ -60,25 +63,26 @@ def sources_sha(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, stage):
-    """HBM bytes per launch of `stage` from the committed counter summary
-    profiles/hbm_traffic_<workload>.txt (FETCH_SIZE + WRITE_SIZE per dispatch,
-    scaled by the same counters' reading for a plain copy of known size), or
-    None when there is none or the kernel sources changed since it was taken."""
+def measured_traffic(workload, stage=None):
+    """HBM bytes per launch of `stage` (or a dict of every stage's) from the
+    committed counter summary profiles/hbm_traffic_<workload>.txt (FETCH_SIZE +
+    WRITE_SIZE per dispatch, scaled by the same counters' reading for a plain copy
+    of known size), or None when there is none or the kernel sources changed since
+    it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
-    sha, val = None, None
+    sha, vals = None, {}
     with open(path) as fh:
         for ln in fh:
             parts = ln.split()
             if len(parts) >= 2 and parts[0] == "sources_sha":
                 sha = parts[1]
-            if len(parts) >= 2 and parts[0] == f"{stage}_bytes_per_launch":
-                val = float(parts[1])
-    if val is None or sha != sources_sha(GEMM_SOURCES):
+            if len(parts) >= 2 and parts[0].endswith("_bytes_per_launch"):
+                vals[parts[0][:-len("_bytes_per_launch")]] = float(parts[1])
+    if sha != sources_sha(KERNEL_SOURCES):
         return None
-    return val
+    return vals if stage is None else vals.get(stage)
 
 
 def stage_roofline(stage, work, ms, dtype="bf16"):
@@ -182,16 +186,17 @@ def stage_work(c, rows, ne_experts):
 
 
 def cpu_baseline_sized(c, inp, target_s=20.0, probe_tokens=16):
-    """Oracle timing on a sample of about `target_s` seconds: a `probe_tokens`
-    sample first; if that already took at least half the target (the largest
-    layers, whose oracle cost is mostly per expert) it is the result, else a
-    sample scaled linearly from it is timed."""
-    probe = min(probe_tokens, c.T)
-    first = cpu_baseline(c, inp, probe)
-    if first["seconds"] >= 0.5 * target_s or probe == c.T:
-        return first
-    n = int(probe * target_s / max(first["seconds"], 1e-3))
-    return cpu_baseline(c, inp, max(probe, min(c.T, n)))
+    """Oracle timing on a sample of about `target_s` seconds: start from
+    `probe_tokens` tokens and grow the sample (at most 8x per try, scaled by the
+    time the last try took) until a try takes at least half the target or covers
+    the whole batch; the last try is the result. (The oracle's cost has a large
+    per-expert part, so a small probe overstates the cost per token.)"""
+    n = min(probe_tokens, c.T)
+    while True:
+        r = cpu_baseline(c, inp, n)
+        if r["seconds"] >= 0.5 * target_s or n == c.T:
+            return r
+        n = min(c.T, max(n + 1, int(n * min(8.0, target_s / max(r["seconds"], 1e-3)))))
 
 
 class _ExpertsF64:
@@ -235,6 +240,8 @@ def cpu_baseline(c, inp, budget_tokens):
             oin[k] = _ExpertsF64(v, O.f64)
         else:
             oin[k] = O.f64(v[:budget_tokens] if k in ("x", "dy", "noise") else v)
+    if os.environ.get("MOE_ORACLE_THREADS"):
+        O.lib().orc_set_threads(int(os.environ["MOE_ORACLE_THREADS"]))
     spec = O.Spec.of(sub)
     fw = O.route(spec, oin["x"], oin["w_router"], oin.get("logit_offset"), oin.get("sel_bias"), oin.get("noise"))
     for e in np.unique(fw["idx"]):  # widen the reached experts' weights before the clock starts
@@ -243,7 +250,7 @@ def cpu_baseline(c, inp, budget_tokens):
     fw = O.forward(spec, oin)
     O.backward(spec, oin, fw, oin["dy"])
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = O.lib().orc_get_threads()  # what the oracle's OpenMP loops use
     return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(), "nproc": os.cpu_count(), "seconds": dt,
             "sample": f"{budget_tokens}-token batch of the same layer (same weights), forward+backward, "
@@ -313,6 +320,9 @@ def main():
                     help="oracle sample size for cpu_baseline (default: sized from a 16-token probe for about "
                          "20 s of host work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="OpenMP threads of the oracle timing (default: the host's setting); 1 gives the "
+                         "single-thread baseline")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB before every timed step, so the 256 MB "
@@ -325,6 +335,9 @@ def main():
                     help="measure the attainable HBM, matrix-core and fp32-ALU peaks with the library's probe "
                          "kernels, print them as one JSON line and exit")
     args = ap.parse_args()
+    if args.cpu_threads:
+        # set in the oracle's OpenMP runtime itself when it is loaded
+        os.environ["MOE_ORACLE_THREADS"] = str(args.cpu_threads)
     if args.gpus != 1:
         print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
               f"(there is no multi-GPU path).", file=sys.stderr)
@@ -457,6 +470,12 @@ def main():
                                for kk, vv in stage_roofline(k, work[k], v, c.dtype).items() if kk != "peak"}
                            for k, v in per_stage.items() if k in work},
     }
+    # counted HBM bytes / algorithmic bytes per stage (committed counter summary)
+    traffic = measured_traffic(c.name) or {}
+    for k, v in line["stage_roofline"].items():
+        if k in traffic and work[k][1]:
+            v["traffic"] = traffic[k]
+            v["traffic_over_algorithmic"] = round(traffic[k] / work[k][1], 3)
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")

@@ -93,6 +93,8 @@ def lib():
             "orc_round_array": (None, [i, ctypes.c_int64, D, D]),
             "orc_router_grads": (None, [i, i, i, i, D, D, D, D, D]),
             "orc_unpermute_bwd": (None, [i, i, i, i, D, D, I, D, D, D]),
+            "orc_set_threads": (None, [i]),
+            "orc_get_threads": (i, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)

@@ -46,6 +46,8 @@
 #include <numeric>
 #include <vector>
 
+#include <omp.h>
+
 #pragma STDC FP_CONTRACT OFF
 
 namespace {
@@ -169,6 +171,10 @@ double gate_deriv(int gate, double s) {
 }  // namespace
 
 extern "C" {
+
+// OpenMP threads of the parallel loops below (timing only; no arithmetic).
+void orc_set_threads(int n) { omp_set_num_threads(n); }
+int orc_get_threads() { return omp_get_max_threads(); }
 
 double orc_round_bf16(double v) { return round_bf16(v); }
 

@@ -197,12 +197,23 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
   const TX* rows[KM];
 #pragma unroll
   for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? dX_perm + (int64_t)c.s[r] * d : gr;
+  // every load of a vector is issued before any sum (a missing router or shared
+  // term loads the token's dy row instead and is skipped); the sums keep the
+  // order dy, kept rows by ascending r, router term, shared expert
+  const float* prr = dx_router ? dx_router + (int64_t)t * d : nullptr;
+  const TX* psh = dx_shared ? dx_shared + (int64_t)t * d : gr;
   for (int v = lane; v < d / V; v += 64) {
     u128 raw[KM];
 #pragma unroll
     for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    const u128 rdy = ld128(gr + v * V);
+    const u128 rsh = ld128(psh + v * V);
+    float4 q[V / 4];
+#pragma unroll
+    for (int e = 0; e < V / 4; ++e)
+      q[e] = prr ? reinterpret_cast<const float4*>(prr + v * V)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     float acc[V], tmp[V];
-    Elem<TX>::unpack(ld128(gr + v * V), acc);
+    Elem<TX>::unpack(rdy, acc);
 #pragma unroll
     for (int r = 0; r < KM; ++r) {
       if (c.s[r] < 0) continue;
@@ -210,16 +221,14 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
-    if (dx_router) {
-      const float* pr = dx_router + (int64_t)t * d + v * V;
+    if (prr) {
 #pragma unroll
-      for (int e = 0; e < V; e += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(pr + e);
-        acc[e] += q.x; acc[e + 1] += q.y; acc[e + 2] += q.z; acc[e + 3] += q.w;
+      for (int e = 0; e < V / 4; ++e) {
+        acc[4 * e] += q[e].x; acc[4 * e + 1] += q[e].y; acc[4 * e + 2] += q[e].z; acc[4 * e + 3] += q[e].w;
       }
     }
     if (dx_shared) {
-      Elem<TX>::unpack(ld128(dx_shared + (int64_t)t * d + v * V), tmp);
+      Elem<TX>::unpack(rsh, tmp);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
