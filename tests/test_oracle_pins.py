@@ -861,3 +861,6 @@ def test_relerr_sum_measures_against_the_terms():
     terms = np.array([2.0625 + 2.15625, 1.0, 1.0])
     assert relerr(a2, r2) > 0.01
     assert relerr_sum(a2, r2, terms) < 0.004
+    # a real error in the same cancelling sum (a dropped term of 0.25) still fails 2e-2
+    a3 = r2 + np.array([0.25, 0.0, 0.0])
+    assert relerr_sum(a3, r2, terms) > 0.05
