@@ -745,15 +745,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   if (!big) return small_tiles(a);
   // Groups capped at 512 rows or fewer (expert capacity): the host knows only
   // the cap, and the realised groups range from full (expert choice, balanced
-  // routing) to mostly empty (skewed routing that drops most assignments). The
-  // matmul then runs as two launches over the groups, each deciding on the
-  // device from the group's row count: 128 rows or more on 256x256 tiles (a
-  // group of 128-255 rows reads each weight slab once, and the waves past its
-  // rows skip their matrix work), the others (and empty ones) on the
+  // routing) to mostly empty (skewed routing that drops most assignments). A
+  // row-ragged matmul then runs as two launches over the groups, each deciding
+  // on the device from the group's row count: 128 rows or more on 256x256
+  // tiles (a group of 128-255 rows reads each weight slab once, and the waves
+  // past its rows skip their matrix work), the others (and empty ones) on the
   // weight-streaming 128x128 tiles. Dropless layers keep one launch: there the
   // zero-fill of empty experts overlaps the big groups' matrix work, which a
   // second launch would serialise.
   const bool capped = a.row_cap > 0 && a.row_cap <= 512 && a.E > 1;
+  // A capped layer's weight gradients contract over at most 512 rows (eight
+  // 64-deep steps): the short-contraction 128x128 tiles, four workgroups per
+  // CU, run them faster than the 256x256 pipeline.
+  if (capped && a.kind == 1) return small_tiles(a);
   if (!capped) return launch_tiles<256, 256, 64, 2, 4>(a, st);
   GemmArgs b = a;
   b.split_part = 1;

@@ -4,8 +4,9 @@ that every grouped matmul runs on the tiles the large workloads use.
 The grouped matmul picks its tiles on the host from the launch's row bound
 (max_rows) and widths: 256x256 tiles when the groups average at least 256 rows,
 every output width is at least 256 and the launch has at least 256 such tiles;
-for capped layers (expert capacity <= 512) the same matmul runs as a split pair,
-groups of >= 128 rows on 256x256 tiles and the rest on 128x128 tiles. `tile_plan`
+for capped layers (expert capacity <= 512) a row-ragged matmul runs as a split
+pair, groups of >= 128 rows on 256x256 tiles and the rest on 128x128 tiles, and
+the weight gradients (at most 512 rows deep) run on 128x128 tiles. `tile_plan`
 below restates that rule and each case asserts the plan it was built for, so a
 change of the rule that moves a case off its tiles fails here instead of
 silently narrowing the coverage.
@@ -18,9 +19,10 @@ B K-contiguous, epilogue, waves along N>):
   big_swiglu_shared      <256,256,64,2,0,1,2,4> SwiGLU forward, <..,0,0,4,4> SwiGLU
                          backward, and the rest as above, with the shared expert as
                          one more group of every launch; sigmoid gate + bias
-  big_capped_relu        the split pair of every matmul: split_part 1 on the
-                         256x256 instantiations above, split_part 2 on
-                         <128,128,64,2,0,..> and <128,128,32,2,1,0,0,2>
+  big_capped_relu        the split pair of every row-ragged matmul: split_part 1 on
+                         the 256x256 instantiations above, split_part 2 on
+                         <128,128,64,2,0,..>; both weight gradients on
+                         <128,128,32,2,1,0,0,2>
   big_capped_swiglu      the same split pair with the SwiGLU epilogues
   router_big_finegrained router weight gradient <256,256,64,2,1,0,5,4> over 16 token
                          chunks (fine-grained top-8 router shape: T 32768, d 2048,
@@ -77,7 +79,7 @@ def _tiles(kind, max_rows, groups, N, M=0, extra_group=False, row_cap=0):
     if not (avg >= 256 and dims and n_big >= 256):
         return "128"
     if 0 < row_cap <= 512 and groups > 1:
-        return "split"
+        return "split" if kind == 0 else "128"
     return "256"
 
 
@@ -120,10 +122,10 @@ CASES = {
     # capacity 512 (cf 2): skewed offsets leave groups from empty to full
     "big_capped_relu": (LayerConfig("big_capped_relu", T=16384, d=264, f=392, E=64, k=2, renorm=True,
                                     act="relu", cf=2.0, alpha=0.01, logit_offset="normal"),
-                        {g: "split" for g in _GEMMS}),
+                        {g: ("128" if "wgrad" in g else "split") for g in _GEMMS}),
     "big_capped_swiglu": (LayerConfig("big_capped_swiglu", T=16384, d=264, f=264, E=64, k=2, renorm=True,
                                       act="swiglu", cf=2.0, alpha=0.01, logit_offset="normal"),
-                          {g: "split" for g in _GEMMS}),
+                          {g: ("128" if "wgrad" in g else "split") for g in _GEMMS}),
     # router products at the full router shapes; a tiny expert width keeps the oracle cheap
     "router_big_finegrained": (LayerConfig("router_big_finegrained", T=32768, d=2048, f=16, E=128, k=4,
                                            renorm=True, act="relu", cf=0.0, alpha=0.01, logit_offset="logzipf"),
