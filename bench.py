@@ -10,7 +10,9 @@ tokens, d_model=7168, 256 routed SwiGLU experts 7168->2048->7168 plus one
 always-on shared expert of the same shape, sigmoid gate with a per-expert
 selection bias, top-8 renormalised, dropless, bf16 activations and weights, fp32
 router). --config picks another (switch_base, gshard_top2, finegrained_top8,
-tiny_f32).
+tiny_f32). The dispatch is fused into the expert matmuls: moe_dispatch writes
+only the positions and moe_expert_ffn_rows / moe_backward read the routed rows
+of x through row_token; --x-perm times the layer with the permuted copy instead.
 
 Prints one JSON line (see the keys below). Also measured and reported:
   roofline: the stage with the largest per-launch time, timed with HIP events on
@@ -146,9 +148,10 @@ class HipEvents:
         return ms.value
 
 
-def stage_work(c, rows, ne_experts):
+def stage_work(c, rows, ne_experts, permuted_copy=False):
     """Algorithmic (flops, bytes) of one launch of each stage, from the realised routing.
-    rows: kept routed rows; ne_experts: experts with at least one row."""
+    rows: kept routed rows; ne_experts: experts with at least one row; permuted_copy:
+    the dispatch writes x_perm (otherwise the matmuls read the rows of x in place)."""
     T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
     ER = 2 * E if c.gate == "noisy_topk" else E  # router rows (clean + noise for noisy gating)
     f1 = 2 * f if c.act == "swiglu" else f
@@ -162,8 +165,10 @@ def stage_work(c, rows, ne_experts):
     return {
         "route": (2 * T * d * ER, T * d * eb + ER * d * 4 + T * ER * 4 + T * k * 8),
         # logits, softmax (probs + transposed copy), selection, token tables, gather
-        "route_ec": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 * 6 + rows * (d * eb * 2 + 4)),
-        "dispatch": (0, T * k * 4 * 3 + T * d * eb + rows * d * eb + rows * 4),
+        "route_ec": (2 * T * d * E, T * d * eb + E * d * 4 + T * E * 4 * 6 + rows * 4 +
+                     (rows * d * eb * 2 if permuted_copy else 0)),
+        # token tables (indices read, positions written, slots written), row map; the copy
+        "dispatch": (0, T * k * 4 * 3 + rows * 4 + ((T * d * eb + rows * d * eb) if permuted_copy else 0)),
         # SwiGLU stores the pre-activations and h; ReLU only h
         "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * ((f1 if c.act == "swiglu" else 0) + f) * eb),
         "ffn_gemm2": (2 * R * f * d, W2 + R * f * eb + R * d * eb),
@@ -324,6 +329,9 @@ def main():
                     help="OpenMP threads of the oracle timing (default: the host's setting); 1 gives the "
                          "single-thread baseline")
     ap.add_argument("--stages", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--x-perm", action="store_true",
+                    help="materialise the permuted copy of x (moe_dispatch writes x_perm, moe_expert_ffn reads "
+                         "it); by default the expert matmuls read the routed rows of x in place")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB before every timed step, so the 256 MB "
                          "last-level cache cannot serve the step's reads from the previous one; the per-step "
@@ -367,7 +375,7 @@ def main():
     inp = make_inputs(c, seed=args.seed, device="cuda")
     cfg = M.make_config(c.T, c.d, c.f, c.E, c.k, cf=c.cf, renorm=c.renorm, gate=c.gate, act=c.act,
                         dtype=c.dtype, alpha=c.alpha, shared=c.shared, routing=c.routing)
-    buf = M.LayerBuffers.allocate(cfg)
+    buf = M.LayerBuffers.allocate(cfg, rows_in_place=not args.x_perm)
     stream = torch.cuda.current_stream()
 
     biased = c.gate in ("sigmoid_bias", "sqrt_softplus_bias")
@@ -428,7 +436,7 @@ def main():
     offs = buf.t["expert_offsets"].cpu()
     rows = int(offs[-1])
     ne = int(((offs[1:] - offs[:-1]) > 0).sum())
-    work = stage_work(c, rows, ne)
+    work = stage_work(c, rows, ne, permuted_copy=args.x_perm)
     roof = stage_roofline(dom, work[dom], dom_ms, c.dtype)
     roof["traffic"] = measured_traffic(c.name, dom)
     roof["kernel"] = dom
@@ -462,7 +470,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, random-init weights of the layer's shapes)",
         "config": {"workload": c.name, "T": c.T, "d_model": c.d, "d_ff": c.f, "experts": c.E, "top_k": c.k,
                    "capacity_factor": c.cf, "act": c.act, "gate": c.gate, "kept_rows": rows,
-                   "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12},
+                   "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
+                   "permuted_copy": bool(args.x_perm)},
         "roofline": roof,
         "zero_fill": zero_fill,
         # every stage against its own roofline, from the per-stage pre-pass times

@@ -110,7 +110,7 @@ typedef struct moe_saved {
   const int32_t* slot;           /* [T, k] row in the permuted buffers, -1 = dropped */
   const int32_t* expert_counts;  /* [E] assignments per expert before drops */
   const int32_t* expert_offsets; /* [E+1] first permuted row of each expert */
-  const void* x_perm;            /* [R, d]  act */
+  const void* x_perm;            /* [R, d]  act, or NULL: routed rows read as x[row_token[r]] */
   const void* act_saved;         /* [R, f1] act: pre-activation(s); SwiGLU only (ReLU: may be NULL) */
   const void* h_saved;           /* [R, f]  act: activation fed to the second matmul */
   const void* y_perm;            /* [R, d]  act: expert outputs */
@@ -118,6 +118,7 @@ typedef struct moe_saved {
   const void* h_shared;          /* [T, f]  shared expert (NULL without one) */
   const float* noisy_logits;     /* [T, 2E] clean | noise logits (noisy gating only, else NULL) */
   const float* noise;            /* [T, E]  eps (noisy gating only, else NULL) */
+  const int32_t* row_token;      /* [R] token of each routed row; needed when x_perm is NULL */
 } moe_saved;
 
 /* Layer parameters (device memory). */
@@ -213,8 +214,8 @@ int moe_aux_noisy(const moe_config* cfg, const float* logits2, const float* nois
  * (k = E; moe_backward needs no topk_idx in this mode). A token no expert took
  * gets y = x. Requires cfg->routing == MOE_ROUTING_EXPERT_CHOICE.
  * x [T,d] act, w_router [E,d]; outputs probs [T,E], topk_w [T,E], slot [T,E],
- * expert_counts [E], expert_offsets [E+1], row_token [E*C'], x_perm [E*C',d].
- * Needs the workspace. */
+ * expert_counts [E], expert_offsets [E+1], row_token [E*C'], x_perm [E*C',d]
+ * or NULL (no permuted copy: see moe_expert_ffn_rows). Needs the workspace. */
 int moe_route_ec(const moe_config* cfg, const void* x, const float* w_router,
                  const float* logit_offset, float* probs, float* topk_w, int32_t* slot,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
@@ -232,7 +233,11 @@ int moe_route_ec(const moe_config* cfg, const void* x, const float* w_router,
  * topk_idx may come from moe_route or from the caller (values must lie in [0,E)).
  * Token-choice routing only (MOE_ERR_UNSUPPORTED otherwise), as is moe_route.
  * Outputs: expert_counts [E], expert_offsets [E+1], slot [T,k], row_token [R],
- * x_perm [R,d] act. Needs the workspace. */
+ * x_perm [R,d] act. x_perm may be NULL: only the positions are written (x may
+ * then be NULL too), and the expert matmuls read each routed row from x
+ * through row_token instead ([WIKI], cross-cutting findings on fusing dispatch
+ * into the expert matmuls: moe_expert_ffn_rows, and moe_backward with
+ * moe_saved.x_perm NULL). Needs the workspace. */
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot,
                  int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes, void* stream);
@@ -275,6 +280,21 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* exp
                    const void* ws2, void* act_saved, void* h_saved, void* y_perm,
                    void* act_shared, void* h_shared, void* y_shared, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn without the permuted copy: the dispatch step fused into the
+ * first matmul's operand loads ([WIKI], cross-cutting findings: the fused
+ * dispatch / first linear / activation / second linear / combine pipeline of
+ * the MegaMoE and Mixture-of-Kittens kernels). Routed row r is read as
+ * x[row_token[r]] (row_token [R] as written by moe_dispatch or moe_route_ec,
+ * device memory); everything else, outputs included, is as in moe_expert_ffn,
+ * and the results are bitwise the same. x [T,d] serves both the routed rows
+ * and the shared expert. Needs T*d*sizeof(act) < 4 GiB (MOE_ERR_HIP
+ * otherwise). Needs the workspace. */
+int moe_expert_ffn_rows(const moe_config* cfg, const void* x, const int32_t* row_token,
+                        const int32_t* expert_offsets, const void* w1, const void* w2,
+                        const void* ws1, const void* ws2, void* act_saved, void* h_saved,
+                        void* y_perm, void* act_shared, void* h_shared, void* y_shared,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: [SW] eq. (2) plus the residual.
  *   y[t] = x[t] + sum over kept r of topk_w[t,r] * y_perm[slot[t,r]] (+ y_shared[t])
@@ -339,6 +359,8 @@ int moe_bias_quantile(const moe_config* cfg, const float* probs, float* sel_bias
  * H = h + eps softplus(n), the importance loss through the gates and the load
  * loss through Phi, also to each token's rival expert); w_router and dw_router
  * are [2E, d]; s->noisy_logits and s->noise must be set.
+ * The routed rows of x for dw1 come from s->x_perm, or, when it is NULL, from
+ * s->x through s->row_token (gathered as they are loaded; bitwise the same).
  * dy: [T,d] act. s, w, g: host structs holding device pointers. Needs the workspace. */
 int moe_backward(const moe_config* cfg, const void* dy, const moe_saved* s,
                  const moe_weights* w, const moe_grads* g, void* ws, size_t ws_bytes,

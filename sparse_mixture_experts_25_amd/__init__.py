@@ -6,9 +6,8 @@ fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
 Entry points mirror the C ABI: moe_plan, moe_route, moe_route_noisy, moe_route_ec, moe_dispatch,
-moe_dispatch_noalloc,
-moe_expert_ffn, moe_combine, moe_aux_loss, moe_aux_noisy, moe_bias_update, moe_bias_quantile, moe_backward,
-moe_status_string.
+moe_dispatch_noalloc, moe_expert_ffn, moe_expert_ffn_rows, moe_combine, moe_aux_loss, moe_aux_noisy,
+moe_bias_update, moe_bias_quantile, moe_backward, moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
 ``forward`` / ``backward`` issue the ABI calls in order on those buffers.
 """
@@ -35,7 +34,7 @@ MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
 EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_dispatch", "moe_dispatch_noalloc",
-           "moe_expert_ffn",
+           "moe_expert_ffn", "moe_expert_ffn_rows",
            "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
@@ -69,7 +68,7 @@ _vp = ctypes.c_void_p
 class moe_saved(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "probs", "topk_idx", "topk_w", "slot", "expert_counts",
                                    "expert_offsets", "x_perm", "act_saved", "h_saved", "y_perm",
-                                   "act_shared", "h_shared", "noisy_logits", "noise")]
+                                   "act_shared", "h_shared", "noisy_logits", "noise", "row_token")]
 
 
 class moe_weights(ctypes.Structure):
@@ -212,6 +211,14 @@ def moe_expert_ffn(cfg, x_perm, expert_offsets, w1, w2, x, ws1, ws2, act_saved, 
                                 _stream(stream)), "moe_expert_ffn")
 
 
+def moe_expert_ffn_rows(cfg, x, row_token, expert_offsets, w1, w2, ws1, ws2, act_saved, h_saved, y_perm, act_shared,
+                        h_shared, y_shared, ws, stream=None):
+    _check(lib().moe_expert_ffn_rows(ctypes.byref(cfg), _p(x), _p(row_token), _p(expert_offsets), _p(w1), _p(w2),
+                                     _p(ws1), _p(ws2), _p(act_saved), _p(h_saved), _p(y_perm), _p(act_shared),
+                                     _p(h_shared), _p(y_shared), _p(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "moe_expert_ffn_rows")
+
+
 def moe_combine(cfg, x, y_perm, slot, topk_w, y_shared, y, stream=None):
     _check(lib().moe_combine(ctypes.byref(cfg), _p(x), _p(y_perm), _p(slot), _p(topk_w), _p(y_shared), _p(y),
                              _stream(stream)), "moe_combine")
@@ -250,7 +257,9 @@ class LayerBuffers:
     t: dict
 
     @staticmethod
-    def allocate(cfg: moe_config, device="cuda", backward=True) -> "LayerBuffers":
+    def allocate(cfg: moe_config, device="cuda", backward=True, rows_in_place=False) -> "LayerBuffers":
+        """rows_in_place: no permuted copy of x (x_perm); the expert matmuls read
+        the routed rows from x through row_token."""
         info = moe_plan(cfg)
         T, d, f, E, k = cfg.num_tokens, cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k
         R, f1 = int(info.max_rows), int(info.f1)
@@ -259,9 +268,11 @@ class LayerBuffers:
         e = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=device)
         t = dict(probs=e((T, E), f32), topk_idx=e((T, k), i32), topk_w=e((T, k), f32),
                  expert_counts=e((E,), i32), expert_offsets=e((E + 1,), i32), slot=e((T, k), i32),
-                 row_token=e((max(R, 1),), i32), x_perm=e((max(R, 1), d), dt),
+                 row_token=e((max(R, 1),), i32),
                  h_saved=e((max(R, 1), f), dt), y_perm=e((max(R, 1), d), dt), y=e((T, d), dt),
                  aux=e((1,), f32), ws=e((max(int(info.workspace_bytes), 256),), torch.uint8))
+        if not rows_in_place:
+            t.update(x_perm=e((max(R, 1), d), dt))
         relu = cfg.act == MOE_ACT_RELU  # ReLU keeps only h (its sign is the derivative's mask)
         if not relu:
             t.update(act_saved=e((max(R, 1), f1), dt))
@@ -281,24 +292,30 @@ class LayerBuffers:
 
 
 def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
-    """moe_route -> moe_dispatch (or moe_route_ec) -> moe_expert_ffn -> moe_combine (-> moe_aux_loss)."""
+    """moe_route -> moe_dispatch (or moe_route_ec) -> moe_expert_ffn (moe_expert_ffn_rows without x_perm)
+    -> moe_combine (-> moe_aux_loss)."""
     c, t = buf.cfg, buf.t
     if c.gate == MOE_GATE_NOISY_TOPK:
         moe_route_noisy(c, inp["x"], inp["w_router"], inp["noise"], t["noisy_logits"], t["probs"], t["topk_idx"],
                         t["topk_w"], stream)
         moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
-                     t["row_token"], t["x_perm"], t["ws"], stream)
+                     t["row_token"], t.get("x_perm"), t["ws"], stream)
     elif c.routing == MOE_ROUTING_EXPERT_CHOICE:
         moe_route_ec(c, inp["x"], inp["w_router"], inp.get("logit_offset"), t["probs"], t["topk_w"], t["slot"],
-                     t["expert_counts"], t["expert_offsets"], t["row_token"], t["x_perm"], t["ws"], stream)
+                     t["expert_counts"], t["expert_offsets"], t["row_token"], t.get("x_perm"), t["ws"], stream)
     else:
         moe_route(c, inp["x"], inp["w_router"], inp.get("logit_offset"), inp.get("sel_bias"), t["probs"],
                   t["topk_idx"], t["topk_w"], stream)
         moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
-                     t["row_token"], t["x_perm"], t["ws"], stream)
-    moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
-                   inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
-                   t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
+                     t["row_token"], t.get("x_perm"), t["ws"], stream)
+    if "x_perm" in t:
+        moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
+                       inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
+                       t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
+    else:
+        moe_expert_ffn_rows(c, inp["x"], t["row_token"], t["expert_offsets"], inp["w1"], inp["w2"], inp.get("ws1"),
+                            inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
+                            t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
     moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
     if aux and c.gate == MOE_GATE_NOISY_TOPK:
         moe_aux_noisy(c, t["noisy_logits"], inp["noise"], t["topk_idx"], t["topk_w"], t["aux"], t["ws"], stream)
@@ -307,7 +324,7 @@ def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
 
 
 SAVED_KEYS = ["probs", "topk_idx", "topk_w", "slot", "expert_counts", "expert_offsets", "x_perm", "act_saved",
-              "h_saved", "y_perm", "act_shared", "h_shared", "noisy_logits"]
+              "h_saved", "y_perm", "act_shared", "h_shared", "noisy_logits", "row_token"]
 
 
 def backward(buf: LayerBuffers, inp: dict, dy, saved: dict | None = None, stream=None):

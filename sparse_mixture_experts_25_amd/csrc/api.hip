@@ -245,7 +245,7 @@ int moe_route_ec(const moe_config* c, const void* x, const float* w_router, cons
   if (c->routing != MOE_ROUTING_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;
   if (!w_router || !expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
-  if (!empty && (!x || !probs || !topk_w || !slot || !row_token || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if (!empty && (!x || !probs || !topk_w || !slot || !row_token)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   const int C = capacity_of(c);
   if (!ws || ws_bytes < workspace_of(c, max_rows_of(c, C))) return MOE_ERR_WORKSPACE;
@@ -263,7 +263,8 @@ int moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, in
   if (st) return st;
   if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;
-  if (!expert_counts || !expert_offsets || (!empty && (!x || !topk_idx || !slot || !row_token || !x_perm)))
+  // x_perm is optional (NULL: positions only); x is read only to fill it
+  if (!expert_counts || !expert_offsets || (!empty && (!topk_idx || !slot || !row_token || (x_perm && !x))))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   const int C = capacity_of(c);
@@ -281,7 +282,8 @@ int moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk
   if (st) return st;
   if (c->routing != MOE_ROUTING_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
   const bool empty = c->num_tokens == 0;
-  if (!expert_counts || !expert_offsets || (!empty && (!x || !topk_idx || !slot || !row_token || !x_perm)))
+  // x_perm is optional (NULL: positions only); x is read only to fill it
+  if (!expert_counts || !expert_offsets || (!empty && (!topk_idx || !slot || !row_token || (x_perm && !x))))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   // the per-chunk histograms must fit the library's fixed scratch array
@@ -292,22 +294,30 @@ int moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk
   return launch_status(moe::launch_dispatch_noalloc(a, (hipStream_t)stream));
 }
 
-int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets, const void* w1,
-                   const void* w2, const void* x, const void* ws1, const void* ws2, void* act_saved,
-                   void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
-                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The expert FFNs; routed rows from x_perm, or (x_perm NULL) from x through
+// row_token, gathered as the first matmul loads them.
+int expert_ffn(const moe_config* c, const void* x_perm, const int32_t* row_token, const int32_t* expert_offsets,
+               const void* w1, const void* w2, const void* x, const void* ws1, const void* ws2, void* act_saved,
+               void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
+               size_t ws_bytes, void* stream) {
   int st = check_config(c);
   if (st) return st;
   const bool empty = c->num_tokens == 0;
   // ReLU: the pre-activations are optional (the backward takes the sign of h)
   const bool need_act = c->act == MOE_ACT_SWIGLU;
-  if (!expert_offsets || !w1 || !w2 || (!empty && (!x_perm || (need_act && !act_saved) || !h_saved || !y_perm)))
+  const bool rows_in_place = x_perm == nullptr;
+  if (!expert_offsets || !w1 || !w2 ||
+      (!empty && ((rows_in_place ? (!x || !row_token) : false) || (need_act && !act_saved) || !h_saved || !y_perm)))
     return MOE_ERR_INVALID_ARG;
   const bool sh = c->num_shared_experts > 0;
   if (sh && (!ws1 || !ws2 || (!empty && (!x || (need_act && !act_shared) || !h_shared || !y_shared))))
     return MOE_ERR_INVALID_ARG;
   if (!sh && (ws1 || ws2 || act_shared || h_shared || y_shared)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x_perm, w1, w2, act_saved, h_saved, y_perm};
+  const void* ptrs[] = {x_perm, x, w1, w2, act_saved, h_saved, y_perm};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
   const int C = capacity_of(c);
@@ -327,7 +337,11 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g1.offsets = expert_offsets; g1.E = E; g1.shared_rows = shr;
   g1.max_rows = R;
   g1.row_cap = C > 0 ? C : 0;
-  g1.A = x_perm; g1.lda = d;
+  g1.A = rows_in_place ? x : x_perm; g1.lda = d;
+  if (rows_in_place) {
+    g1.a_rows = row_token;
+    g1.src_rows = T;
+  }
   g1.B = w1; g1.ldb = d; g1.strideB = (int64_t)f1 * d;
   g1.A_sh = x; g1.B_sh = ws1;
   g1.C = act_saved; g1.ldc = f1; g1.C_sh = act_shared;
@@ -348,6 +362,27 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   g2.A_sh = h_shared; g2.B_sh = ws2;
   g2.C = y_perm; g2.ldc = d; g2.C_sh = y_shared;
   return gemm(c, g2, s, "ffn_gemm2");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                   const void* w2, const void* x, const void* ws1, const void* ws2, void* act_saved,
+                   void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (c && c->num_tokens > 0 && !x_perm) return MOE_ERR_INVALID_ARG;
+  return expert_ffn(c, x_perm, nullptr, expert_offsets, w1, w2, x, ws1, ws2, act_saved, h_saved, y_perm, act_shared,
+                    h_shared, y_shared, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_rows(const moe_config* c, const void* x, const int32_t* row_token, const int32_t* expert_offsets,
+                        const void* w1, const void* w2, const void* ws1, const void* ws2, void* act_saved,
+                        void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return expert_ffn(c, nullptr, row_token, expert_offsets, w1, w2, x, ws1, ws2, act_saved, h_saved, y_perm,
+                    act_shared, h_shared, y_shared, ws, ws_bytes, stream);
 }
 
 int moe_combine(const moe_config* c, const void* x, const void* y_perm, const int32_t* slot, const float* topk_w,
@@ -414,8 +449,10 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   const bool noisy = c->gate == MOE_GATE_NOISY_TOPK;
   if (noisy && !empty && (!sv->noisy_logits || !sv->noise)) return MOE_ERR_INVALID_ARG;
   const bool relu = c->act == MOE_ACT_RELU;  // the ReLU mask comes from h > 0, which equals act > 0
-  if (!empty && (!dy || !sv->x || !sv->probs || (!ec && !sv->topk_idx) || !sv->topk_w || !sv->slot || !sv->x_perm ||
-                 (!relu && !sv->act_saved) || !sv->h_saved || !sv->y_perm || !g->dx))
+  // routed rows of x: x_perm, or (x_perm NULL) x through row_token
+  if (!empty && (!dy || !sv->x || !sv->probs || (!ec && !sv->topk_idx) || !sv->topk_w || !sv->slot ||
+                 (!sv->x_perm && !sv->row_token) || (!relu && !sv->act_saved) || !sv->h_saved || !sv->y_perm ||
+                 !g->dx))
     return MOE_ERR_INVALID_ARG;
   if (!w->w_router || !w->w1 || !w->w2 || !g->dw_router || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
   if (sh && (!w->ws1 || !w->ws2 || !g->dws1 || !g->dws2 ||
@@ -507,7 +544,8 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   a1.A_sh = dA_sh; a1.B_sh = w->ws1;
   a1.C = dXp; a1.ldc = d; a1.C_sh = dX_sh;
   if ((st = gemm(c, a1, s, "bwd_dgrad1"))) return st;
-  // dW1_e = dA^T x_perm over the expert's rows
+  // dW1_e = dA^T x_perm over the expert's rows (x_perm's rows gathered from x
+  // through row_token when no permuted copy was made)
   moe::GemmArgs w1g{};
   w1g.kind = 1;
   w1g.epi = moe::EPI_STORE;
@@ -518,7 +556,11 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
   w1g.order = order;
   w1g.offsets = sv->expert_offsets; w1g.E = E; w1g.shared_rows = shr;
   w1g.A = dA; w1g.lda = f1;
-  w1g.B = sv->x_perm; w1g.ldb = d;
+  w1g.B = sv->x_perm ? sv->x_perm : sv->x; w1g.ldb = d;
+  if (!sv->x_perm) {
+    w1g.b_rows = sv->row_token;
+    w1g.src_rows = T;
+  }
   w1g.A_sh = dA_sh; w1g.B_sh = sv->x;
   w1g.C = g->dw1; w1g.ldc = d; w1g.strideC = (int64_t)f1 * d; w1g.C_sh = g->dws1;
   if ((st = gemm(c, w1g, s, "bwd_wgrad1"))) return st;

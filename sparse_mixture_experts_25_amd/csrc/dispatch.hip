@@ -18,7 +18,8 @@
 //      same expert; the rank is the popcount of that set below the lane),
 //      giving pos, slot and row_token
 //   4. per token: copy the row of x into each of its kept slots (16-byte moves;
-//      each row of x is read once)
+//      each row of x is read once); skipped when the caller passes no x_perm
+//      (the expert matmuls then read the rows of x through row_token)
 #include <atomic>
 
 #include "common.h"
@@ -229,9 +230,10 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   if (nch == 0) return hipGetLastError();  // no tokens: counts and offsets are all zero
   hipLaunchKernelGGL(assign_kernel, dim3(nch), dim3(256), 4 * a.E * sizeof(int32_t), st, a.topk_idx,
                      total, a.k, a.E, a.capacity, a.ws_chunk, a.offsets, a.slot, a.row_token);
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3((a.T + 3) / 4), dim3(256), 0, st,
-                     (const uint8_t*)a.x, a.slot, a.T, a.k, (int64_t)a.d * a.elem_bytes,
-                     (uint8_t*)a.x_perm);
+  if (a.x_perm)  // without x_perm the matmuls read the rows through row_token
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3((a.T + 3) / 4), dim3(256), 0, st,
+                       (const uint8_t*)a.x, a.slot, a.T, a.k, (int64_t)a.d * a.elem_bytes,
+                       (uint8_t*)a.x_perm);
   return hipGetLastError();
 }
 

@@ -216,7 +216,7 @@ hipError_t launch_route_ec(const RouteEcArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(ec_table_kernel, dim3((a.T + 63) / 64, (a.E + 63) / 64), dim3(256), 0, st, selpos, a.probs,
                      a.T, a.E, a.slot, a.topk_w);
   const int64_t rows = (int64_t)a.E * a.Cp;
-  if (rows > 0)
+  if (rows > 0 && a.x_perm)  // without x_perm the matmuls read the rows through row_token
     hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
                        (const uint8_t*)a.x, a.row_token, rows, a.T, (int64_t)a.d * a.elem_bytes,
                        (uint8_t*)a.x_perm);

@@ -95,6 +95,24 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
         : "memory");
 }
 
+// One 4-byte global->LDS load per lane: lane i lands at `lds` + 4*i.
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -162,6 +180,24 @@ struct DmaPlan {
       dma16s<NT>(v, base, lds_tile + (wave * Q + q) * 1024);
     }
   }
+  // An MN-contiguous operand whose k-rows are gathered: the k-row of load q
+  // of this lane is row rowq[q] of the operand (past the end of K the last
+  // row again, which the caller zeroes in LDS); column chunks clamped to
+  // cvalid as in make_mn.
+  template <bool NT>
+  __device__ void issue_mn_rows(const uint16_t* base, uint32_t lds_tile, int wave, int lane, const int (&rowq)[Q],
+                                int64_t ld, int cvalid) const {
+    constexpr int CPR = R / 8;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int p = (wave * Q + q) * 64 + lane;
+      const int c = mn_chunk<R>(p / CPR, p % CPR);
+      const int cc = c < cvalid ? c : cvalid - 1;
+      dma16s<NT>((uint32_t)(((int64_t)rowq[q] * ld + 8 * cc) * 2), base, lds_tile + (wave * Q + q) * 1024);
+    }
+  }
+  // the k-row (within the step) of load q of this lane
+  __device__ static int mn_krow(int wave, int lane, int q) { return ((wave * Q + q) * 64 + lane) / (R / 8); }
   // The partial last step of an MN-contiguous operand (make_mn plan): k-rows
   // at or past kv (1 <= kv < BK) read k-row kv-1 instead, so every address
   // stays inside the group; the caller zeroes those k-rows in LDS.
@@ -188,7 +224,12 @@ struct DmaPlan {
 template <int WGN, int KIND>
 constexpr int waves_per_simd() { return WGN == 4 ? 2 : (KIND == 1 ? 4 : 3); }
 
-template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN>
+// GB (weight gradients): B's k-rows of the routed groups are gathered through
+// GemmArgs::b_rows. Each wave brings the row indices of a step into its own
+// two-slot LDS ring with one more direct load, issued with the operand loads
+// two steps earlier, and reads its lanes' indices into registers one step
+// before the operand loads that use them go out.
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN, int GB>
 __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WGN, KIND>(), waves_per_simd<WGN, KIND>()))) void gemm_bf16_kernel(
     GemmArgs a) {
   constexpr int kBK = BK;
@@ -202,8 +243,11 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   constexpr int CP = BN + 8;  // padded row of the staged fp32 tile
   constexpr int HM = BM / 2;  // the fp32 tile is staged half (one wave row) at a time
   constexpr int kStageBytes = HM * CP * 4;
-  constexpr int kLds = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
-  constexpr int L = (BM + BN) * BK * 2 / 1024 / NW;  // direct loads per wave per K step
+  constexpr int kRingOff = kOperandBytes;            // GB: index rings (512 bytes per wave), after the stages
+  constexpr int kLoopBytes = kOperandBytes + (GB ? NW * 512 : 0);
+  constexpr int kLds = kLoopBytes > kStageBytes ? kLoopBytes : kStageBytes;
+  constexpr int L = (BM + BN) * BK * 2 / 1024 / NW + GB;  // direct loads per wave per K step
+  static_assert(!GB || (KIND == 1 && BK <= 64 && NS == 2), "row gathers are for the weight gradients");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
   __shared__ __attribute__((aligned(16))) int info[12];
 
@@ -270,8 +314,12 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   const uint16_t* Aorig;
   const uint16_t* Borig;
   int a_valid, b_valid;  // KC: valid rows of the tile; MN: valid 8-column chunks
+  // routed rows of A read in place through the row map (ragged-M)
+  const bool ga = KIND == 0 && a.a_rows && !sh;
+  // routed k-rows of B gathered through the row map (ragged-K)
+  const bool gb = GB && !sh;
   if (KIND == 0) {
-    Aorig = Ab + (r0 + mrow0) * a.lda;
+    Aorig = ga ? Ab : Ab + (r0 + mrow0) * a.lda;
     a_valid = min(rows - mrow0, BM);
     if (B_KC) {
       Borig = Bb;
@@ -281,29 +329,12 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       b_valid = min(a.N - nb * BN, BN) / 8;
     }
   } else {
-    Aorig = Ab + r0 * a.lda + (int64_t)mb * BM;  // [rows][M]
-    Borig = Bb + r0 * a.ldb + (int64_t)nb * BN;  // [rows][N]
+    Aorig = Ab + r0 * a.lda + (int64_t)mb * BM;                  // [rows][M]
+    Borig = Bb + (gb ? 0 : r0 * a.ldb) + (int64_t)nb * BN;  // [rows][N]
     a_valid = min(a.M - mb * BM, BM) / 8;
     b_valid = min(a.N - nb * BN, BN) / 8;
   }
   const int h0 = nb * (BN / 2);  // SwiGLU: first h column of this tile
-
-  // global address of (tile row r, k0) for the K-contiguous operands
-  auto a_row = [&](int r, int k0) {
-    return Aorig + (int64_t)(r < a_valid ? r : a_valid - 1) * a.lda + k0;
-  };
-  auto b_row = [&](int r, int k0) {
-    int64_t src;
-    if (EPI == EPI_SWIGLU_FWD) {
-      // tile rows [0, BN/2) -> gate rows h0 + r; [BN/2, BN) -> up rows f + h0 + r - BN/2
-      const int hc0 = h0 + (r < BN / 2 ? r : r - BN / 2);
-      const int hc = hc0 < a.f ? hc0 : a.f - 1;
-      src = r < BN / 2 ? hc : a.f + hc;
-    } else {
-      src = nb * BN + (r < b_valid ? r : b_valid - 1);
-    }
-    return Borig + src * a.ldb + k0;
-  };
 
   // the operand origins are the same for the whole workgroup (the tile decode
   // reaches every lane through LDS): as scalars, each K step moves a scalar base
@@ -311,7 +342,11 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   Borig = uniform_ptr(Borig);
   DmaPlan<BM, BK, NW> pa;
   DmaPlan<BN, BK, NW> pb;
-  if (A_KC) pa.make_kc(wave, lane, a.lda, [&](int r) { return r < a_valid ? r : a_valid - 1; });
+  if (A_KC)
+    pa.make_kc(wave, lane, a.lda, [&](int r) {
+      const int rr = r < a_valid ? r : a_valid - 1;
+      return ga ? a.a_rows[r0 + mrow0 + rr] : rr;
+    });
   else pa.make_mn(wave, lane, a.lda, a_valid);
   if (B_IS_KC)
     pb.make_kc(wave, lane, a.ldb, [&](int r) {
@@ -328,11 +363,42 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   // the weight loads stream past the caches (non-temporal) and leave L2 to the
   // activation tiles, which every column tile re-reads.
   constexpr bool kStreamB = KIND == 0 && BM < 256;
+  // GB: the row indices of step k, in slot k & 1 of this wave's ring, and
+  // this lane's rows of the next step to be issued
+  auto ring = [&](int k) { return reinterpret_cast<const int32_t*>(smem + kRingOff + wave * 512 + (k & 1) * 256); };
+  int growq[GB ? DmaPlan<BN, BK, NW>::Q : 1];
+  auto prefetch_rows = [&](int k) {
+    if constexpr (GB) {
+      if (gb) {
+#pragma unroll
+        for (int q = 0; q < DmaPlan<BN, BK, NW>::Q; ++q) growq[q] = ring(k)[DmaPlan<BN, BK, NW>::mn_krow(wave, lane, q)];
+      }
+    }
+  };
+  auto dma_idx = [&](int k) {
+    if constexpr (GB) {
+      const uint32_t slot = lds0 + kRingOff + wave * 512 + (k & 1) * 256;
+      // rows past K repeat the last one; the shared group (rows in place)
+      // loads a placeholder, so every wave issues the same loads per step
+      if (gb) dma4s((uint32_t)min(k * kBK + lane, K - 1) * 4u, a.b_rows + r0, slot);
+      else dma4s(0u, Borig, slot);
+    }
+  };
+  // B's k-rows through the row map (GB); true when it issued them
+  auto dma_rows = [&](uint32_t sb) {
+    if constexpr (GB) {
+      if (gb) {
+        pb.template issue_mn_rows<kStreamB>(Borig, sb, wave, lane, growq, a.ldb, b_valid);
+        return true;
+      }
+    }
+    return false;
+  };
   auto dma_step = [&](int stage, int k0) {
     const uint32_t sa = lds0 + stage * kStage * 2;
     const uint32_t sb = sa + BM * kBK * 2;
     pa.template issue<false>(A_KC ? Aorig + k0 : Aorig + (int64_t)k0 * a.lda, sa, wave);
-    pb.template issue<kStreamB>(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
+    if (!dma_rows(sb)) pb.template issue<kStreamB>(B_IS_KC ? Borig + k0 : Borig + (int64_t)k0 * a.ldb, sb, wave);
   };
   // the partial last step as one more direct-load step with clamped addresses
   auto dma_tail = [&](int stage, int k0) {
@@ -340,6 +406,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     const uint32_t sb = sa + BM * kBK * 2;
     if (A_KC) pa.template issue_kc_tail<false>(Aorig + k0, sa, wave, lane, K - k0);
     else pa.template issue_mn_tail<false>(Aorig + (int64_t)k0 * a.lda, sa, wave, lane, K - k0, a.lda);
+    if (dma_rows(sb)) return;
     if (B_IS_KC) pb.template issue_kc_tail<kStreamB>(Borig + k0, sb, wave, lane, K - k0);
     else pb.template issue_mn_tail<kStreamB>(Borig + (int64_t)k0 * a.ldb, sb, wave, lane, K - k0, a.ldb);
   };
@@ -432,9 +499,16 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   // wave has read it, one barrier earlier than the publish of the next step;
   // 256x256 tiles (matrix-bound) save that barrier
   constexpr bool kEarly = BM < 256;
+  // GB: after a step's operand loads (whose rows were read from the ring a
+  // step earlier) the indices of step k+2 go into the slot those rows came
+  // from. Each publish then also waits for the indices loaded with the step
+  // before the one it publishes, so prefetch_rows(k + NS + 1) may follow
+  // publish(k + 1) in both pipelines (the one-step-in-flight wait of the
+  // 128x128 tiles leaves out only the last step's operand and index loads).
   auto issue_step = [&](int stage, int k) {
     if (k < nfull) dma_step(stage, k * kBK);
     else dma_tail(stage, k * kBK);
+    dma_idx(k + 2);
   };
   // Direct loads issued before publish(k): steps 0 .. min(NS-1, nk-1) for
   // k = 0 (prologue); steps 0 .. min(k+NS-2, nk-1) for k >= 1. The wait lets
@@ -464,9 +538,17 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       __syncthreads();
     }
   };
+  if (GB && nk > 0) {
+    dma_idx(0);
+    dma_idx(1);
+    wait_vm<0>();
+  }
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    if (s < nk) issue_step(s, s);
+    if (s < nk) {
+      prefetch_rows(s);
+      issue_step(s, s);
+    }
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
   // sub-steps 0 .. SUB-2 of the current step (no barrier inside)
@@ -485,6 +567,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   };
   auto main_loop = [&](auto fmv) {
     publish(0);
+    if (NS < nk) prefetch_rows(NS);
     read_frags(fmv, Set0(), 0, 0);
     for (int k = 0; k + 1 < nk; ++k) {
       const int stage = k % NS;
@@ -499,6 +582,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       // last sub-step of step k (set 1, SUB is even) overlaps the first reads of step k+1
       publish(k + 1);
       if (!kEarly && k + NS < nk) issue_step(stage, k + NS);
+      if (k + NS + 1 < nk) prefetch_rows(k + NS + 1);
       read_frags(fmv, Set0(), (k + 1) % NS, 0);
       mfmas(fmv, Set1());
       interleave(fmv);
@@ -656,7 +740,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   }
 }
 
-template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN = 2>
+template <int BM, int BN, int BK, int NS, int KIND, int B_KC, int EPI, int WGN = 2, int GB = 0>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   int64_t n;
   if (KIND == 0) {
@@ -669,7 +753,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     n = (int64_t)ng * ((BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN);
   }
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI, WGN>), dim3((unsigned)n), dim3(128 * WGN), 0,
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI, WGN, GB>), dim3((unsigned)n), dim3(128 * WGN), 0,
                      st, a);
   return hipGetLastError();
 }
@@ -677,13 +761,18 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 template <int BM, int BN, int BK, int NS, int WGN = 2>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // the direct loads address each operand as base + 32-bit per-lane byte offset
+  // (gathered rows: anywhere in the mapped operand)
   const int64_t lim = int64_t(1) << 32;
-  const int64_t b_rows = a.kind == 0 && a.b_kcontig ? (a.epi == EPI_SWIGLU_FWD ? 2 * (int64_t)a.f : a.N) : BK;
-  const int64_t a_rows = a.kind == 0 ? BM : BK;
-  if (a_rows * a.lda * 2 >= lim || b_rows * a.ldb * 2 >= lim) return hipErrorInvalidValue;
-  if (a.kind == 1)
-    return a.epi == EPI_STORE_F32 ? launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE_F32, WGN>(a, st)
-                                  : launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN>(a, st);
+  int64_t b_span = a.kind == 0 && a.b_kcontig ? (a.epi == EPI_SWIGLU_FWD ? 2 * (int64_t)a.f : a.N) : BK;
+  int64_t a_span = a.kind == 0 ? BM : BK;
+  if (a.kind == 0 && a.a_rows) a_span = a.src_rows;
+  if (a.kind == 1 && a.b_rows) b_span = a.src_rows;
+  if (a_span * a.lda * 2 >= lim || b_span * a.ldb * 2 >= lim) return hipErrorInvalidValue;
+  if (a.kind == 1) {
+    if (a.epi == EPI_STORE_F32) return launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE_F32, WGN>(a, st);
+    return a.b_rows ? launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN, 1>(a, st)
+                    : launch_t<BM, BN, BK, NS, 1, 0, EPI_STORE, WGN>(a, st);
+  }
   if (a.b_kcontig) {
     switch (a.epi) {
       case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE, WGN>(a, st);
@@ -736,12 +825,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const bool big = avg_rows >= 256 && (a.kind == 0 ? a.N >= 256 : (a.M >= 256 && a.N >= 256)) &&
                    big_tiles >= 256;
   // short contractions (one or two K steps per tile): two stages suffice
-  auto small_tiles = [&](const GemmArgs& s) {
-    if (s.kind == 1)
-      return s.epi == EPI_STORE_F32 ? launch_t<128, 128, 32, 2, 1, 0, EPI_STORE_F32>(s, st)
-                                    : launch_t<128, 128, 32, 2, 1, 0, EPI_STORE>(s, st);
-    return launch_tiles<128, 128, 64, 2>(s, st);
-  };
+  auto small_tiles = [&](const GemmArgs& s) { return s.kind == 1 ? launch_tiles<128, 128, 32, 2>(s, st) : launch_tiles<128, 128, 64, 2>(s, st); };
   if (!big) return small_tiles(a);
   // Groups capped at 512 rows or fewer (expert capacity): the host knows only
   // the cap, and the realised groups range from full (expert choice, balanced

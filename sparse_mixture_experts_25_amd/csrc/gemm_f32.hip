@@ -67,7 +67,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       const int k = k0 + kk;
       float v = 0.0f;
       if (KIND == 0) {
-        if (r < rows - mrow0 && k < K) v = Ab[(r0 + mrow0 + r) * a.lda + k];
+        if (r < rows - mrow0 && k < K) {
+          const int64_t row = r0 + mrow0 + r;
+          v = Ab[(sh || !a.a_rows ? row : (int64_t)a.a_rows[row]) * a.lda + k];
+        }
       } else {
         const int m = mb * BM + r;
         if (m < a.M && k < K) v = Ab[(r0 + k) * a.lda + m];
@@ -98,7 +101,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
         }
       } else {
         const int n = nb * BN + c;
-        if (n < a.N && k < K) v = Bb[(r0 + k) * a.ldb + n];
+        if (n < a.N && k < K) {
+          const int64_t row = r0 + k;
+          v = Bb[(sh || !a.b_rows ? row : (int64_t)a.b_rows[row]) * a.ldb + n];
+        }
       }
       Bs[kk][c] = v;
     }

@@ -123,6 +123,11 @@ struct GemmArgs {
   // 0 all groups; 1 only groups with at least split_rows rows (the extra dense
   // group counts shared_rows); 2 only groups with fewer
   int split_part; int split_rows;
+  // Row maps of the routed groups (nullable; the shared group reads its rows
+  // in place). ragged-M: row r of A is row a_rows[r] of A (the rows are
+  // gathered as they are loaded, so no permuted copy is needed); ragged-K:
+  // k-row r of B is row b_rows[r] of B. src_rows: rows of the mapped operand.
+  const int32_t* a_rows; const int32_t* b_rows; int64_t src_rows;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // order[0..E(+1)): the groups with rows sorted by row count, largest first

@@ -87,9 +87,9 @@ def host64(t) -> np.ndarray:
     return O.f64(t)
 
 
-def run_forward(c, inp_dev: dict, backward: bool = True):
+def run_forward(c, inp_dev: dict, backward: bool = True, rows_in_place: bool = False):
     cfg = cfg_of(c)
-    buf = M.LayerBuffers.allocate(cfg, backward=backward)
+    buf = M.LayerBuffers.allocate(cfg, backward=backward, rows_in_place=rows_in_place)
     M.forward(buf, inp_dev, aux=True)
     return buf
 
