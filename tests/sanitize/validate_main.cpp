@@ -83,6 +83,8 @@ int main() {
            MOE_OK);
     EXPECT(moe_expert_ffn(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                           nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
+    EXPECT(moe_expert_ffn_rows(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
     const int cb = moe_combine(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     EXPECT(cb != MOE_OK || (st == MOE_OK && c.num_tokens == 0));
     EXPECT(moe_aux_loss(&c, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
@@ -96,6 +98,11 @@ int main() {
     EXPECT(moe_dispatch(&c, A, Ai, Ai, Ai, Ai, Ai, A, A, ws ? ws - 1 : 0, nullptr) != MOE_OK || ws == 0);
     EXPECT(moe_dispatch(&c, MIS, Ai, Ai, Ai, Ai, Ai, MIS, A, ws, nullptr) != MOE_OK || c.routing != 0);
     EXPECT(moe_aux_loss(&c, Af, Ai, Af, nullptr, ws, nullptr) != MOE_OK);
+    // the rows-in-place matmuls: a short workspace, or no row map with tokens, is refused
+    EXPECT(moe_expert_ffn_rows(&c, A, Ai, Ai, A, A, nullptr, nullptr, A, A, A, nullptr, nullptr, nullptr, A,
+                               ws ? ws - 1 : 0, nullptr) != MOE_OK || ws == 0);
+    EXPECT(moe_expert_ffn_rows(&c, A, nullptr, Ai, A, A, nullptr, nullptr, A, A, A, nullptr, nullptr, nullptr, A, ws,
+                               nullptr) != MOE_OK || c.num_tokens == 0);
     moe_saved sv = {};
     moe_weights w = {};
     moe_grads g = {};
