@@ -288,8 +288,9 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* exp
  * x[row_token[r]] (row_token [R] as written by moe_dispatch or moe_route_ec,
  * device memory); everything else, outputs included, is as in moe_expert_ffn,
  * and the results are bitwise the same. x [T,d] serves both the routed rows
- * and the shared expert. Needs T*d*sizeof(act) < 4 GiB (MOE_ERR_HIP
- * otherwise). Needs the workspace. */
+ * and the shared expert. x must be under 4 GiB (T*d*sizeof(act) < 2^32,
+ * MOE_ERR_UNSUPPORTED otherwise, as for moe_backward without x_perm): its rows
+ * are addressed with 32-bit offsets. Needs the workspace. */
 int moe_expert_ffn_rows(const moe_config* cfg, const void* x, const int32_t* row_token,
                         const int32_t* expert_offsets, const void* w1, const void* w2,
                         const void* ws1, const void* ws2, void* act_saved, void* h_saved,

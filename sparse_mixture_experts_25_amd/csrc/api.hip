@@ -159,6 +159,12 @@ struct StageTimer {
   }
 };
 
+// Routed rows read in place through row_token are addressed anywhere in x with
+// 32-bit per-lane byte offsets: x must stay under 4 GiB.
+bool rows_in_place_fit(const moe_config* c) {
+  return (uint64_t)c->num_tokens * (uint64_t)c->d_model * (uint64_t)elem_bytes(c) < (uint64_t(1) << 32);
+}
+
 int gemm(const moe_config* c, moe::GemmArgs a, hipStream_t st, const char* stage) {
   StageTimer pt(stage, st);
   hipError_t e = c->dtype == MOE_DT_BF16 ? moe::launch_gemm_bf16(a, st) : moe::launch_gemm_f32(a, st);
@@ -310,6 +316,7 @@ int expert_ffn(const moe_config* c, const void* x_perm, const int32_t* row_token
   // ReLU: the pre-activations are optional (the backward takes the sign of h)
   const bool need_act = c->act == MOE_ACT_SWIGLU;
   const bool rows_in_place = x_perm == nullptr;
+  if (rows_in_place && !rows_in_place_fit(c)) return MOE_ERR_UNSUPPORTED;
   if (!expert_offsets || !w1 || !w2 ||
       (!empty && ((rows_in_place ? (!x || !row_token) : false) || (need_act && !act_saved) || !h_saved || !y_perm)))
     return MOE_ERR_INVALID_ARG;
@@ -455,6 +462,7 @@ int moe_backward(const moe_config* c, const void* dy, const moe_saved* sv, const
                  !g->dx))
     return MOE_ERR_INVALID_ARG;
   if (!w->w_router || !w->w1 || !w->w2 || !g->dw_router || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
+  if (!empty && !sv->x_perm && !rows_in_place_fit(c)) return MOE_ERR_UNSUPPORTED;
   if (sh && (!w->ws1 || !w->ws2 || !g->dws1 || !g->dws2 ||
              (!empty && ((!relu && !sv->act_shared) || !sv->h_shared))))
     return MOE_ERR_INVALID_ARG;

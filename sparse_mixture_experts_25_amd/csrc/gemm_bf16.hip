@@ -487,7 +487,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
 #pragma unroll
       for (int r = 0; r < RD; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, RD > 0 ? (MF + RD - 1) / RD : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (MF + RD - 1) / (RD > 0 ? RD : 1), 0);
       }
     }
   };

@@ -211,6 +211,32 @@ def test_plan_rejects_expert_matrices_past_32bit_offsets(d, f, act, dtype, ok):
             M.MOE_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("T,ok", [(262143, True), (262144, False)])
+def test_rows_in_place_refuses_inputs_past_4gib(T, ok):
+    """Without x_perm the matmuls address the routed rows anywhere in x with
+    32-bit per-lane byte offsets: host validation refuses T*d*2 >= 4 GiB
+    (d = 8192, bf16) for moe_expert_ffn_rows and for moe_backward without
+    x_perm, before any launch; the same config is valid with the permuted copy."""
+    L = M.lib()
+    cfg = M.make_config(T, 8192, 64, 4, 1, act="relu", dtype="bf16")
+    info = M.moe_plan_info()
+    assert L.moe_plan(ctypes.byref(cfg), ctypes.byref(info)) == M.MOE_OK
+    if ok:
+        return
+    c = ctypes.byref(cfg)
+    assert L.moe_expert_ffn_rows(c, A, A, A, A, A, N, N, N, A, A, N, N, N, A, 1 << 40, N) == M.MOE_ERR_UNSUPPORTED
+    s, w, g = M.moe_saved(), M.moe_weights(), M.moe_grads()
+    for n in ("x", "probs", "topk_idx", "topk_w", "slot", "expert_counts", "expert_offsets", "h_saved", "y_perm",
+              "row_token"):
+        setattr(s, n, A)
+    for n in ("w_router", "w1", "w2"):
+        setattr(w, n, A)
+    for n in ("dx", "dw_router", "dw1", "dw2"):
+        setattr(g, n, A)
+    assert L.moe_backward(c, A, ctypes.byref(s), ctypes.byref(w), ctypes.byref(g), A, 1 << 40, N) == \
+        M.MOE_ERR_UNSUPPORTED
+
+
 def test_dispatch_noalloc_validates_before_launch():
     """The allocation-free dispatch refuses bad arguments, and configs whose
     per-chunk histograms (ceil(T*k / 1024) * E int32) exceed its fixed 2^20-entry
