@@ -497,12 +497,15 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
 
 // Narrow d_model: the scalar-operand logits kernel (more waves in flight; x
 // rows are short). Wide d_model: the register-tiled kernel, which streams x
-// once per 32 or 64 tokens and reuses each LDS read over 4-8 tokens.
+// once per 32 or 64 tokens and reuses each LDS read over 4-8 tokens. With 129
+// to 256 experts, 8 tokens per thread (158 VGPRs, 84 KB of LDS: one
+// workgroup and one wave per SIMD) left the multiply-adds waiting on LDS; 4
+// tokens per thread (two workgroups per CU) is faster at any batch size.
 template <typename TX>
 hipError_t launch_router_wide(const RouterArgs& a, hipStream_t st) {
   const bool big = (a.T + 63) / 64 >= 256;  // 64-token tiles still cover every CU
   if (a.E <= 128) return big ? launch_router_tile<TX, 8, 1>(a, st) : launch_router_tile<TX, 4, 1>(a, st);
-  if (a.E <= 256) return big ? launch_router_tile<TX, 8, 2>(a, st) : launch_router_tile<TX, 4, 2>(a, st);
+  if (a.E <= 256) return launch_router_tile<TX, 4, 2>(a, st);
   return launch_router_tile<TX, 4, 4>(a, st);
 }
 
