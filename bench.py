@@ -190,6 +190,28 @@ def stage_work(c, rows, ne_experts, permuted_copy=False):
     }
 
 
+def check_determinism(buf, inp, step, c):
+    """After the timed region: the step twice more from the same state (the
+    selection bias restored between the two), with the routing tables, the
+    output, the input gradient and every weight gradient compared bit for bit."""
+    import torch
+    keys = ["expert_counts", "expert_offsets", "slot", "topk_w", "y", "dx", "dw_router", "dw1", "dw2", "dws1", "dws2"]
+    if c.routing != "expert_choice":
+        keys.append("topk_idx")  # written by token-choice routing only
+    keys = [k for k in keys if k in buf.t]
+    bias0 = inp["sel_bias"].clone() if "sel_bias" in inp else None
+    step()
+    torch.cuda.synchronize()
+    first = {k: buf.t[k].clone() for k in keys}
+    if bias0 is not None:
+        inp["sel_bias"].copy_(bias0)
+    step()
+    torch.cuda.synchronize()
+    differ = [k for k in keys if not torch.equal(first[k].view(torch.uint8), buf.t[k].view(torch.uint8))]
+    del first
+    return {"runs": 2, "compared": keys, "bitwise_equal": not differ, "differ": differ}
+
+
 def cpu_baseline_sized(c, inp, target_s=20.0, probe_tokens=16):
     """Oracle timing on a sample of about `target_s` seconds: start from
     `probe_tokens` tokens and grow the sample (at most 8x per try, scaled by the
@@ -428,6 +450,7 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     nd = M.lib().moe_profile_disarm()
+    determinism = check_determinism(buf, inp, step, c)
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
     per_step = sorted(a.elapsed_time(b) for a, b in sev)
@@ -474,6 +497,7 @@ def main():
                    "permuted_copy": bool(args.x_perm)},
         "roofline": roof,
         "zero_fill": zero_fill,
+        "determinism": determinism,
         # every stage against its own roofline, from the per-stage pre-pass times
         "stage_roofline": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv
                                for kk, vv in stage_roofline(k, work[k], v, c.dtype).items() if kk != "peak"}
