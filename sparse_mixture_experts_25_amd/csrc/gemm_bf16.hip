@@ -613,13 +613,49 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   __syncthreads();
 
   // ---- epilogue: stage the fp32 tile in LDS one half (the rows of one wave
-  // row) at a time, then write 16-byte row vectors
+  // row) at a time, then write 16-byte row vectors. The epilogues that read
+  // other tensors (the saved pre-activations, the rows the unpermute adds)
+  // issue every load of a half before staging it, so that their latency
+  // overlaps the staging once instead of stalling each output vector.
   float* Cs = reinterpret_cast<float*>(smem);
   uint16_t* C = reinterpret_cast<uint16_t*>(sh ? a.C_sh : a.C);
   uint16_t* C2 = reinterpret_cast<uint16_t*>(sh ? a.C2_sh : a.C2);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(sh ? a.X_sh : a.X);
+  constexpr int U = HM * BN / 8;  // 16-byte output vectors of a half
+  constexpr int IT = U / NTH;     // per thread
+  static_assert(U % NTH == 0, "every thread writes the same number of vectors");
+  constexpr bool kReadsX = EPI == EPI_RELU_BWD || EPI == EPI_SWIGLU_BWD || EPI == EPI_UNPERMUTE;
+  constexpr int kUK = 2;  // unpermute: kept rows per token loaded ahead (it runs for k <= 2)
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    const int mbase = half * HM;  // tile row of Cs row 0
+    // the output vector of iteration it: tile row m, column col, and whether it is stored
+    auto unit = [&](int it, int& m, int& n, int& col) {
+      const int u = tid + it * NTH;
+      m = mbase + u / (BN / 8);
+      n = (u % (BN / 8)) * 8;
+      col = nb * BN + n;
+      return m < rows - mrow0 && col < a.N;
+    };
+    // (the unpermute loads only its slots here; dy comes with the rows below)
+    u128 xa[kReadsX && EPI != EPI_UNPERMUTE ? IT : 1], xb[EPI == EPI_SWIGLU_BWD ? IT : 1];
+    int sl[EPI == EPI_UNPERMUTE ? IT * kUK : 1];
+    if constexpr (kReadsX) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        int m, n, col;
+        const bool ok = unit(it, m, n, col);
+        // vectors that are not stored read the tile's first one (always inside the tensors)
+        const int64_t row = r0 + mrow0 + (ok ? m : 0);
+        const int cc = ok ? col : 0;
+        if constexpr (EPI != EPI_UNPERMUTE) xa[it] = ld128(X + row * a.ldx + cc);
+        if constexpr (EPI == EPI_SWIGLU_BWD) xb[it] = ld128(X + row * a.ldx + a.f + cc);
+        if constexpr (EPI == EPI_UNPERMUTE) {
+#pragma unroll
+          for (int r = 0; r < kUK; ++r) sl[it * kUK + r] = (ok && r < a.slot_k) ? a.slot[row * a.slot_k + r] : -1;
+        }
+      }
+    }
     // the blocks (of every wave, or of wave row `half`) whose rows fall in this half
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -634,11 +670,9 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         }
     }
     __syncthreads();
-    const int mbase = half * HM;  // tile row of Cs row 0
     if (EPI == EPI_SWIGLU_FWD) {
       // columns [0, BN/2) hold gate, [BN/2, BN) up, for h columns h0 + j
-      constexpr int U = HM * (BN / 2) / 8;
-      for (int u = tid; u < U; u += NTH) {
+      for (int u = tid; u < U / 2; u += NTH) {
         const int ml = u / (BN / 16);
         const int j = (u % (BN / 16)) * 8;
         const int m = mbase + ml;
@@ -657,82 +691,113 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         st128(C2 + row * a.ldc2 + hc, Elem<uint16_t>::pack(hv));
       }
     } else {
-      constexpr int U = HM * BN / 8;
-      for (int u = tid; u < U; u += NTH) {
-        const int ml = u / (BN / 8);
-        const int n = (u % (BN / 8)) * 8;
-        const int m = mbase + ml;
-        float v[8];
+      // unpermute: the kept rows' vectors (and the shared expert's) of CH
+      // iterations, loaded together once the slots are in (CH bounds the
+      // registers they hold)
+      constexpr int CH = (EPI == EPI_UNPERMUTE && IT > 4) ? 2 : IT;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = Cs[ml * CP + n + e];
-        if (KIND == 1) {
-          const int mm = mb * BM + m, nn = nb * BN + n;
-          if (mm >= a.M || nn >= a.N) continue;
-          if (EPI == EPI_STORE_F32) {
-            float* Cf = reinterpret_cast<float*>(a.C) + (int64_t)g * a.strideC + (int64_t)mm * a.ldc + nn;
-            reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
-            reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      for (int c0 = 0; c0 < IT; c0 += CH) {
+        u128 xc[EPI == EPI_UNPERMUTE ? CH : 1], yr[EPI == EPI_UNPERMUTE ? CH * kUK : 1], ys[EPI == EPI_UNPERMUTE ? CH : 1];
+        if constexpr (EPI == EPI_UNPERMUTE) {
+          const uint16_t* Yp = reinterpret_cast<const uint16_t*>(a.Y);
+          const uint16_t* Ys = reinterpret_cast<const uint16_t*>(a.Y_sh);
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            int m, n, col;
+            if (!unit(c0 + c, m, n, col)) continue;
+            xc[c] = ld128(X + (r0 + mrow0 + m) * a.ldx + col);
+#pragma unroll
+            for (int r = 0; r < kUK; ++r) {
+              const int q = sl[(c0 + c) * kUK + r];
+              if (q >= 0) yr[c * kUK + r] = ld128(Yp + (int64_t)q * a.N + col);
+            }
+            if (Ys) ys[c] = ld128(Ys + (r0 + mrow0 + m) * a.N + col);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int it = c0 + c;
+          int m, n, col;
+          const bool ok = unit(it, m, n, col);
+          const int ml = m - mbase;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = Cs[ml * CP + n + e];
+          if (KIND == 1) {
+            const int mm = mb * BM + m, nn = nb * BN + n;
+            if (mm >= a.M || nn >= a.N) continue;
+            if (EPI == EPI_STORE_F32) {
+              float* Cf = reinterpret_cast<float*>(a.C) + (int64_t)g * a.strideC + (int64_t)mm * a.ldc + nn;
+              reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
+              reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
+              continue;
+            }
+            // weight gradients are written once and not read in this pass
+            uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
+            st128_nt(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
             continue;
           }
-          // weight gradients are written once and not read in this pass
-          uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
-          st128_nt(Cg + (int64_t)mm * a.ldc + nn, Elem<uint16_t>::pack(v));
-          continue;
-        }
-        const int col = nb * BN + n;
-        if (m >= rows - mrow0 || col >= a.N) continue;
-        const int64_t row = r0 + mrow0 + m;
-        if (EPI == EPI_STORE) {
-          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
-        } else if (EPI == EPI_STORE_F32) {
-          float* Cf = reinterpret_cast<float*>(sh ? a.C_sh : a.C) + row * a.ldc + col;
-          reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
-          reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
-        } else if (EPI == EPI_RELU_FWD) {
-          float h[8];
+          if (!ok) continue;
+          const int64_t row = r0 + mrow0 + m;
+          if (EPI == EPI_STORE) {
+            st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+          } else if (EPI == EPI_STORE_F32) {
+            float* Cf = reinterpret_cast<float*>(sh ? a.C_sh : a.C) + row * a.ldc + col;
+            reinterpret_cast<float4*>(Cf)[0] = make_float4(v[0], v[1], v[2], v[3]);
+            reinterpret_cast<float4*>(Cf)[1] = make_float4(v[4], v[5], v[6], v[7]);
+          } else if (EPI == EPI_RELU_FWD) {
+            float h[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = fmaxf(v[e], 0.0f);
-          if (C) st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));  // pre-activation only if asked for
-          st128(C2 + row * a.ldc2 + col, Elem<uint16_t>::pack(h));
-        } else if (EPI == EPI_RELU_BWD) {
-          float xs[8];
-          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), xs);
+            for (int e = 0; e < 8; ++e) h[e] = fmaxf(v[e], 0.0f);
+            if (C) st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));  // pre-activation only if asked for
+            st128(C2 + row * a.ldc2 + col, Elem<uint16_t>::pack(h));
+          } else if (EPI == EPI_RELU_BWD) {
+            float xs[8];
+            Elem<uint16_t>::unpack(xa[it], xs);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = xs[e] > 0.0f ? v[e] : 0.0f;
-          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
-        } else if (EPI == EPI_UNPERMUTE) {
-          // same order as the separate pass: dy, kept expert rows in r order,
-          // router term, shared expert
-          const uint16_t* Yp = reinterpret_cast<const uint16_t*>(a.Y);
-          float o[8], tmp[8];
-          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), o);
-          for (int r = 0; r < a.slot_k; ++r) {
-            const int sl = a.slot[row * a.slot_k + r];
-            if (sl < 0) continue;
-            Elem<uint16_t>::unpack(ld128(Yp + (int64_t)sl * a.N + col), tmp);
+            for (int e = 0; e < 8; ++e) v[e] = xs[e] > 0.0f ? v[e] : 0.0f;
+            st128(C + row * a.ldc + col, Elem<uint16_t>::pack(v));
+          } else if (EPI == EPI_UNPERMUTE) {
+            // same order as the separate pass: dy, kept expert rows in r order,
+            // router term, shared expert
+            float o[8], tmp[8];
+            Elem<uint16_t>::unpack(xc[c], o);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+            for (int r = 0; r < kUK; ++r) {
+              if (sl[it * kUK + r] < 0) continue;
+              Elem<uint16_t>::unpack(yr[c * kUK + r], tmp);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+            }
+            // rows past the ones loaded ahead (not used by the layer: k <= 2)
+            for (int r = kUK; r < a.slot_k; ++r) {
+              const int s2 = a.slot[row * a.slot_k + r];
+              if (s2 < 0) continue;
+              Elem<uint16_t>::unpack(ld128(reinterpret_cast<const uint16_t*>(a.Y) + (int64_t)s2 * a.N + col), tmp);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += v[e];
+            if (a.Y_sh) {
+              Elem<uint16_t>::unpack(ys[c], tmp);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] += tmp[e];
+            }
+            st128(C + row * a.ldc + col, Elem<uint16_t>::pack(o));
+          } else if (EPI == EPI_SWIGLU_BWD) {
+            float gs[8], us[8], dg[8], du[8];
+            Elem<uint16_t>::unpack(xa[it], gs);
+            Elem<uint16_t>::unpack(xb[it], us);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float s = 1.0f / (1.0f + __expf(-gs[e]));
+              du[e] = v[e] * gs[e] * s;
+              dg[e] = v[e] * us[e] * s * (1.0f + gs[e] * (1.0f - s));
+            }
+            st128(C + row * a.ldc + col, Elem<uint16_t>::pack(dg));
+            st128(C + row * a.ldc + a.f + col, Elem<uint16_t>::pack(du));
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += v[e];
-          if (a.Y_sh) {
-            Elem<uint16_t>::unpack(ld128(reinterpret_cast<const uint16_t*>(a.Y_sh) + row * a.N + col), tmp);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += tmp[e];
-          }
-          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(o));
-        } else if (EPI == EPI_SWIGLU_BWD) {
-          float gs[8], us[8], dg[8], du[8];
-          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + col), gs);
-          Elem<uint16_t>::unpack(ld128(X + row * a.ldx + a.f + col), us);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float s = 1.0f / (1.0f + __expf(-gs[e]));
-            du[e] = v[e] * gs[e] * s;
-            dg[e] = v[e] * us[e] * s * (1.0f + gs[e] * (1.0f - s));
-          }
-          st128(C + row * a.ldc + col, Elem<uint16_t>::pack(dg));
-          st128(C + row * a.ldc + a.f + col, Elem<uint16_t>::pack(du));
         }
       }
     }
