@@ -61,14 +61,14 @@ __device__ inline bool raster_tile(int64_t nrow, int64_t ncol, int GM, int64_t& 
 // Ragged-M tile placement. Wave 0 scans ceil(rows_g / BM) over the groups
 // (each lane owns a run of groups) to get the actual number of row tiles; the
 // workgroup id is then mapped XCD-aware over (actual row tiles) x ncol (see
-// raster_tile), and the owning lane resolves the row tile to (group, first row).
-// Everything goes through LDS to the whole workgroup. Returns false when this
-// workgroup has no tile.
+// raster_tile), and the lane owning that row tile resolves it to (group, first
+// row). One pass of wave 0, then one barrier: the result reaches the whole
+// workgroup through LDS (lds[0..4]). Returns false when this workgroup has no
+// tile.
 template <int BM>
 __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* lds, TileInfo& ti, int& col) {
   const int ngroups = a.E + (a.shared_rows > 0 ? 1 : 0);
   const int per = (ngroups + 63) / 64;
-  int64_t* lds64 = reinterpret_cast<int64_t*>(lds + 8);  // [0]: total row tiles
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int64_t local = 0;
@@ -84,30 +84,15 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
       const int64_t n = __shfl_up(incl, o, 64);
       if (lane >= o) incl += n;
     }
-    if (lane == 63) lds64[0] = incl;
-    if (lane == 0) lds[0] = -1;
-  }
-  __syncthreads();
-  const int64_t nrow = lds64[0];
-  int64_t row, c;
-  const bool have = raster_tile(nrow, ncol, GM, row, c);
-  if (have && threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int64_t local = 0;
-    for (int i = 0; i < per; ++i) {
-      const int g = lane * per + i;
-      if (g < ngroups) {
-        const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        if (group_in_part(a, rows)) local += (rows + BM - 1) / BM;
-      }
-    }
-    int64_t incl = local;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t n = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += n;
+    const int64_t nrow = __shfl(incl, 63, 64);  // row tiles of the launch
+    int64_t row, c;
+    const bool have = raster_tile(nrow, ncol, GM, row, c);
+    if (lane == 0) {
+      lds[0] = -1;  // replaced below by the owning lane (a later LDS write of this wave)
+      lds[4] = have ? (int)c : 0;
     }
     const int64_t excl = incl - local;
-    if (row >= excl && row < incl) {
+    if (have && row >= excl && row < incl) {
       int64_t accum = excl;
       for (int i = 0; i < per; ++i) {
         const int g = lane * per + i;
@@ -125,12 +110,12 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
     }
   }
   __syncthreads();
-  if (!have || lds[0] < 0) return false;
+  if (lds[0] < 0) return false;
   ti.g = lds[0];
   ti.r0 = lds[1];
   ti.rows = lds[2];
   ti.m0 = lds[3];
-  col = (int)c;
+  col = lds[4];
   return true;
 }
 
