@@ -692,12 +692,14 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
       }
     } else {
       // unpermute: the kept rows' vectors (and the shared expert's) of CH
-      // iterations, loaded together once the slots are in (CH bounds the
-      // registers they hold)
-      constexpr int CH = (EPI == EPI_UNPERMUTE && IT > 4) ? 2 : IT;
+      // iterations, loaded together once the slots are in. CH bounds the
+      // registers they hold while the other wave row's accumulators are still
+      // live (the first half of a 256x256 tile); in the second half every
+      // accumulator is in LDS and all of them go out at once.
+      const int CH = (EPI == EPI_UNPERMUTE && IT > 4 && half == 0) ? 2 : IT;
 #pragma unroll
       for (int c0 = 0; c0 < IT; c0 += CH) {
-        u128 xc[EPI == EPI_UNPERMUTE ? CH : 1], yr[EPI == EPI_UNPERMUTE ? CH * kUK : 1], ys[EPI == EPI_UNPERMUTE ? CH : 1];
+        u128 xc[EPI == EPI_UNPERMUTE ? IT : 1], yr[EPI == EPI_UNPERMUTE ? IT * kUK : 1], ys[EPI == EPI_UNPERMUTE ? IT : 1];
         if constexpr (EPI == EPI_UNPERMUTE) {
           const uint16_t* Yp = reinterpret_cast<const uint16_t*>(a.Y);
           const uint16_t* Ys = reinterpret_cast<const uint16_t*>(a.Y_sh);
