@@ -614,9 +614,10 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
 
   // ---- epilogue: stage the fp32 tile in LDS one half (the rows of one wave
   // row) at a time, then write 16-byte row vectors. The epilogues that read
-  // other tensors (the saved pre-activations, the rows the unpermute adds)
-  // issue every load of a half before staging it, so that their latency
-  // overlaps the staging once instead of stalling each output vector.
+  // other tensors issue those loads for a whole half together instead of one
+  // output vector at a time: the saved pre-activations before the half is
+  // staged (their latency overlaps the staging), the unpermute's slots before
+  // it and the rows they name after it, in batches.
   float* Cs = reinterpret_cast<float*>(smem);
   uint16_t* C = reinterpret_cast<uint16_t*>(sh ? a.C_sh : a.C);
   uint16_t* C2 = reinterpret_cast<uint16_t*>(sh ? a.C2_sh : a.C2);
