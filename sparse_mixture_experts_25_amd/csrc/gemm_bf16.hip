@@ -794,7 +794,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
             Elem<uint16_t>::unpack(xb[it], us);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float s = 1.0f / (1.0f + __expf(-gs[e]));
+              const float s = act_sigmoid(gs[e]);
               du[e] = v[e] * gs[e] * s;
               dg[e] = v[e] * us[e] * s * (1.0f + gs[e] * (1.0f - s));
             }

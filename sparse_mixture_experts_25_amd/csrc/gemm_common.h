@@ -142,7 +142,14 @@ __device__ inline bool k_tile(int64_t t, int nM, int nN, int& mb, int& nb) {
   return true;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// The expert activation's logistic function. The activation is not a rounding
+// point of the layer (its value is rounded to bf16 when stored, or feeds the
+// fp32 derivative), so 1 / (1 + e^-z) takes the hardware reciprocal (1 ulp)
+// instead of the correctly rounded division sequence, which made the SwiGLU
+// epilogues ALU-bound. (The router's sigmoid gate decides routing and keeps its
+// exact contract in gate_math.h.)
+__device__ __forceinline__ float act_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z * act_sigmoid(z); }
 
 // Epilogue for 8 consecutive output columns of one row (bf16 outputs), or
 // fewer for fp32 (V = 4). `v` holds the fp32 accumulators. For SwiGLU forward,
