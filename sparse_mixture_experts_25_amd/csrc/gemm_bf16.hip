@@ -612,6 +612,46 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   }
   __syncthreads();
 
+  if constexpr (EPI == EPI_STORE && (BM == 256 || KIND == 0)) {
+    // A plain bf16 output: the tile is staged in LDS as the bf16 values it is
+    // stored as (the same rounding of the same accumulators), all of it in one
+    // pass: half the LDS bytes of fp32 staging, and one barrier instead of three.
+    // (Not for the 128x128 weight-gradient tiles: there the conversions of
+    // every accumulator at once cost the registers of their fourth workgroup
+    // per CU.)
+    constexpr int CB = BN + 8;  // padded bf16 row
+    static_assert(BM * CB * 2 <= kLds, "the bf16 tile fits the LDS of the main loop");
+    uint16_t* Cb = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = brow(i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int n = wn * WN + j * 32 + (lane & 31);
+          Cb[m * CB + n] = f2bf(acc[i][j][e]);
+        }
+    __syncthreads();
+    uint16_t* C = reinterpret_cast<uint16_t*>(sh ? a.C_sh : a.C);
+    for (int u = tid; u < BM * BN / 8; u += NTH) {
+      const int m = u / (BN / 8), n = (u % (BN / 8)) * 8;
+      const u128 v = ld128(Cb + m * CB + n);
+      if (KIND == 1) {
+        // weight gradients are written once and not read in this pass
+        const int mm = mb * BM + m, nn = nb * BN + n;
+        if (mm >= a.M || nn >= a.N) continue;
+        uint16_t* Cg = sh ? C : C + (int64_t)g * a.strideC;
+        st128_nt(Cg + (int64_t)mm * a.ldc + nn, v);
+      } else {
+        const int col = nb * BN + n;
+        if (m >= rows - mrow0 || col >= a.N) continue;
+        st128(C + (r0 + mrow0 + m) * a.ldc + col, v);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: stage the fp32 tile in LDS one half (the rows of one wave
   // row) at a time, then write 16-byte row vectors. The epilogues that read
   // other tensors issue those loads for a whole half together instead of one
