@@ -275,7 +275,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     // placed on the XCDs by k_tile; 256x256 tiles (compute-bound) keep the row
     // block fastest.
     const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
-    const int64_t per_g = (BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN;
+    const uint32_t per_g = (uint32_t)((BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN);
     const int rank = (int)(blockIdx.x / per_g);
     if (BM < 256) {
       if (!k_tile(blockIdx.x % per_g, nM, nN, mb, nb)) return;

@@ -42,17 +42,20 @@ constexpr int kXcds = 8;
 __host__ __device__ inline int64_t raster_grid(int64_t nrow, int64_t ncol) {
   return (nrow * ncol + kXcds - 1) / kXcds * kXcds;
 }
-__device__ inline bool raster_tile(int64_t nrow, int64_t ncol, int GM, int64_t& row, int64_t& col) {
-  const int64_t total = nrow * ncol;
-  const int64_t per = raster_grid(nrow, ncol) / kXcds;
-  const int64_t bid = blockIdx.x;
+__device__ inline bool raster_tile(int64_t nrow64, int64_t ncol64, int GM, int64_t& row, int64_t& col) {
+  // nrow * ncol is at most the 1-D grid size (below 2^32), so every quotient
+  // here is 32-bit (64-bit divisions are long instruction sequences)
+  const uint32_t nrow = (uint32_t)nrow64, ncol = (uint32_t)ncol64;
+  const uint32_t total = nrow * ncol;
+  const uint32_t per = (total + kXcds - 1) / kXcds;
+  const uint32_t bid = blockIdx.x;
   if (bid / kXcds >= per) return false;
-  const int64_t L = (bid % kXcds) * per + bid / kXcds;
+  const uint32_t L = (bid % kXcds) * per + bid / kXcds;
   if (L >= total) return false;
-  const int64_t gsize = (int64_t)GM * ncol;
-  const int64_t first = (L / gsize) * GM;
-  const int64_t gm = (nrow - first) < GM ? (nrow - first) : GM;
-  const int64_t local = L % gsize;
+  const uint32_t gsize = (uint32_t)GM * ncol;
+  const uint32_t first = (L / gsize) * (uint32_t)GM;
+  const uint32_t gm = (nrow - first) < (uint32_t)GM ? (nrow - first) : (uint32_t)GM;
+  const uint32_t local = L % gsize;
   row = first + local % gm;
   col = local / gm;
   return true;
@@ -69,41 +72,69 @@ template <int BM>
 __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* lds, TileInfo& ti, int& col) {
   const int ngroups = a.E + (a.shared_rows > 0 ? 1 : 0);
   const int per = (ngroups + 63) / 64;
+  // the first kKeep groups of each lane keep their first row and row count in
+  // registers, so the owning lane resolves its tile without loading them again
+  constexpr int kKeep = 8;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int64_t local = 0;
-    for (int i = 0; i < per; ++i) {
+    auto group_rows = [&](int g) { return (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows; };
+    auto group_tiles = [&](int rows) { return group_in_part(a, rows) ? (rows + BM - 1) / BM : 0; };
+    int off[kKeep], rws[kKeep];
+    int local = 0;  // row tiles of this lane's groups (every count is below 2^31)
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i) {
       const int g = lane * per + i;
-      if (g < ngroups) {
-        const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        if (group_in_part(a, rows)) local += (rows + BM - 1) / BM;
+      off[i] = 0;
+      rws[i] = 0;
+      if (i < per && g < ngroups) {
+        off[i] = (g < a.E) ? a.offsets[g] : 0;
+        rws[i] = group_rows(g);
+        local += group_tiles(rws[i]);
       }
     }
-    int64_t incl = local;
+    for (int i = kKeep; i < per; ++i) {  // more than 64 * kKeep groups
+      const int g = lane * per + i;
+      if (g < ngroups) local += group_tiles(group_rows(g));
+    }
+    int incl = local;
     for (int o = 1; o < 64; o <<= 1) {
-      const int64_t n = __shfl_up(incl, o, 64);
+      const int n = __shfl_up(incl, o, 64);
       if (lane >= o) incl += n;
     }
-    const int64_t nrow = __shfl(incl, 63, 64);  // row tiles of the launch
+    const int nrow = __shfl(incl, 63, 64);  // row tiles of the launch
     int64_t row, c;
     const bool have = raster_tile(nrow, ncol, GM, row, c);
     if (lane == 0) {
       lds[0] = -1;  // replaced below by the owning lane (a later LDS write of this wave)
       lds[4] = have ? (int)c : 0;
     }
-    const int64_t excl = incl - local;
+    const int excl = incl - local;
     if (have && row >= excl && row < incl) {
-      int64_t accum = excl;
-      for (int i = 0; i < per; ++i) {
+      const int r = (int)row;
+      int accum = excl;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i) {
+        const int nt = group_tiles(rws[i]);
+        if (!found && i < per && r < accum + nt) {
+          lds[0] = lane * per + i;
+          lds[1] = off[i];
+          lds[2] = rws[i];
+          lds[3] = (r - accum) * BM;
+          found = true;
+        }
+        accum += nt;
+      }
+      for (int i = kKeep; i < per && !found; ++i) {
         const int g = lane * per + i;
-        const int rows = (g < a.E) ? (a.offsets[g + 1] - a.offsets[g]) : a.shared_rows;
-        const int64_t nt = group_in_part(a, rows) ? (rows + BM - 1) / BM : 0;
-        if (row < accum + nt) {
+        const int rows = group_rows(g);
+        const int nt = group_tiles(rows);
+        if (r < accum + nt) {
           lds[0] = g;
           lds[1] = (g < a.E) ? a.offsets[g] : 0;
           lds[2] = rows;
-          lds[3] = (int)(row - accum) * BM;
-          break;
+          lds[3] = (r - accum) * BM;
+          found = true;
         }
         accum += nt;
       }
@@ -128,16 +159,18 @@ __device__ bool locate_ragged_m(const GemmArgs& a, int64_t ncol, int GM, int* ld
 __host__ __device__ inline int64_t ragged_k_per_group(int nM, int nN) {
   return (((int64_t)nM * nN + 7) / 8) * 8;
 }
-__device__ inline bool k_tile(int64_t t, int nM, int nN, int& mb, int& nb) {
-  const int64_t per = ((int64_t)nM * nN + 7) / 8;
-  const int64_t L = (t % 8) * per + t / 8;
-  if (L >= (int64_t)nM * nN) return false;
+__device__ inline bool k_tile(int64_t t64, int nM, int nN, int& mb, int& nb) {
+  // 32-bit quotients: a group has far fewer than 2^31 tiles
+  const uint32_t t = (uint32_t)t64, tiles = (uint32_t)nM * (uint32_t)nN;
+  const uint32_t per = (tiles + 7) / 8;
+  const uint32_t L = (t % 8) * per + t / 8;
+  if (L >= tiles) return false;
   if (nM <= nN) {
-    nb = (int)(L / nM);
-    mb = (int)(L % nM);
+    nb = (int)(L / (uint32_t)nM);
+    mb = (int)(L % (uint32_t)nM);
   } else {
-    mb = (int)(L / nN);
-    nb = (int)(L % nN);
+    mb = (int)(L / (uint32_t)nN);
+    nb = (int)(L % (uint32_t)nN);
   }
   return true;
 }
