@@ -397,8 +397,8 @@ __global__ __launch_bounds__(256) void router_tile_kernel(
     const float* Xs = Ws + KC * EP;
     if (ch + 1 < nch) fetch((ch + 1) * KC);  // in flight during this chunk's multiply-adds
     const int kc = min(KC, d - ch * KC);
-    for (int j = 0; j < kc; ++j) {
-      float xs[TPT], ws[EPT];
+    // this thread's x values and router weights of step j of the chunk
+    auto read_step = [&](int j, float* xs, float* ws) {
 #pragma unroll
       for (int i = 0; i < TPT / 4; ++i) {
         const float4 v = *reinterpret_cast<const float4*>(Xs + j * XP + tg * TPT + 4 * i);
@@ -409,10 +409,32 @@ __global__ __launch_bounds__(256) void router_tile_kernel(
         const float4 v = *reinterpret_cast<const float4*>(Ws + j * EP + 4 * (eg + EG * h));
         ws[4 * h] = v.x; ws[4 * h + 1] = v.y; ws[4 * h + 2] = v.z; ws[4 * h + 3] = v.w;
       }
+    };
+    auto fma_step = [&](const float* xs, const float* ws) {
 #pragma unroll
       for (int i = 0; i < TPT; ++i)
 #pragma unroll
         for (int c = 0; c < EPT; ++c) acc[i][c] = __builtin_fmaf(xs[i], ws[c], acc[i][c]);
+    };
+    if (kc == KC) {
+      // A full chunk: the LDS reads of step j + 1 are issued before the
+      // multiply-adds of step j, which hide their latency. Each logit still
+      // takes its multiply-adds in ascending j.
+      float xs[2][TPT], ws[2][EPT];
+      read_step(0, xs[0], ws[0]);
+#pragma unroll
+      for (int j = 0; j + 1 < KC; ++j) {
+        read_step(j + 1, xs[(j + 1) & 1], ws[(j + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the multiply-adds
+        fma_step(xs[j & 1], ws[j & 1]);
+      }
+      fma_step(xs[(KC - 1) & 1], ws[(KC - 1) & 1]);
+    } else {
+      for (int j = 0; j < kc; ++j) {
+        float xs[TPT], ws[EPT];
+        read_step(j, xs, ws);
+        fma_step(xs, ws);
+      }
     }
     if (ch + 1 < nch) stash(smem + ((ch + 1) & 1) * STAGE);
     __syncthreads();
