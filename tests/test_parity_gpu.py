@@ -202,6 +202,63 @@ def test_backward_parity_end_to_end(name):
         assert relerr(host64(t["dws2"]), bw["dws2"]) <= tol
 
 
+@pytest.mark.parametrize("name", ["deepseek_v3", "deep_groups_swiglu", "swiglu_f32_shared"])
+def test_swiglu_saturated_activations(name):
+    """SwiGLU with the up-projection weights scaled by 64 (exact in bf16 and
+    fp32), so that many gate pre-activations lie beyond |z| = 88, where e^-z
+    overflows fp32: the logistic function of the SwiGLU epilogues then takes
+    the reciprocal of +inf (0) for z << 0 and of 1 for z >> 0. The forward
+    against the oracle (fp64 logistic); the backward stage-isolated (from the
+    oracle's saved pre-activations, so the activation derivative is compared
+    on identical inputs) and, for bf16, also end to end. (End to end in fp32
+    the pre-activations differ from the oracle's by fp32 accumulation of
+    64x larger terms, which the derivative amplifies near z = 0 beyond the
+    1e-5 bound, as a ReLU mask near zero is ambiguous.)"""
+    c = CASES[name]
+    print(f"[swiglu saturated] {name}", flush=True)
+    inp = make_inputs(c, seed=3)
+    inp["w1"] = inp["w1"] * 64
+    if c.shared:
+        inp["ws1"] = inp["ws1"] * 64
+    dev = to_dev(inp)
+    buf = run_forward(c, dev, backward=True)
+    torch.cuda.synchronize()
+    spec = O.Spec.of(c)
+    inp64 = oracle_inputs(inp)
+    fw = O.forward(spec, inp64)
+    bw = O.backward(spec, inp64, fw, host64(inp["dy"]))
+    n = int(fw["n_rows"])
+    _check_routing(buf, fw, n)
+    gate = fw["act"][:n, :c.f]
+    sat = np.abs(gate) > 88.0
+    print(f"  gate pre-activations beyond |z| = 88: {int(sat.sum())} of {gate.size}", flush=True)
+    assert sat.sum() > 0.05 * gate.size and (gate < -88).any() and (gate > 88).any()
+    t = buf.t
+    tol = tol_for(c)
+    assert relerr(host64(t["act_saved"][:n]), fw["act"]) <= tol
+    assert relerr(host64(t["h_saved"][:n]), fw["h"]) <= tol
+    assert relerr(host64(t["y_perm"][:n]), fw["y_perm"]) <= tol
+    assert relerr_sum(host64(t["y"]), fw["y"], y_terms_abs(fw, host64(inp["x"]))) <= tol
+    if c.shared:
+        assert relerr(host64(t["y_shared"]), fw["y_shared"]) <= tol
+
+    def check_backward():
+        assert relerr_sum(host64(t["dx"]), bw["dx"], dx_terms_abs(fw, bw, host64(inp["dy"]))) <= tol
+        assert relerr(host64(t["dw1"]), bw["dw1"]) <= tol
+        assert relerr(host64(t["dw2"]), bw["dw2"]) <= tol
+        if c.shared:
+            assert relerr(host64(t["dws1"]), bw["dws1"]) <= tol
+            assert relerr(host64(t["dws2"]), bw["dws2"]) <= tol
+
+    if c.dtype == "bf16":
+        run_backward(buf, dev)
+        torch.cuda.synchronize()
+        check_backward()
+    run_backward(buf, dev, saved=gpu_saved_from_oracle(c, fw, buf.info))
+    torch.cuda.synchronize()
+    check_backward()
+
+
 @pytest.mark.parametrize("name", ["finegrained_top8_s", "ec_relu_bf16", "noisy_relu_bf16", "sqrt_softplus_bf16"])
 def test_determinism_bitwise(name):
     # two full forward+backward runs give identical bytes in every output (no atomics anywhere)
