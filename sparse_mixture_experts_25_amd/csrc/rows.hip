@@ -411,9 +411,16 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
   }
   const float c = alpha * (float)E / (float)T;
   const float invTk = 1.0f / ((float)T * (float)k);
+  // f_j = counts_j / (T k), rounded once (no contraction) and used both in
+  // sum_j f_j p_j and in each f_j - that sum, so that with one expert (p = 1)
+  // the softmax term is exactly zero
+  auto frac = [&](int j) {
+#pragma clang fp contract(off)
+    return (float)counts[j] * invTk;
+  };
   float fp = 0.0f;
   if (alpha != 0.0f) {
-    for (int j = lane; j < E; j += 64) fp += (float)counts[j] * invTk * p[j];
+    for (int j = lane; j < E; j += 64) fp += frac(j) * p[j];
     fp = wave_sum(fp);
   }
   for (int j = lane; j < E; j += 64) {
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
       } else if (rsel >= 0) {
         v = wt[rsel] * (gt[rsel] - wdg);
       }
-      if (alpha != 0.0f) v += c * pj * ((float)counts[j] * invTk - fp);
+      if (alpha != 0.0f) v += c * pj * (frac(j) - fp);
     } else {
       // derivative of the gate written with its value s: sigmoid s (1 - s);
       // sqrt(softplus) sigmoid(h) / (2 s) = (1 - e^(-s^2)) / (2 s), 0 at s = 0
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
         const float ds = renorm ? (gt[rsel] - wdg) / ssum : gt[rsel];
         v = ds * gd;
       }
-      if (alpha != 0.0f) v += c * (float)counts[j] * invTk * gd;
+      if (alpha != 0.0f) v += c * frac(j) * gd;
     }
     if (dlogits) dlogits[(int64_t)t * E + j] = v;
     if (gx) {

@@ -65,6 +65,15 @@ CASES["ec_f32_shared"] = LayerConfig("ec_f32_shared", T=130, d=72, f=48, E=6, k=
                                      cf=1.5, shared=1, **_EC)
 CASES["ec_all_tokens"] = LayerConfig("ec_all_tokens", T=96, d=64, f=64, E=4, k=4, act="relu", cf=6.0, **_EC)
 
+# degenerate routings: one expert (a dense FFN through the MoE path; every
+# probability is 1), the same with capacity 0.5 (the second half of the tokens
+# dropped, in token order), and every token to all four experts (k = E)
+CASES["single_expert_relu"] = LayerConfig("single_expert_relu", T=300, d=136, f=200, E=1, k=1, act="relu", cf=0.0,
+                                          alpha=0.01)
+CASES["single_expert_capped"] = LayerConfig("single_expert_capped", T=300, d=136, f=200, E=1, k=1, act="relu",
+                                            cf=0.5, alpha=0.01)
+CASES["all_experts_swiglu"] = LayerConfig("all_experts_swiglu", T=257, d=136, f=72, E=4, k=4, renorm=True,
+                                          act="swiglu", cf=0.0, alpha=0.01, shared=1)
 
 def _forward_both(c, seed=0):
     inp = make_inputs(c, seed=seed)
