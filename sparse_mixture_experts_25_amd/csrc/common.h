@@ -179,6 +179,4 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
 }  // namespace moe
