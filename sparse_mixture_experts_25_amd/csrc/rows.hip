@@ -106,25 +106,46 @@ __global__ __launch_bounds__(256) void combine_narrow_kernel(const TX* __restric
   const TX* rows[KM];
 #pragma unroll
   for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? y_perm + (int64_t)c.s[r] * d : xr;
-  for (int v = lane; v < d / V; v += 64) {
-    u128 raw[KM];
+  // Two vectors per lane and iteration (2 KB of each row per wave), all their
+  // loads issued before either is summed; a missing shared expert loads x again.
+  const TX* ysr = y_shared ? y_shared + (int64_t)t * d : xr;
+  struct In { u128 raw[KM], xv, sv; };
+  auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    in.xv = ld128(xr + v * V);
+    in.sv = ld128(ysr + v * V);
+  };
+  auto finish = [&](int v, const In& in) {
     float acc[V], tmp[V];
-    Elem<TX>::unpack(ld128(xr + v * V), acc);
+    Elem<TX>::unpack(in.xv, acc);
 #pragma unroll
     for (int r = 0; r < KM; ++r) {
       if (c.s[r] < 0) continue;
-      Elem<TX>::unpack(raw[r], tmp);
+      Elem<TX>::unpack(in.raw[r], tmp);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] = __builtin_fmaf(c.w[r], tmp[e], acc[e]);
     }
     if (y_shared) {
-      Elem<TX>::unpack(ld128(y_shared + (int64_t)t * d + v * V), tmp);
+      Elem<TX>::unpack(in.sv, tmp);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
     st128(y + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  };
+  const int nv = d / V;
+  int v = lane;
+  for (; v + 64 < nv; v += 128) {
+    In a, b;
+    load(v, a);
+    load(v + 64, b);
+    finish(v, a);
+    finish(v + 64, b);
+  }
+  if (v < nv) {
+    In a;
+    load(v, a);
+    finish(v, a);
   }
 }
 
@@ -152,16 +173,22 @@ __global__ __launch_bounds__(256) void combine_bwd_narrow_kernel(const TX* __res
   float dot[KM];
 #pragma unroll
   for (int r = 0; r < KM; ++r) dot[r] = 0.0f;
-  for (int v = lane; v < d / V; v += 64) {
-    u128 raw[KM];
+  // Two vectors per lane and iteration (2 KB of each row per wave), all their
+  // loads issued before either is used; each lane's dot products still add its
+  // vectors in ascending order.
+  struct In { u128 raw[KM], gv; };
+  auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    in.gv = ld128(gr + v * V);
+  };
+  auto finish = [&](int v, const In& in) {
     float g[V], yv[V], o[V];
-    Elem<TX>::unpack(ld128(gr + v * V), g);
+    Elem<TX>::unpack(in.gv, g);
 #pragma unroll
     for (int r = 0; r < KM; ++r) {
       if (c.s[r] < 0) continue;
-      Elem<TX>::unpack(raw[r], yv);
+      Elem<TX>::unpack(in.raw[r], yv);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         dot[r] = __builtin_fmaf(g[e], yv[e], dot[r]);
@@ -169,6 +196,20 @@ __global__ __launch_bounds__(256) void combine_bwd_narrow_kernel(const TX* __res
       }
       st128(dO + (int64_t)c.s[r] * d + v * V, Elem<TX>::pack(o));
     }
+  };
+  const int nv = d / V;
+  int v = lane;
+  for (; v + 64 < nv; v += 128) {
+    In a, b;
+    load(v, a);
+    load(v + 64, b);
+    finish(v, a);
+    finish(v + 64, b);
+  }
+  if (v < nv) {
+    In a;
+    load(v, a);
+    finish(v, a);
   }
 #pragma unroll
   for (int r = 0; r < KM; ++r) {
@@ -202,18 +243,24 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
   // order dy, kept rows by ascending r, router term, shared expert
   const float* prr = dx_router ? dx_router + (int64_t)t * d : nullptr;
   const TX* psh = dx_shared ? dx_shared + (int64_t)t * d : gr;
-  for (int v = lane; v < d / V; v += 64) {
-    u128 raw[KM];
+  // Two vectors per lane and iteration (2 KB of each row per wave), all their
+  // loads issued before either is summed.
+  struct In { u128 raw[KM], rdy, rsh; float4 q[V / 4]; };
+  auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) raw[r] = ld128(rows[r] + v * V);
-    const u128 rdy = ld128(gr + v * V);
-    const u128 rsh = ld128(psh + v * V);
-    float4 q[V / 4];
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    in.rdy = ld128(gr + v * V);
+    in.rsh = ld128(psh + v * V);
 #pragma unroll
     for (int e = 0; e < V / 4; ++e)
-      q[e] = prr ? reinterpret_cast<const float4*>(prr + v * V)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      in.q[e] = prr ? reinterpret_cast<const float4*>(prr + v * V)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto finish = [&](int v, const In& in) {
+    const u128* raw = in.raw;
+    const u128 rsh = in.rsh;
+    const float4* q = in.q;
     float acc[V], tmp[V];
-    Elem<TX>::unpack(rdy, acc);
+    Elem<TX>::unpack(in.rdy, acc);
 #pragma unroll
     for (int r = 0; r < KM; ++r) {
       if (c.s[r] < 0) continue;
@@ -233,6 +280,20 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
     st128(dx + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+  };
+  const int nv = d / V;
+  int v = lane;
+  for (; v + 64 < nv; v += 128) {
+    In a, b;
+    load(v, a);
+    load(v + 64, b);
+    finish(v, a);
+    finish(v + 64, b);
+  }
+  if (v < nv) {
+    In a;
+    load(v, a);
+    finish(v, a);
   }
 }
 
