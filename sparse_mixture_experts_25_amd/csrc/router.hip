@@ -137,12 +137,14 @@ struct X8<float> {
   }
 };
 
-// Four router weights of one expert (wave-uniform address, read into SGPRs).
-struct W4 {
-  float v[4];
+// Eight router weights of one expert (wave-uniform address, read into SGPRs).
+struct W8 {
+  float v[8];
   __device__ void load(const float* p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 };
 
@@ -180,43 +182,42 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TX* __restrict
 #pragma unroll
   for (int i = 0; i < kEW; ++i) acc[i] = 0.0f;
 
-  // Blocks of 4 along d with ping-pong weight buffers (4 experts x 4 values =
-  // 16 SGPRs each). Scalar loads may complete out of order, so the only wait
+  // Blocks of 8 along d with ping-pong weight buffers (4 experts x 8 values =
+  // 32 SGPRs each). Scalar loads may complete out of order, so the only wait
   // for them is lgkmcnt(0), placed by the compiler before the first use: each
   // block starts with its first multiply-adds (waiting for its own weights,
   // issued one block earlier) and only then issues the next block's scalar
-  // loads, which stay in flight during the rest of the block. x is read 8
-  // values at a time, one 16-byte vector load per lane, two loads ahead.
-  const int nb = d / 4;
-  W4 w0[kEW], w1[kEW];
-  auto loadw = [&](W4* w, int blk) {
+  // loads, which stay in flight during the other 28 multiply-adds of the block
+  // (4-deep blocks left 12, and the waves waited on the weights). x is read 8
+  // values at a time, one 16-byte vector load per lane, two blocks ahead.
+  const int nb = d / 8;
+  W8 w0[kEW], w1[kEW];
+  auto loadw = [&](W8* w, int blk) {
 #pragma unroll
-    for (int i = 0; i < kEW; ++i) w[i].load(wbase + wstep[i] + 4 * blk);
+    for (int i = 0; i < kEW; ++i) w[i].load(wbase + wstep[i] + 8 * blk);
   };
-  auto fma_j = [&](float xv, const W4* wc, int j) {
+  auto fma_j = [&](float xv, const W8* wc, int j) {
 #pragma unroll
     for (int i = 0; i < kEW; ++i) acc[i] = __builtin_fmaf(xv, wc[i].v[j], acc[i]);
   };
-  auto block = [&](const X8<TX>& xc, int half, const W4* wc, W4* wn, int nxt) {
-    fma_j(xc.get(4 * half), wc, 0);
+  auto block = [&](const X8<TX>& xc, const W8* wc, W8* wn, int nxt) {
+    fma_j(xc.get(0), wc, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (nxt < nb) loadw(wn, nxt);
 #pragma unroll
-    for (int j = 1; j < 4; ++j) fma_j(xc.get(4 * half + j), wc, j);
+    for (int j = 1; j < 8; ++j) fma_j(xc.get(j), wc, j);
   };
   X8<TX> x0, x1;
   x0.load(xr);
-  if (nb > 2) x1.load(xr + 8);
+  if (nb > 1) x1.load(xr + 8);
   loadw(w0, 0);
-  // nb is even (d is a multiple of 8): 8 values of x per pair of blocks
-  for (int b = 0; b < nb; b += 4) {
-    block(x0, 0, w0, w1, b + 1);
-    block(x0, 1, w1, w0, b + 2);
-    if (b + 4 < nb) x0.load(xr + 4 * (b + 4));
-    if (b + 2 >= nb) break;
-    block(x1, 0, w0, w1, b + 3);
-    block(x1, 1, w1, w0, b + 4);
-    if (b + 6 < nb) x1.load(xr + 4 * (b + 6));
+  // d is a multiple of 8: one block per 8 values of x, in ascending order
+  for (int b = 0; b < nb; b += 2) {
+    block(x0, w0, w1, b + 1);
+    if (b + 2 < nb) x0.load(xr + 8 * (b + 2));
+    if (b + 1 >= nb) break;
+    block(x1, w1, w0, b + 2);
+    if (b + 3 < nb) x1.load(xr + 8 * (b + 3));
   }
   if (t < T) {
     float* o = out + (int64_t)t * E + e0;
