@@ -10,9 +10,10 @@
 // The assignments (t, r) are taken in token-major order a = t*k + r and cut
 // into chunks of kChunk. Four launches:
 //   1. per-chunk expert histogram (LDS integer atomics: exact counts)
-//   2. one workgroup: per-expert totals over chunks, kept rows, and the
-//      exclusive scan over experts (offsets)
-//   3. per chunk: the chunk's base per expert (sum over earlier chunks), the
+//   2. one workgroup: per-expert totals over chunks, kept rows, the exclusive
+//      scan over experts (offsets), and each chunk's base per expert (the
+//      exclusive prefix over chunks, written over the histograms)
+//   3. per chunk: the chunk's base per expert, the
 //      stable rank of each assignment among equal experts inside the
 //      chunk (wave ballots on the expert id bits give the set of lanes with the
 //      same expert; the rank is the popcount of that set below the lane),
@@ -44,52 +45,69 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan of up to 1024 values held 4 per thread by 256 threads.
-__device__ int block_exclusive_scan4(int v[4], int* lds_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int s0 = v[0], s1 = s0 + v[1], s2 = s1 + v[2], s3 = s2 + v[3];
-  int incl = s3;
+// One workgroup: per-expert totals over the chunk histograms, the kept rows and
+// the exclusive scan over experts (offsets); the chunk histograms are replaced
+// by their exclusive prefix over chunks (the assignments to each expert in
+// earlier chunks: the base that assign_kernel reads). The chunks are split into
+// G = 1024 / E contiguous ranges, one per group of E threads, so each expert's
+// sum is G short chains of independent loads and a G-term combine rather than
+// one chain over every chunk. Integer sums: the order does not change them.
+constexpr int kScanThreads = 1024;  // >= E (moe_plan accepts at most 512 experts)
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks,
+                                                            int E, int C, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int part[kScanThreads];  // [G][E]: group sums, then their exclusive prefix over groups
+  __shared__ int wsum[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  const int G = kScanThreads / E;
+  const int g = tid / E, e = tid % E;
+  const bool act = g < G;
+  const int cpg = (nchunks + G - 1) / G;
+  const int c0 = g * cpg, c1 = min(nchunks, c0 + cpg);
+  int s = 0;
+  if (act)
+    for (int c = c0; c < c1; ++c) s += chunk_counts[(int64_t)c * E + e];
+  if (act) part[g * E + e] = s;
+  __syncthreads();
+  int total_e = 0;  // held by the threads of group 0 (tid = e)
+  if (act && g == 0) {
+    for (int h = 0; h < G; ++h) {
+      const int v = part[h * E + e];
+      part[h * E + e] = total_e;
+      total_e += v;
+    }
+  }
+  __syncthreads();
+  if (act) {
+    int run = part[g * E + e];
+    for (int c = c0; c < c1; ++c) {
+      const int64_t i = (int64_t)c * E + e;
+      const int v = chunk_counts[i];
+      chunk_counts[i] = run;
+      run += v;
+    }
+  }
+  // kept rows of expert tid and their exclusive scan over the experts
+  int kept = 0;
+  if (tid < E) {
+    counts[tid] = total_e;
+    kept = (C < 0) ? total_e : min(total_e, C);
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = kept;
   for (int o = 1; o < 64; o <<= 1) {
     const int n = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += n;
   }
-  if (lane == 63) lds_waves[wave] = incl;
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int wbase = 0, total = 0;
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) wbase += lds_waves[w];
-    total += lds_waves[w];
+  int wbase = 0, tot = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    if (w < wave) wbase += wsum[w];
+    tot += wsum[w];
   }
-  const int base = wbase + incl - s3;
-  v[3] = base + s2;
-  v[2] = base + s1;
-  v[1] = base + s0;
-  v[0] = base;
-  return total;
-}
-
-__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks,
-                                                   int E, int C, int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets) {
-  __shared__ int waves[4];
-  int kept[4];
-  for (int i = 0; i < 4; ++i) {
-    const int e = threadIdx.x * 4 + i;
-    kept[i] = 0;
-    if (e < E) {
-      int run = 0;
-#pragma unroll 8
-      for (int c = 0; c < nchunks; ++c) run += chunk_counts[(int64_t)c * E + e];
-      counts[e] = run;
-      kept[i] = (C < 0) ? run : min(run, C);
-    }
-  }
-  const int total = block_exclusive_scan4(kept, waves);
-  for (int i = 0; i < 4; ++i) {
-    const int e = threadIdx.x * 4 + i;
-    if (e < E) offsets[e] = kept[i];
-  }
-  if (threadIdx.x == 0) offsets[E] = total;
+  if (tid < E) offsets[tid] = wbase + incl - kept;
+  if (tid == 0) offsets[E] = tot;
 }
 
 __global__ __launch_bounds__(256) void assign_kernel(const int32_t* __restrict__ idx, int total, int k,
@@ -112,9 +130,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const int32_t* __restrict__
   __syncthreads();
   // bases: base(w, e) = (assignments to e in earlier chunks) + (in earlier waves of this chunk)
   for (int e = threadIdx.x; e < E; e += 256) {
-    int b = 0;  // assignments to e in earlier chunks
-#pragma unroll 8
-    for (int c = 0; c < (int)blockIdx.x; ++c) b += chunk_counts[(int64_t)c * E + e];
+    int b = chunk_counts[(int64_t)blockIdx.x * E + e];  // assignments to e in earlier chunks (scan_kernel)
     for (int w = 0; w < 4; ++w) {
       const int c = run[w * E + e];
       run[w * E + e] = b;
@@ -225,8 +241,9 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   if (nch > 0)
     hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), a.E * sizeof(int32_t), st, a.topk_idx, total,
                        a.E, a.ws_chunk);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, a.ws_chunk, nch, a.E, a.capacity, a.counts,
-                     a.offsets);
+  if (a.E > kScanThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, a.ws_chunk, nch, a.E, a.capacity,
+                     a.counts, a.offsets);
   if (nch == 0) return hipGetLastError();  // no tokens: counts and offsets are all zero
   hipLaunchKernelGGL(assign_kernel, dim3(nch), dim3(256), 4 * a.E * sizeof(int32_t), st, a.topk_idx,
                      total, a.k, a.E, a.capacity, a.ws_chunk, a.offsets, a.slot, a.row_token);
