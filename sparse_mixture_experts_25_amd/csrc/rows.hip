@@ -444,7 +444,9 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
     return;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  // wave-uniform: the token's k indices, weights and gate gradients, and the
+  // probabilities they select, are scalar loads
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
   if (t >= T) return;
   const float* p = probs + (int64_t)t * E;
   // without topk_idx (expert-choice tables) column r is expert r and k = E
