@@ -26,6 +26,15 @@ __device__ __forceinline__ u128 ld128(const void* p) {
   r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   return r;
 }
+// 16-byte load with the non-temporal (streaming) cache policy, for gathered rows
+// that are read once.
+__device__ __forceinline__ u128 ld128_nt(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  u128 r;
+  r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  return r;
+}
 __device__ __forceinline__ void st128(void* p, const u128& r) {
   *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }

@@ -108,11 +108,12 @@ __global__ __launch_bounds__(256) void combine_narrow_kernel(const TX* __restric
   for (int r = 0; r < KM; ++r) rows[r] = c.s[r] >= 0 ? y_perm + (int64_t)c.s[r] * d : xr;
   // Two vectors per lane and iteration (2 KB of each row per wave), all their
   // loads issued before either is summed; a missing shared expert loads x again.
+  // The gathered rows (read once) and y (written once) bypass the caches.
   const TX* ysr = y_shared ? y_shared + (int64_t)t * d : xr;
   struct In { u128 raw[KM], xv, sv; };
   auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128_nt(rows[r] + v * V);
     in.xv = ld128(xr + v * V);
     in.sv = ld128(ysr + v * V);
   };
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void combine_narrow_kernel(const TX* __restric
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
-    st128(y + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+    st128_nt(y + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
   };
   const int nv = d / V;
   int v = lane;
@@ -175,11 +176,11 @@ __global__ __launch_bounds__(256) void combine_bwd_narrow_kernel(const TX* __res
   for (int r = 0; r < KM; ++r) dot[r] = 0.0f;
   // Two vectors per lane and iteration (2 KB of each row per wave), all their
   // loads issued before either is used; each lane's dot products still add its
-  // vectors in ascending order.
+  // vectors in ascending order. The gathered rows (read once) bypass the caches.
   struct In { u128 raw[KM], gv; };
   auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128_nt(rows[r] + v * V);
     in.gv = ld128(gr + v * V);
   };
   auto finish = [&](int v, const In& in) {
@@ -244,11 +245,12 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
   const float* prr = dx_router ? dx_router + (int64_t)t * d : nullptr;
   const TX* psh = dx_shared ? dx_shared + (int64_t)t * d : gr;
   // Two vectors per lane and iteration (2 KB of each row per wave), all their
-  // loads issued before either is summed.
+  // loads issued before either is summed. The gathered rows (read once) and dx
+  // (written once) bypass the caches.
   struct In { u128 raw[KM], rdy, rsh; float4 q[V / 4]; };
   auto load = [&](int v, In& in) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r) in.raw[r] = ld128(rows[r] + v * V);
+    for (int r = 0; r < KM; ++r) in.raw[r] = ld128_nt(rows[r] + v * V);
     in.rdy = ld128(gr + v * V);
     in.rsh = ld128(psh + v * V);
 #pragma unroll
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += tmp[e];
     }
-    st128(dx + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
+    st128_nt(dx + (int64_t)t * d + v * V, Elem<TX>::pack(acc));
   };
   const int nv = d / V;
   int v = lane;
