@@ -245,17 +245,24 @@ __global__ __launch_bounds__(256) void unpermute_bwd_narrow_kernel(const TX* __r
   const float* prr = dx_router ? dx_router + (int64_t)t * d : nullptr;
   const TX* psh = dx_shared ? dx_shared + (int64_t)t * d : gr;
   // Two vectors per lane and iteration (2 KB of each row per wave), all their
-  // loads issued before either is summed. The gathered rows (read once) and dx
+  // loads issued before either is summed. Every input row (read once) and dx
   // (written once) bypass the caches.
   struct In { u128 raw[KM], rdy, rsh; float4 q[V / 4]; };
   auto load = [&](int v, In& in) {
 #pragma unroll
     for (int r = 0; r < KM; ++r) in.raw[r] = ld128_nt(rows[r] + v * V);
-    in.rdy = ld128(gr + v * V);
-    in.rsh = ld128(psh + v * V);
+    in.rdy = ld128_nt(gr + v * V);
+    in.rsh = ld128_nt(psh + v * V);
 #pragma unroll
-    for (int e = 0; e < V / 4; ++e)
-      in.q[e] = prr ? reinterpret_cast<const float4*>(prr + v * V)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < V / 4; ++e) {
+      if (prr) {
+        const u128 w = ld128_nt(prr + v * V + 4 * e);
+        in.q[e] = make_float4(__uint_as_float(w.w[0]), __uint_as_float(w.w[1]), __uint_as_float(w.w[2]),
+                              __uint_as_float(w.w[3]));
+      } else {
+        in.q[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
   };
   auto finish = [&](int v, const In& in) {
     const u128* raw = in.raw;
