@@ -415,6 +415,57 @@ def test_caller_supplied_routing():
     np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), row_token[:n])
 
 
+# Capacity and positions alone (moe_dispatch on a caller-supplied routing),
+# against the oracle bit for bit, over the shapes the histogram scan splits
+# differently: one expert (1024 thread groups), expert counts that leave threads
+# of the scan workgroup idle (3, 300), the largest supported count (512), one
+# chunk of 1024 assignments exactly, one assignment past it, and 157 chunks that
+# the thread groups do not divide evenly; capped and dropless. The routing is
+# skewed so that some experts get no rows and capped ones overflow.
+DISPATCH_SHAPES = [
+    # (name, T, k, E, capacity factor)
+    ("one_expert", 3000, 1, 1, 0.0),
+    ("three_capped", 5000, 2, 3, 1.0),
+    ("e300_dropless", 4000, 8, 300, 0.0),
+    ("e512_capped_157_chunks", 20000, 8, 512, 1.25),
+    ("one_chunk_capped", 100, 4, 64, 2.0),
+    ("exactly_one_chunk", 128, 8, 128, 0.0),
+    ("one_past_a_chunk", 1025, 1, 128, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,T,k,E,cf", DISPATCH_SHAPES, ids=[s[0] for s in DISPATCH_SHAPES])
+def test_dispatch_shapes(name, T, k, E, cf):
+    print(f"[dispatch] {name} T={T} k={k} E={E} cf={cf}", flush=True)
+    g = torch.Generator().manual_seed(E * 7919 + T)
+    skew = -0.5 * torch.log(torch.arange(1, E + 1, dtype=torch.float32))
+    idx = torch.topk(torch.rand(T, E, generator=g) * 4.0 + skew, k, dim=1).indices.to(torch.int32)
+    cfg = M.make_config(T, 64, 64, E, k, cf=cf)
+    buf = M.LayerBuffers.allocate(cfg, backward=False)
+    t = buf.t
+    C = O.capacity(T, E, cf)
+    counts, offsets, slot, row_token = O.positions(idx.numpy(), E, C)
+    n = int(offsets[-1])
+    dev_idx = idx.cuda()
+    x = torch.zeros((T, 64), dtype=torch.bfloat16, device="cuda")
+    for noalloc in (False, True):
+        for key in ("slot", "row_token", "expert_counts", "expert_offsets"):
+            t[key].fill_(-7)
+        if noalloc:
+            M.moe_dispatch_noalloc(cfg, x, dev_idx, t["expert_counts"], t["expert_offsets"], t["slot"],
+                                   t["row_token"], None)
+        else:
+            M.moe_dispatch(cfg, x, dev_idx, t["expert_counts"], t["expert_offsets"], t["slot"], t["row_token"],
+                           None, t["ws"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(t["expert_counts"].cpu().numpy(), counts)
+        np.testing.assert_array_equal(t["expert_offsets"].cpu().numpy(), offsets)
+        np.testing.assert_array_equal(t["slot"].cpu().numpy(), slot)
+        np.testing.assert_array_equal(t["row_token"][:n].cpu().numpy(), row_token[:n])
+    print(f"  kept {n} of {T * k}, experts without rows {int((counts == 0).sum())}", flush=True)
+    assert (counts == 0).any() or E <= 3
+
+
 def test_expert_choice_ties_and_empty():
     # a zero router gives every token the same probabilities: each expert takes
     # the first C tokens; an empty batch writes zero counts and offsets
