@@ -29,15 +29,19 @@ __host__ __device__ inline bool group_in_part(const GemmArgs& a, int rows) {
   return a.split_part == 0 || (a.split_part == 1 ? rows >= a.split_rows : rows < a.split_rows);
 }
 
-// XCD-aware grouped rasterization. The dispatcher hands workgroup ids to the
-// 8 XCDs round-robin (id % 8), and each XCD has its own L2. Workgroup ids are
-// remapped so that each XCD owns one contiguous range of logical tiles, and the
-// logical order walks groups of GM row tiles across all column tiles, so that
-// concurrently running workgroups on one XCD share operand tiles in its L2.
-// The grid is 1-D with at least nrow * ncol rounded up to a multiple of 8
-// workgroups (a ragged-M launch sizes it from an upper bound on nrow). The map
-// bid -> L is a bijection from the workgroups with bid / 8 < per onto
-// [0, 8 * per); every other workgroup has no tile.
+// Grouped rasterization. Logical tile L = workgroup id, walked in bands of GM
+// row tiles across all column tiles (row fastest inside a band). The
+// dispatcher hands workgroup ids to the 8 XCDs round-robin (id % 8), and each
+// XCD has its own L2: inside a band of 8 rows, XCD x then takes row tile x
+// against every column tile, so a row tile's activation panel is read into one
+// L2, and the weight panel of a column tile, which all eight XCDs read at about
+// the same time, comes to the seven later ones from the last-level cache.
+// (Remapping ids so that each XCD owned a contiguous range of logical tiles, 8
+// row tiles x 4 column tiles at a time, was 1-2 % slower per step on the
+// DeepSeek-V3-, GShard- and Switch-shaped layers, and even on the fine-grained
+// one.) The grid is 1-D with at least nrow * ncol rounded up to a multiple of
+// 8 workgroups (a ragged-M launch sizes it from an upper bound on nrow); the
+// workgroups past nrow * ncol have no tile.
 constexpr int kXcds = 8;
 __host__ __device__ inline int64_t raster_grid(int64_t nrow, int64_t ncol) {
   return (nrow * ncol + kXcds - 1) / kXcds * kXcds;
@@ -47,10 +51,7 @@ __device__ inline bool raster_tile(int64_t nrow64, int64_t ncol64, int GM, int64
   // here is 32-bit (64-bit divisions are long instruction sequences)
   const uint32_t nrow = (uint32_t)nrow64, ncol = (uint32_t)ncol64;
   const uint32_t total = nrow * ncol;
-  const uint32_t per = (total + kXcds - 1) / kXcds;
-  const uint32_t bid = blockIdx.x;
-  if (bid / kXcds >= per) return false;
-  const uint32_t L = (bid % kXcds) * per + bid / kXcds;
+  const uint32_t L = blockIdx.x;
   if (L >= total) return false;
   const uint32_t gsize = (uint32_t)GM * ncol;
   const uint32_t first = (L / gsize) * (uint32_t)GM;
@@ -63,7 +64,7 @@ __device__ inline bool raster_tile(int64_t nrow64, int64_t ncol64, int GM, int64
 
 // Ragged-M tile placement. Wave 0 scans ceil(rows_g / BM) over the groups
 // (each lane owns a run of groups) to get the actual number of row tiles; the
-// workgroup id is then mapped XCD-aware over (actual row tiles) x ncol (see
+// workgroup id is then placed over (actual row tiles) x ncol in bands (see
 // raster_tile), and the lane owning that row tile resolves it to (group, first
 // row). One pass of wave 0, then one barrier: the result reaches the whole
 // workgroup through LDS (lds[0..4]). Returns false when this workgroup has no
