@@ -267,7 +267,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
     const int ncols = (EPI == EPI_SWIGLU_FWD) ? a.f : a.N;
     const int bn = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;
     TileInfo ti;
-    if (!locate_ragged_m<BM>(a, (ncols + bn - 1) / bn, 8, info, ti, nb)) return;
+    if (!locate_ragged_m<BM>(a, (ncols + bn - 1) / bn, 4, info, ti, nb)) return;
     g = ti.g; r0 = ti.r0; rows = ti.rows; mrow0 = ti.m0;
   } else {
     // groups in the given order (largest first), tiles of one group

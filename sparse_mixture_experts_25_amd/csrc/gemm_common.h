@@ -32,14 +32,15 @@ __host__ __device__ inline bool group_in_part(const GemmArgs& a, int rows) {
 // Grouped rasterization. Logical tile L = workgroup id, walked in bands of GM
 // row tiles across all column tiles (row fastest inside a band). The
 // dispatcher hands workgroup ids to the 8 XCDs round-robin (id % 8), and each
-// XCD has its own L2: inside a band of 8 rows, XCD x then takes row tile x
-// against every column tile, so a row tile's activation panel is read into one
-// L2, and the weight panel of a column tile, which all eight XCDs read at about
-// the same time, comes to the seven later ones from the last-level cache.
-// (Remapping ids so that each XCD owned a contiguous range of logical tiles, 8
-// row tiles x 4 column tiles at a time, was 1-2 % slower per step on the
-// DeepSeek-V3-, GShard- and Switch-shaped layers, and even on the fine-grained
-// one.) The grid is 1-D with at least nrow * ncol rounded up to a multiple of
+// XCD has its own L2: with GM = 4 (the row-ragged launches), XCDs x and x + 4
+// take row tile x of a band against alternate column tiles, so a row tile's
+// activation panel is read into two L2s, and the weight panel of a column
+// tile, which four XCDs read at about the same time, comes to the later ones
+// from the last-level cache. (Measured per step: GM = 4 beat 8 by about 1 %
+// and 16, 2 and 1 by more; remapping ids so that each XCD owned a contiguous
+// range of logical tiles, 8 row tiles x 4 column tiles at a time, was 1-2 %
+// slower than this on the DeepSeek-V3-, GShard- and Switch-shaped layers.)
+// The grid is 1-D with at least nrow * ncol rounded up to a multiple of
 // 8 workgroups (a ragged-M launch sizes it from an upper bound on nrow); the
 // workgroups past nrow * ncol have no tile.
 constexpr int kXcds = 8;
