@@ -173,6 +173,9 @@ def stage_work(c, rows, ne_experts, permuted_copy=False):
         "ffn_gemm1": (2 * R * d * f1, W1 + R * d * eb + R * ((f1 if c.act == "swiglu" else 0) + f) * eb),
         "ffn_gemm2": (2 * R * f * d, W2 + R * f * eb + R * d * eb),
         "combine": (0, T * d * eb * (2 + (1 if c.shared else 0)) + rows * d * eb + T * k * 8),
+        # top-1: the down projection with the combine in its epilogue (x read, y written, the token of
+        # each row, the weight and slot of each token)
+        "ffn_gemm2_combine": (2 * R * f * d, W2 + R * f * eb + R * d * eb + 2 * T * d * eb + rows * 4 + T * 8),
         "aux": (0, T * E * 4),
         "bwd_combine": (0, T * d * eb + rows * d * eb * 2 + T * k * 12),
         "bwd_dgrad2": (2 * R * d * f, W2 + R * d * eb + 2 * R * f1 * eb),
@@ -354,6 +357,9 @@ def main():
     ap.add_argument("--x-perm", action="store_true",
                     help="materialise the permuted copy of x (moe_dispatch writes x_perm, moe_expert_ffn reads "
                          "it); by default the expert matmuls read the routed rows of x in place")
+    ap.add_argument("--separate-combine", action="store_true",
+                    help="top-1 bf16 layers: run the combine as its own pass (moe_expert_ffn_rows + "
+                         "moe_combine) instead of in the down projection's epilogue (moe_expert_ffn_combine)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB before every timed step, so the 256 MB "
                          "last-level cache cannot serve the step's reads from the previous one; the per-step "
@@ -399,11 +405,14 @@ def main():
                         dtype=c.dtype, alpha=c.alpha, shared=c.shared, routing=c.routing)
     buf = M.LayerBuffers.allocate(cfg, rows_in_place=not args.x_perm)
     stream = torch.cuda.current_stream()
+    # top-1 token choice in bf16 without a shared expert: the combine runs in the down projection's epilogue
+    fused_combine = (not args.x_perm and not args.separate_combine and c.k == 1 and not c.shared and
+                     c.dtype == "bf16" and c.routing == "token_choice")
 
     biased = c.gate in ("sigmoid_bias", "sqrt_softplus_bias")
 
     def step():
-        M.forward(buf, inp, stream=stream)
+        M.forward(buf, inp, stream=stream, fused_combine=fused_combine)
         if biased and args.balance == "quantile":
             M.moe_bias_quantile(cfg, buf.t["probs"], inp["sel_bias"], buf.t["ws"], stream=stream)
         elif biased:
@@ -494,7 +503,7 @@ def main():
         "config": {"workload": c.name, "T": c.T, "d_model": c.d, "d_ff": c.f, "experts": c.E, "top_k": c.k,
                    "capacity_factor": c.cf, "act": c.act, "gate": c.gate, "kept_rows": rows,
                    "nonempty_experts": ne, "tflops_algorithmic": total_flops / (ms_step * 1e-3) / 1e12,
-                   "permuted_copy": bool(args.x_perm)},
+                   "permuted_copy": bool(args.x_perm), "fused_combine": fused_combine},
         "roofline": roof,
         "zero_fill": zero_fill,
         "determinism": determinism,

@@ -306,6 +306,28 @@ int moe_expert_ffn_rows(const moe_config* cfg, const void* x, const int32_t* row
 int moe_combine(const moe_config* cfg, const void* x, const void* y_perm, const int32_t* slot,
                 const float* topk_w, const void* y_shared, void* y, void* stream);
 
+/* moe_expert_ffn_rows with the combine of [SW] eq. (2) (plus the residual,
+ * as in moe_combine) fused into the down projection's epilogue, for top-1
+ * token-choice layers without a shared expert in bf16 ([WIKI], cross-cutting
+ * findings: the fused dispatch / linear / activation / linear / combine
+ * pipelines). With one choice per token, the routed row r = slot[t] is the only
+ * expert row of token t, so the tile that computes y_perm[r] also writes
+ *   y[t] = x[t] + topk_w[t] * y_perm[r]   (fp32, one rounding to bf16)
+ * with no atomics; extra workgroups of the same launch write y[t] = x[t] for
+ * the tokens whose choice was dropped (slot[t] == -1). y_perm, act_saved and
+ * h_saved are as in moe_expert_ffn_rows, and y is bitwise moe_combine's result
+ * for the same inputs. Inputs: x [T,d], row_token [R], expert_offsets [E+1],
+ * slot [T,1] and topk_w [T,1] as written by moe_dispatch and moe_route, w1, w2
+ * (device). Outputs: act_saved [R,f1] (ReLU: optional), h_saved [R,f],
+ * y_perm [R,d], y [T,d] (16-byte aligned; must not overlap the inputs). Returns
+ * MOE_ERR_UNSUPPORTED unless dtype is bf16, top_k is 1, there is no shared
+ * expert and the routing is token choice; x must be under 4 GiB as for
+ * moe_expert_ffn_rows. Needs the workspace. */
+int moe_expert_ffn_combine(const moe_config* cfg, const void* x, const int32_t* row_token,
+                           const int32_t* expert_offsets, const int32_t* slot, const float* topk_w,
+                           const void* w1, const void* w2, void* act_saved, void* h_saved, void* y_perm,
+                           void* y, void* ws, size_t ws_bytes, void* stream);
+
 /* Switch load-balancing loss, [SW] eq. (4) and the numpy sketch after it:
  *   aux = alpha * E * sum_i f_i * P_i,  f_i = expert_counts[i] / (T*k) (counted
  *   before drops), P_i = mean over t of probs[t,i].

@@ -12,7 +12,8 @@
  *
  * Stage names (one stage = one kernel unless noted):
  *   "route" (moe_route, moe_route_noisy), "route_ec" (moe_route_ec, several
- *   kernels), "dispatch" (4 kernels), "ffn_gemm1", "ffn_gemm2", "combine",
+ *   kernels), "dispatch" (4 kernels), "ffn_gemm1", "ffn_gemm2",
+ *   "ffn_gemm2_combine" (moe_expert_ffn_combine's down projection), "combine",
  *   "aux" (moe_aux_loss or moe_aux_noisy, 2 kernels), "bias_update",
  *   "bias_quantile" (several kernels), "bwd_combine", "bwd_dgrad2",
  *   "bwd_wgrad2", "bwd_dgrad1", "bwd_wgrad1", "bwd_dlogits",

@@ -6,7 +6,8 @@ fallback: if libmoe.so is missing or cannot be loaded, importing the binding's
 calls raises.
 
 Entry points mirror the C ABI: moe_plan, moe_route, moe_route_noisy, moe_route_ec, moe_dispatch,
-moe_dispatch_noalloc, moe_expert_ffn, moe_expert_ffn_rows, moe_combine, moe_aux_loss, moe_aux_noisy,
+moe_dispatch_noalloc, moe_expert_ffn, moe_expert_ffn_rows, moe_expert_ffn_combine, moe_combine, moe_aux_loss,
+moe_aux_noisy,
 moe_bias_update, moe_bias_quantile, moe_backward, moe_status_string.
 ``LayerBuffers`` allocates the tensors one forward+backward needs, and
 ``forward`` / ``backward`` issue the ABI calls in order on those buffers.
@@ -34,7 +35,7 @@ MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
 EXPORTS = ["moe_plan", "moe_route", "moe_route_noisy", "moe_route_ec", "moe_dispatch", "moe_dispatch_noalloc",
-           "moe_expert_ffn", "moe_expert_ffn_rows",
+           "moe_expert_ffn", "moe_expert_ffn_rows", "moe_expert_ffn_combine",
            "moe_combine", "moe_aux_loss", "moe_aux_noisy", "moe_bias_update", "moe_bias_quantile", "moe_backward", "moe_status_string"]
 
 
@@ -99,6 +100,7 @@ def lib():
         L.moe_dispatch.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_dispatch_noalloc.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn.argtypes = [cfg] + [_vp] * 14 + [ctypes.c_size_t, _vp]
+        L.moe_expert_ffn_combine.argtypes = [cfg] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [cfg, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_aux_loss.argtypes = [cfg, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_bias_update.argtypes = [cfg, _vp, ctypes.c_float, _vp, _vp]
@@ -219,6 +221,14 @@ def moe_expert_ffn_rows(cfg, x, row_token, expert_offsets, w1, w2, ws1, ws2, act
                                      _stream(stream)), "moe_expert_ffn_rows")
 
 
+def moe_expert_ffn_combine(cfg, x, row_token, expert_offsets, slot, topk_w, w1, w2, act_saved, h_saved, y_perm, y,
+                           ws, stream=None):
+    _check(lib().moe_expert_ffn_combine(ctypes.byref(cfg), _p(x), _p(row_token), _p(expert_offsets), _p(slot),
+                                        _p(topk_w), _p(w1), _p(w2), _p(act_saved), _p(h_saved), _p(y_perm), _p(y),
+                                        _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_expert_ffn_combine")
+
+
 def moe_combine(cfg, x, y_perm, slot, topk_w, y_shared, y, stream=None):
     _check(lib().moe_combine(ctypes.byref(cfg), _p(x), _p(y_perm), _p(slot), _p(topk_w), _p(y_shared), _p(y),
                              _stream(stream)), "moe_combine")
@@ -291,9 +301,10 @@ class LayerBuffers:
         return LayerBuffers(cfg, info, t)
 
 
-def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
+def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True, fused_combine=False):
     """moe_route -> moe_dispatch (or moe_route_ec) -> moe_expert_ffn (moe_expert_ffn_rows without x_perm)
-    -> moe_combine (-> moe_aux_loss)."""
+    -> moe_combine (-> moe_aux_loss). fused_combine (buffers without x_perm; bf16, top-1, token choice, no
+    shared expert): moe_expert_ffn_combine in place of moe_expert_ffn_rows and moe_combine."""
     c, t = buf.cfg, buf.t
     if c.gate == MOE_GATE_NOISY_TOPK:
         moe_route_noisy(c, inp["x"], inp["w_router"], inp["noise"], t["noisy_logits"], t["probs"], t["topk_idx"],
@@ -308,7 +319,12 @@ def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
                   t["topk_idx"], t["topk_w"], stream)
         moe_dispatch(c, inp["x"], t["topk_idx"], t["expert_counts"], t["expert_offsets"], t["slot"],
                      t["row_token"], t.get("x_perm"), t["ws"], stream)
-    if "x_perm" in t:
+    if fused_combine:
+        if "x_perm" in t:
+            raise MoeError("fused_combine reads the routed rows through row_token: allocate without x_perm")
+        moe_expert_ffn_combine(c, inp["x"], t["row_token"], t["expert_offsets"], t["slot"], t["topk_w"], inp["w1"],
+                               inp["w2"], t.get("act_saved"), t["h_saved"], t["y_perm"], t["y"], t["ws"], stream)
+    elif "x_perm" in t:
         moe_expert_ffn(c, t["x_perm"], t["expert_offsets"], inp["w1"], inp["w2"], inp["x"], inp.get("ws1"),
                        inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
                        t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
@@ -316,7 +332,8 @@ def forward(buf: LayerBuffers, inp: dict, stream=None, aux=True):
         moe_expert_ffn_rows(c, inp["x"], t["row_token"], t["expert_offsets"], inp["w1"], inp["w2"], inp.get("ws1"),
                             inp.get("ws2"), t.get("act_saved"), t["h_saved"], t["y_perm"], t.get("act_shared"),
                             t.get("h_shared"), t.get("y_shared"), t["ws"], stream)
-    moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
+    if not fused_combine:
+        moe_combine(c, inp["x"], t["y_perm"], t["slot"], t["topk_w"], t.get("y_shared"), t["y"], stream)
     if aux and c.gate == MOE_GATE_NOISY_TOPK:
         moe_aux_noisy(c, t["noisy_logits"], inp["noise"], t["topk_idx"], t["topk_w"], t["aux"], t["ws"], stream)
     elif aux:

@@ -304,12 +304,20 @@ int moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk
 
 namespace {
 
+// The top-1 combine fused into the down projection (moe_expert_ffn_combine).
+struct Combine1 {
+  const int32_t* slot;
+  const float* topk_w;
+  void* y;
+};
+
 // The expert FFNs; routed rows from x_perm, or (x_perm NULL) from x through
-// row_token, gathered as the first matmul loads them.
+// row_token, gathered as the first matmul loads them; with cb, the down
+// projection's epilogue also writes the top-1 combine.
 int expert_ffn(const moe_config* c, const void* x_perm, const int32_t* row_token, const int32_t* expert_offsets,
                const void* w1, const void* w2, const void* x, const void* ws1, const void* ws2, void* act_saved,
                void* h_saved, void* y_perm, void* act_shared, void* h_shared, void* y_shared, void* ws,
-               size_t ws_bytes, void* stream) {
+               size_t ws_bytes, void* stream, const Combine1* cb = nullptr) {
   int st = check_config(c);
   if (st) return st;
   const bool empty = c->num_tokens == 0;
@@ -368,6 +376,14 @@ int expert_ffn(const moe_config* c, const void* x_perm, const int32_t* row_token
   g2.B = w2; g2.ldb = f; g2.strideB = (int64_t)d * f;
   g2.A_sh = h_shared; g2.B_sh = ws2;
   g2.C = y_perm; g2.ldc = d; g2.C_sh = y_shared;
+  if (cb) {
+    g2.epi = moe::EPI_COMBINE1;
+    g2.X = x; g2.ldx = d;
+    g2.slot = cb->slot; g2.slot_k = 1;
+    g2.row_tok = row_token; g2.tok_w = cb->topk_w;
+    g2.Yc = cb->y; g2.copy_tokens = T;
+    return gemm(c, g2, s, "ffn_gemm2_combine");
+  }
   return gemm(c, g2, s, "ffn_gemm2");
 }
 
@@ -390,6 +406,22 @@ int moe_expert_ffn_rows(const moe_config* c, const void* x, const int32_t* row_t
                         size_t ws_bytes, void* stream) {
   return expert_ffn(c, nullptr, row_token, expert_offsets, w1, w2, x, ws1, ws2, act_saved, h_saved, y_perm,
                     act_shared, h_shared, y_shared, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_combine(const moe_config* c, const void* x, const int32_t* row_token,
+                           const int32_t* expert_offsets, const int32_t* slot, const float* topk_w, const void* w1,
+                           const void* w2, void* act_saved, void* h_saved, void* y_perm, void* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = check_config(c);
+  if (st) return st;
+  if (c->dtype != MOE_DT_BF16 || c->top_k != 1 || c->num_shared_experts != 0 ||
+      c->routing != MOE_ROUTING_TOKEN_CHOICE)
+    return MOE_ERR_UNSUPPORTED;
+  if (c->num_tokens > 0 && (!x || !row_token || !slot || !topk_w || !y)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const Combine1 cb{slot, topk_w, y};
+  return expert_ffn(c, nullptr, row_token, expert_offsets, w1, w2, x, nullptr, nullptr, act_saved, h_saved, y_perm,
+                    nullptr, nullptr, nullptr, ws, ws_bytes, stream, c->num_tokens > 0 ? &cb : nullptr);
 }
 
 int moe_combine(const moe_config* c, const void* x, const void* y_perm, const int32_t* slot, const float* topk_w,

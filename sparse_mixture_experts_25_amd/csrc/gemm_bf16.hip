@@ -214,6 +214,26 @@ struct DmaPlan {
   }
 };
 
+// The top-1 combine of a token whose only choice was dropped: y = x bit for
+// bit. Wave w (counted over the copy workgroups) takes the 64 tokens from
+// 64 w, finds the dropped ones with one ballot and copies their rows, 16 bytes
+// per lane.
+__device__ __forceinline__ void copy_dropped_rows(const GemmArgs& a, int wave_global, int lane) {
+  const int t0 = wave_global * 64;
+  if (t0 >= a.copy_tokens) return;
+  const int t = t0 + lane;
+  uint64_t mask = __ballot(t < a.copy_tokens && a.slot[t] < 0);
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
+  uint16_t* Y = reinterpret_cast<uint16_t*>(a.Yc);
+  const int nv = a.N / 8;
+  while (mask) {
+    const int j = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int64_t off = (int64_t)(t0 + j) * a.ldx;
+    for (int v = lane; v < nv; v += 64) st128_nt(Y + off + 8 * v, ld128(X + off + 8 * v));
+  }
+}
+
 // ------------------------------------------------------------ kernel
 // WGN waves along N (2 along M): 4 waves for 128x128 tiles, or 8 waves for
 // 256x256 tiles with 128x64 per wave (two waves per SIMD, so one wave's matrix
@@ -259,6 +279,13 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   // addresses of the direct loads are scalar arithmetic
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WGN, wn = wave % WGN;
+
+  if constexpr (EPI == EPI_COMBINE1) {
+    if ((int64_t)blockIdx.x >= a.copy_base) {
+      copy_dropped_rows(a, (int)((int64_t)blockIdx.x - a.copy_base) * NW + wave, lane);
+      return;
+    }
+  }
 
   // ---- locate the tile
   int g, rows, mrow0 = 0, nb, mb = 0;
@@ -623,7 +650,7 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
   }
   __syncthreads();
 
-  if constexpr (EPI == EPI_STORE && (BM == 256 || KIND == 0)) {
+  if constexpr ((EPI == EPI_STORE || EPI == EPI_COMBINE1) && (BM == 256 || KIND == 0)) {
     // A plain bf16 output: the tile is staged in LDS as the bf16 values it is
     // stored as (the same rounding of the same accumulators), all of it in one
     // pass: half the LDS bytes of fp32 staging, and one barrier instead of three.
@@ -645,6 +672,46 @@ __global__ __launch_bounds__(128 * WGN, 1) __attribute__((amdgpu_waves_per_eu(wa
         }
     __syncthreads();
     uint16_t* C = reinterpret_cast<uint16_t*>(sh ? a.C_sh : a.C);
+    if constexpr (EPI == EPI_COMBINE1) {
+      // y_perm as above, and the combine of each row's token in the order of
+      // the separate pass (x, then the weighted expert row; one rounding). The
+      // tokens, their weights and x's vectors of all of a thread's outputs go
+      // out before any is used: three dependent loads per output.
+      constexpr int IT1 = BM * BN / 8 / NTH;
+      static_assert((BM * BN / 8) % NTH == 0, "every thread writes the same number of vectors");
+      const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
+      uint16_t* Y = reinterpret_cast<uint16_t*>(a.Yc);
+      int tok[IT1];
+      float w[IT1];
+      u128 xv[IT1];
+#pragma unroll
+      for (int it = 0; it < IT1; ++it) {
+        const int u = tid + it * NTH, m = u / (BN / 8), col = nb * BN + (u % (BN / 8)) * 8;
+        tok[it] = (m < rows - mrow0 && col < a.N) ? a.row_tok[r0 + mrow0 + m] : -1;
+      }
+#pragma unroll
+      for (int it = 0; it < IT1; ++it) {
+        const int u = tid + it * NTH, col = nb * BN + (u % (BN / 8)) * 8;
+        if (tok[it] >= 0) {
+          w[it] = a.tok_w[tok[it]];
+          xv[it] = ld128(X + (int64_t)tok[it] * a.ldx + col);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < IT1; ++it) {
+        if (tok[it] < 0) continue;
+        const int u = tid + it * NTH, m = u / (BN / 8), n = (u % (BN / 8)) * 8, col = nb * BN + n;
+        const u128 v = ld128(Cb + m * CB + n);
+        st128(C + (r0 + mrow0 + m) * a.ldc + col, v);
+        float yp[8], o[8];
+        Elem<uint16_t>::unpack(v, yp);
+        Elem<uint16_t>::unpack(xv[it], o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w[it], yp[e], o[e]);
+        st128_nt(Y + (int64_t)tok[it] * a.ldx + col, Elem<uint16_t>::pack(o));
+      }
+      return;
+    }
     for (int u = tid; u < BM * BN / 8; u += NTH) {
       const int m = u / (BN / 8), n = (u % (BN / 8)) * 8;
       const u128 v = ld128(Cb + m * CB + n);
@@ -871,9 +938,15 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     const int nM = (a.M + BM - 1) / BM, nN = (a.N + BN - 1) / BN;
     n = (int64_t)ng * ((BM < 256) ? ragged_k_per_group(nM, nN) : (int64_t)nM * nN);
   }
+  GemmArgs b = a;
+  if constexpr (EPI == EPI_COMBINE1) {
+    // the dropped tokens' copies: one wave per 64 tokens, after the tiles
+    b.copy_base = n;
+    n += (a.copy_tokens + 128 * WGN - 1) / (128 * WGN);
+  }
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NS, KIND, B_KC, EPI, WGN, GB>), dim3((unsigned)n), dim3(128 * WGN), 0,
-                     st, a);
+                     st, b);
   return hipGetLastError();
 }
 
@@ -897,6 +970,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
       case EPI_STORE: return launch_t<BM, BN, BK, NS, 0, 1, EPI_STORE, WGN>(a, st);
       case EPI_RELU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_RELU_FWD, WGN>(a, st);
       case EPI_SWIGLU_FWD: return launch_t<BM, BN, BK, NS, 0, 1, EPI_SWIGLU_FWD, WGN>(a, st);
+      case EPI_COMBINE1: return launch_t<BM, BN, BK, NS, 0, 1, EPI_COMBINE1, WGN>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -965,6 +1039,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   GemmArgs b = a;
   b.split_part = 1;
   b.split_rows = 128;
+  b.copy_tokens = 0;  // the dropped tokens of a fused combine are copied by the second launch
   const hipError_t e = launch_tiles<256, 256, 64, 2, 4>(b, st);
   if (e != hipSuccess) return e;
   GemmArgs sm = a;

@@ -97,6 +97,12 @@ enum GemmEpi {
   // the input gradient of the layer (dy + expert input gradients + router
   // term + shared expert), rows = tokens (ragged-M, one group, B MN-contiguous)
   EPI_UNPERMUTE = 6,
+  // top-1 combine in the down projection's epilogue (bf16, no shared expert,
+  // B K-contiguous): C = acc (y_perm) and, for routed row r of token
+  // t = row_tok[r], Yc[t] = X[t] + tok_w[t] * C[r] rounded once; extra
+  // workgroups past copy_base copy X[t] to Yc[t] for the tokens t < copy_tokens
+  // whose slot is -1
+  EPI_COMBINE1 = 7,
 };
 
 struct GemmArgs {
@@ -128,6 +134,8 @@ struct GemmArgs {
   // gathered as they are loaded, so no permuted copy is needed); ragged-K:
   // k-row r of B is row b_rows[r] of B. src_rows: rows of the mapped operand.
   const int32_t* a_rows; const int32_t* b_rows; int64_t src_rows;
+  // EPI_COMBINE1 (X, ldx: x; slot: [T] slots of the top-1 choice)
+  const int32_t* row_tok; const float* tok_w; void* Yc; int copy_tokens; int64_t copy_base;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // order[0..E(+1)): the groups with rows sorted by row count, largest first

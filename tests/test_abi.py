@@ -257,3 +257,31 @@ def test_dispatch_noalloc_validates_before_launch():
     assert L.moe_dispatch_noalloc(ctypes.byref(over), A, A, A, A, A, A, A, N) == M.MOE_ERR_WORKSPACE
     info = M.moe_plan_info()
     assert L.moe_plan(ctypes.byref(fits), ctypes.byref(info)) == M.MOE_OK
+
+
+def test_expert_ffn_combine_validates_before_launch():
+    """moe_expert_ffn_combine fuses the combine only where a token has one
+    routed row: bf16, top-1, token choice, no shared expert. Everything else
+    is refused before any launch, as are missing or misaligned outputs, a short
+    workspace and inputs past the 32-bit row offsets."""
+    L = M.lib()
+    U, E = M.MOE_ERR_UNSUPPORTED, M.MOE_ERR_INVALID_ARG
+
+    def call(cfg, x=A, y=A, ws_bytes=None, slot=A):
+        if ws_bytes is None:
+            ws_bytes = M.moe_plan(cfg).workspace_bytes
+        return L.moe_expert_ffn_combine(ctypes.byref(cfg), x, A, A, slot, A, A, A, N, A, A, y, A, ws_bytes, N)
+
+    assert call(M.make_config(64, 64, 64, 4, 2, cf=1.0)) == U
+    assert call(M.make_config(64, 64, 64, 4, 1, cf=1.0, dtype="f32")) == U
+    assert call(M.make_config(64, 64, 64, 4, 1, cf=1.0, shared=1)) == U
+    ec = M.make_config(64, 64, 64, 4, 1, cf=1.0, routing="expert_choice")
+    assert call(ec, ws_bytes=1 << 30) in (U, E)
+    ok = M.make_config(64, 64, 64, 4, 1, cf=1.0)
+    assert call(ok, y=N) == E
+    assert call(ok, y=MIS) == E
+    assert call(ok, slot=N) == E
+    assert call(ok, x=MIS) == E
+    assert call(ok, ws_bytes=M.moe_plan(ok).workspace_bytes - 16) == M.MOE_ERR_WORKSPACE
+    big = M.make_config(262144, 8192, 64, 4, 1, act="relu", dtype="bf16")
+    assert call(big, ws_bytes=1 << 40) == U
