@@ -123,3 +123,13 @@ def test_fused_combine_bitwise_full_size_switch_base():
     sep, fus = _fused_and_separate(c, dev)
     n, nd = _assert_bitwise(sep, fus, dev["x"])
     print(f"  kept rows {n}, dropped tokens {nd}: bitwise equal", flush=True)
+
+
+def test_fused_combine_empty_batch():
+    """T = 0: nothing to compute; the call succeeds and writes no rows."""
+    c = CASES["most_dropped"].replace(name="empty", T=0)
+    dev = to_dev(make_inputs(c, seed=0, with_dy=False))
+    fus = M.LayerBuffers.allocate(cfg_of(c), backward=False, rows_in_place=True)
+    M.forward(fus, dev, aux=True, fused_combine=True)
+    torch.cuda.synchronize()
+    assert int(fus.t["expert_offsets"][-1]) == 0

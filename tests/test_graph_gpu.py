@@ -19,6 +19,8 @@ BIAS_GAMMA = 1e-3
 
 GRAPH_CASES = {
     "switch_base_s": SMALL["switch_base"],
+    # the forward with the top-1 combine in the down projection (moe_expert_ffn_combine, no x_perm)
+    "switch_base_s_fused": SMALL["switch_base"],
     "gshard_top2_s": SMALL["gshard_top2"],
     "deepseek_v3_s": SMALL["deepseek_v3"],
     "ec_relu": LayerConfig("ec_relu", T=777, d=192, f=320, E=8, k=8, act="relu", cf=2.0, gate="softmax",
@@ -46,12 +48,13 @@ def test_graph_replay_matches_eager(name):
     c = GRAPH_CASES[name]
     inp = to_dev(make_inputs(c))
     cfg = cfg_of(c)
-    buf = M.LayerBuffers.allocate(cfg)
+    fused = name.endswith("_fused")
+    buf = M.LayerBuffers.allocate(cfg, rows_in_place=fused)
     biased = c.gate in ("sigmoid_bias", "sqrt_softplus_bias")
     bias0 = inp["sel_bias"].clone() if biased else None
 
     def step():
-        M.forward(buf, inp, aux=True)
+        M.forward(buf, inp, aux=True, fused_combine=fused)
         if biased:
             M.moe_bias_update(cfg, buf.t["expert_counts"], BIAS_GAMMA, inp["sel_bias"])
         M.backward(buf, inp, inp["dy"])
