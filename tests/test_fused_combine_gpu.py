@@ -9,7 +9,7 @@ dropped are copied by extra workgroups of the same launch. The epilogue takes
 the same bf16 y_perm value and applies the combine's fp32 multiply-add in the
 same order, so y must match bit for bit. The separate path is compared with
 the oracle element by element in test_parity_gpu.py and test_full_size_gpu.py;
-two reduced cases are compared with the oracle here as well.
+three reduced cases are compared with the oracle here as well.
 
 Cases, with the instantiation each one reaches under the launcher's tile rule
 (256x256 tiles when the average group has at least 256 rows and there are at
@@ -22,6 +22,8 @@ also runs the copy workgroups):
     with nothing to copy)
   * ragged_swiglu: SwiGLU, d and f off the tile sizes, T not a multiple of 64
   * most_dropped: three quarters of the tokens dropped (most of y is copied)
+  * noisy_top1, sigmoid_bias_top1: noisy top-1 and sigmoid gating with a
+    selection bias (the routing differs; the fused step is the same)
   * switch_base at full size: the layer the fused bench forward times
 """
 import numpy as np
@@ -47,8 +49,13 @@ CASES = {
                                  logit_offset="normal", fwd_only=True),
     "most_dropped": LayerConfig("most_dropped", T=2048, d=264, f=128, E=16, k=1, cf=0.25,
                                 logit_offset="logzipf", fwd_only=True),
+    # the other gates the entry point accepts with one choice per token
+    "noisy_top1": LayerConfig("noisy_top1", T=1536, d=192, f=320, E=8, k=1, gate="noisy_topk", renorm=True,
+                              cf=1.0, alpha=0.01, fwd_only=True),
+    "sigmoid_bias_top1": LayerConfig("sigmoid_bias_top1", T=1536, d=192, f=320, E=8, k=1, gate="sigmoid_bias",
+                                     sel_bias="uniform", cf=1.0, logit_offset="normal", fwd_only=True),
 }
-ORACLE = ["ragged_swiglu", "most_dropped"]
+ORACLE = ["ragged_swiglu", "most_dropped", "sigmoid_bias_top1"]
 NAN_BF16 = -1  # 0xFFFF: a bf16 NaN, so any output element left unwritten fails the comparison
 
 
