@@ -85,6 +85,8 @@ int main() {
                           nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
     EXPECT(moe_expert_ffn_rows(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
+    EXPECT(moe_expert_ffn_combine(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
     const int cb = moe_combine(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     EXPECT(cb != MOE_OK || (st == MOE_OK && c.num_tokens == 0));
     EXPECT(moe_aux_loss(&c, nullptr, nullptr, nullptr, nullptr, 0, nullptr) != MOE_OK);
