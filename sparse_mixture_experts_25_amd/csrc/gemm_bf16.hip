@@ -1024,10 +1024,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // the cap, and the realised groups range from full (expert choice, balanced
   // routing) to mostly empty (skewed routing that drops most assignments). A
   // row-ragged matmul then runs as two launches over the groups, each deciding
-  // on the device from the group's row count: 128 rows or more on 256x256
-  // tiles (a group of 128-255 rows reads each weight slab once, and the waves
-  // past its rows skip their matrix work), the others (and empty ones) on the
-  // weight-streaming 128x128 tiles. Dropless layers keep one launch: there the
+  // on the device from the group's row count: kSplitRows (64) rows or more on
+  // 256x256 tiles (a group of 64-255 rows reads each weight slab once, and the
+  // waves past its rows skip their matrix work), the others (and empty ones)
+  // on the weight-streaming 128x128 tiles. Below 64 rows a group's few
+  // 256-wide column tiles each stream a long weight slab alone. Dropless layers keep one launch: there the
   // zero-fill of empty experts overlaps the big groups' matrix work, which a
   // second launch would serialise.
   const bool capped = a.row_cap > 0 && a.row_cap <= 512 && a.E > 1;
@@ -1036,15 +1037,16 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   // CU, run them faster than the 256x256 pipeline.
   if (capped && a.kind == 1) return small_tiles(a);
   if (!capped) return launch_tiles<256, 256, 64, 2, 4>(a, st);
+  constexpr int kSplitRows = 64;
   GemmArgs b = a;
   b.split_part = 1;
-  b.split_rows = 128;
+  b.split_rows = kSplitRows;
   b.copy_tokens = 0;  // the dropped tokens of a fused combine are copied by the second launch
   const hipError_t e = launch_tiles<256, 256, 64, 2, 4>(b, st);
   if (e != hipSuccess) return e;
   GemmArgs sm = a;
   sm.split_part = 2;
-  sm.split_rows = 128;
+  sm.split_rows = kSplitRows;
   return small_tiles(sm);
 }
 

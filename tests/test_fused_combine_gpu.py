@@ -14,7 +14,7 @@ three reduced cases are compared with the oracle here as well.
 Cases, with the instantiation each one reaches under the launcher's tile rule
 (256x256 tiles when the average group has at least 256 rows and there are at
 least 256 such tiles; layers capped at C <= 512 rows split into a 256x256
-launch for groups of 128 rows or more and a 128x128 launch for the rest, which
+launch for groups of 64 rows or more and a 128x128 launch for the rest, which
 also runs the copy workgroups):
   * capped_drops_small_tiles: gemm_bf16_kernel<128, 128, 64, 2, 0, 1, 7, 2, 0>
   * capped_split_pair: <256, 256, 64, 2, 0, 1, 7, 4, 0> then the 128x128 one

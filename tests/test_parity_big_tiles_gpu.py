@@ -5,7 +5,7 @@ The grouped matmul picks its tiles on the host from the launch's row bound
 (max_rows) and widths: 256x256 tiles when the groups average at least 256 rows,
 every output width is at least 256 and the launch has at least 256 such tiles;
 for capped layers (expert capacity <= 512) a row-ragged matmul runs as a split
-pair, groups of >= 128 rows on 256x256 tiles and the rest on 128x128 tiles, and
+pair, groups of >= 64 rows on 256x256 tiles and the rest on 128x128 tiles, and
 the weight gradients (at most 512 rows deep) run on 128x128 tiles. `tile_plan`
 below restates that rule and each case asserts the plan it was built for, so a
 change of the rule that moves a case off its tiles fails here instead of
@@ -107,6 +107,8 @@ def tile_plan(c):
     return plan
 
 
+# a capped layer's split pair: groups of at least this many rows on the 256x256 launch
+SPLIT_ROWS = 64
 _GEMMS = ("ffn_gemm1", "ffn_gemm2", "bwd_dgrad2", "bwd_wgrad2", "bwd_dgrad1", "bwd_wgrad1")
 
 CASES = {
@@ -210,11 +212,12 @@ def test_big_tiles_parity(name):
     t = buf.t
     n = int(fw["n_rows"])
     rows = np.diff(fw["offsets"])
-    print(f"  kept rows {n}, groups >= 128 rows: {int((rows >= 128).sum())}, "
-          f"1..127 rows: {int(((rows > 0) & (rows < 128)).sum())}, empty: {int((rows == 0).sum())}", flush=True)
+    print(f"  kept rows {n}, groups >= {SPLIT_ROWS} rows: {int((rows >= SPLIT_ROWS).sum())}, "
+          f"1..{SPLIT_ROWS - 1} rows: {int(((rows > 0) & (rows < SPLIT_ROWS)).sum())}, "
+          f"empty: {int((rows == 0).sum())}", flush=True)
     if want.get("ffn_gemm1") == "split":
         # both launches of the split pair have groups to run
-        assert (rows >= 128).any() and ((rows > 0) & (rows < 128)).any()
+        assert (rows >= SPLIT_ROWS).any() and ((rows > 0) & (rows < SPLIT_ROWS)).any()
 
     # ---- forward
     np.testing.assert_array_equal(t["topk_idx"].cpu().numpy(), fw["idx"])
